@@ -1,0 +1,413 @@
+#!/usr/bin/env python3
+"""Throughput of the block-scaled FP8 linear-layer hot path on one MI355X.
+
+One step = the full FP8 path of every linear layer of one transformer block
+(2048 hidden, 16 heads, 8192 FFN; QKV 2048->6144, out-proj 2048->2048,
+up/gate 2048->16384, down 8192->2048) on a micro-batch of 8 x 4096 = 32768
+tokens, inputs already resident in HBM:
+
+  per linear:  quant_act(X, 1x128 + 128x1^T)   quant_weight(W, 128x128 + W^T)
+               FWD    Y  = X . W^T      (bf16 out)
+               quant_act(dY, 1x128 + 128x1^T)
+               DGRAD  dX = dY . W       (bf16 out)
+               WGRAD  dW = dY^T . X     (FP32 out)
+
+The metric is the GEMM work of the step (2*M*N*K summed over the 12 GEMMs,
+13.19 TFLOP) divided by the whole step's time (quantizers included), in
+TFLOP/s.  Per-kernel durations come from HIP events recorded around every
+launch inside the timed region, on the stream the kernels run on; the
+dominant kernel's achieved rate is reported against the MI355X dense FP8
+MFMA peak (5.0 PFLOP/s), the quantizers' against HBM (8 TB/s).
+
+The CPU baseline times the plain CPU oracle (quantize + block-scaled GEMM in
+all three modes) on a bounded slice of the same workload: the first
+`--cpu-tokens` tokens of every linear layer, all host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "FP8 block-scaled GEMM TFLOP/s (fwd+dgrad+wgrad) and % of MI355X FP8 peak"
+FP8_PEAK_TFLOPS = 5000.0          # MI355X dense FP8 MFMA, published
+HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_block_stack.json")
+GEMM_SOURCE = os.path.join(ROOT, "fp8_block_scaled_tile_amd", "csrc", "gemm.hip")
+QUANT_SOURCE = os.path.join(ROOT, "fp8_block_scaled_tile_amd", "csrc", "quant.hip")
+
+# kernel symbol of each launch class (for matching rocprofv3 summaries)
+KERNEL_SYMBOLS = {
+    "gemm_fwd_bf16": "void puro::gemm_bs_kernel<0, 0>",
+    "gemm_dgrad_bf16": "void puro::gemm_bs_kernel<1, 0>",
+    "gemm_wgrad_fp32": "void puro::gemm_bs_kernel<2, 1>",
+    "gemm_wgrad_splitk": "void puro::gemm_bs_kernel<2, 3> + splitk_reduce_kernel<1>",
+    "quant_act_dual": "void puro::quant_block_kernel<true, true, false, false>",
+    "quant_weight_t": "void puro::quant_block_kernel<false, false, true, true>",
+}
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="block_stack")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--cpu-tokens", type=int, default=512,
+                   help="token slice for the CPU-oracle baseline (0 = skip)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--ingest-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_DIR"),
+                   help="turn rocprofv3 --pmc counter CSVs into the traffic file and exit")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run only a plain 1 GiB device copy (counter calibration) and exit")
+    return p.parse_args()
+
+
+def sha(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+# ---- per-launch algorithmic work -------------------------------------------
+
+def act_dual_bytes(rows, cols):
+    # read bf16, write 1x128 codes + 128x1 transposed codes, two scale sets
+    return rows * cols * (2 + 1 + 1) + 2 * (rows * cols // 128) * 4
+
+
+def weight_t_bytes(n, k):
+    return n * k * (2 + 1 + 1) + (n * k // (128 * 128)) * 4
+
+
+class Linear:
+    """Device buffers of one linear layer's FP8 path (allocated once)."""
+
+    def __init__(self, torch, pf, spec, tensors):
+        T, din, dout = spec.tokens, spec.d_in, spec.d_out
+        Tp = (T + 127) // 128 * 128
+        d = "cuda:0"
+        u8, f32, bf16 = torch.uint8, torch.float32, torch.bfloat16
+        self.spec = spec
+        self.T, self.Tp, self.din, self.dout = T, Tp, din, dout
+        self.x = tensors["x"].to(d)
+        self.w = tensors["w"].to(d)
+        self.dy = tensors["dy"].to(d)
+        self.qx = torch.empty((T, din), dtype=u8, device=d)
+        self.sx = torch.empty((din // 128, T), dtype=f32, device=d)
+        self.qtx = torch.empty((din, Tp), dtype=u8, device=d)
+        self.stx = torch.empty((Tp // 128, din), dtype=f32, device=d)
+        self.qw = torch.empty((dout, din), dtype=u8, device=d)
+        self.qtw = torch.empty((din, dout), dtype=u8, device=d)
+        self.sw = torch.empty((dout // 128, din // 128), dtype=f32, device=d)
+        self.y = torch.empty((T, dout), dtype=bf16, device=d)
+        self.qdy = torch.empty((T, dout), dtype=u8, device=d)
+        self.sdy = torch.empty((dout // 128, T), dtype=f32, device=d)
+        self.qtdy = torch.empty((dout, Tp), dtype=u8, device=d)
+        self.stdy = torch.empty((Tp // 128, dout), dtype=f32, device=d)
+        self.dx = torch.empty((T, din), dtype=bf16, device=d)
+        self.dw = torch.empty((dout, din), dtype=f32, device=d)
+        self.gemms = [  # (class, mode, M, N, K)
+            ("gemm_fwd_bf16", pf.GEMM_FWD, T, dout, din),
+            ("gemm_dgrad_bf16", pf.GEMM_DGRAD, T, din, dout),
+            (None, pf.GEMM_WGRAD, dout, din, Tp),
+        ]
+        ws_need = max(pf.puro_fp8_gemm_workspace_bytes(m, M, N, K) for _, m, M, N, K in self.gemms)
+        self.ws = torch.empty(max(ws_need, 16), dtype=u8, device=d)
+        self.wgrad_split = pf.puro_fp8_gemm_workspace_bytes(pf.GEMM_WGRAD, dout, din, Tp) > 0
+        self.gemms[2] = ("gemm_wgrad_splitk" if self.wgrad_split else "gemm_wgrad_fp32",
+                         pf.GEMM_WGRAD, dout, din, Tp)
+
+    def flops(self):
+        return sum(2.0 * M * N * K for _, _, M, N, K in self.gemms)
+
+
+def check(pf, rc, what):
+    if rc != 0:
+        raise RuntimeError(f"{what}: {pf.puro_fp8_status_string(rc)}")
+
+
+def run_step(pf, layers, stream, rec=None):
+    """Enqueue one step.  rec(name, work) returns (start_event, end_event) to
+    bracket a launch, or None to launch unbracketed."""
+    P = lambda t: t.data_ptr()
+    for L in layers:
+        calls = [
+            ("quant_act_dual", act_dual_bytes(L.T, L.din), lambda: pf.puro_fp8_quant_act(
+                P(L.x), L.T, L.din, P(L.qx), P(L.sx), P(L.qtx), P(L.stx), stream)),
+            ("quant_weight_t", weight_t_bytes(L.dout, L.din), lambda: pf.puro_fp8_quant_weight(
+                P(L.w), L.dout, L.din, P(L.qw), P(L.qtw), P(L.sw), stream)),
+            (L.gemms[0][0], 2.0 * L.T * L.dout * L.din, lambda: pf.puro_fp8_gemm_blockscaled(
+                pf.GEMM_FWD, L.T, L.dout, L.din, P(L.qx), P(L.sx), P(L.qw), P(L.sw), P(L.y),
+                pf.OUT_BF16, 0, P(L.ws), L.ws.numel(), stream)),
+            ("quant_act_dual", act_dual_bytes(L.T, L.dout), lambda: pf.puro_fp8_quant_act(
+                P(L.dy), L.T, L.dout, P(L.qdy), P(L.sdy), P(L.qtdy), P(L.stdy), stream)),
+            (L.gemms[1][0], 2.0 * L.T * L.din * L.dout, lambda: pf.puro_fp8_gemm_blockscaled(
+                pf.GEMM_DGRAD, L.T, L.din, L.dout, P(L.qdy), P(L.sdy), P(L.qtw), P(L.sw), P(L.dx),
+                pf.OUT_BF16, 0, P(L.ws), L.ws.numel(), stream)),
+            (L.gemms[2][0], 2.0 * L.dout * L.din * L.Tp, lambda: pf.puro_fp8_gemm_blockscaled(
+                pf.GEMM_WGRAD, L.dout, L.din, L.Tp, P(L.qtdy), P(L.stdy), P(L.qtx), P(L.stx),
+                P(L.dw), pf.OUT_FP32, 0, P(L.ws), L.ws.numel(), stream)),
+        ]
+        for name, work, fn in calls:
+            ev = rec(name, work) if rec else None
+            if ev:
+                ev[0].record()
+            check(pf, fn(), name)
+            if ev:
+                ev[1].record()
+
+
+# ---- counters (rocprofv3 --pmc) ----------------------------------------------
+
+def _read_pmc_csv(path):
+    """{kernel_name: [values per dispatch]} from a rocprofv3 counter_collection.csv."""
+    import csv
+    out = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            name = row.get("Kernel_Name") or row.get("Kernel-Name") or ""
+            val = row.get("Counter_Value") or row.get("Counter-Value")
+            if val is None:
+                continue
+            out.setdefault(name, []).append(float(val))
+    return out
+
+
+def ingest_pmc(fetch_csv, write_csv, copy_dir):
+    """Write the traffic file: per kernel, FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch) scaled by the factor a plain copy of known size reads on the
+    same counters (bytes expected / bytes counted)."""
+    fetch = _read_pmc_csv(fetch_csv)
+    write = _read_pmc_csv(write_csv)
+    cf = _read_pmc_csv(os.path.join(copy_dir, "fetch.csv"))
+    cw = _read_pmc_csv(os.path.join(copy_dir, "write.csv"))
+    copy_bytes = float(1 << 30)
+    def copy_factor(tbl):
+        vals = [v for k, vs in tbl.items() if "copy" in k.lower() or "elementwise" in k.lower()
+                for v in vs]
+        if not vals:
+            return None
+        return copy_bytes / (max(vals) * 1024.0)
+    ff, fw = copy_factor(cf), copy_factor(cw)
+    kernels = {}
+    for name in set(fetch) | set(write):
+        f = fetch.get(name, [])
+        w = write.get(name, [])
+        if not f or not w:
+            continue
+        kernels[name] = {
+            "fetch_kib_per_dispatch": sum(f) / len(f),
+            "write_kib_per_dispatch": sum(w) / len(w),
+            "dispatches": len(f),
+            "hbm_bytes_per_dispatch": (sum(f) / len(f) * 1024.0 * (ff or 1.0) +
+                                       sum(w) / len(w) * 1024.0 * (fw or 1.0)),
+        }
+    doc = {"copy_factor_fetch": ff, "copy_factor_write": fw,
+           "gemm_source_sha": sha(GEMM_SOURCE), "quant_source_sha": sha(QUANT_SOURCE),
+           "kernels": kernels}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(doc, f, indent=1, sort_keys=True)
+    print(f"wrote {TRAFFIC_FILE}: {len(kernels)} kernels")
+
+
+def traffic_for(symbol_prefix):
+    """HBM bytes per dispatch for a kernel, or None if the counters are absent
+    or were taken on a different version of the kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            doc = json.load(f)
+    except (OSError, ValueError):
+        return None
+    src = GEMM_SOURCE if "gemm" in symbol_prefix else QUANT_SOURCE
+    key = "gemm_source_sha" if "gemm" in symbol_prefix else "quant_source_sha"
+    if doc.get(key) != sha(src):
+        return None
+    for name, v in doc.get("kernels", {}).items():
+        if name.startswith(symbol_prefix):
+            return v["hbm_bytes_per_dispatch"]
+    return None
+
+
+# ---- CPU baseline --------------------------------------------------------------
+
+def cpu_baseline(specs, host_tensors, tokens):
+    """The oracle (quantize + block-scaled GEMM, all three modes) on the first
+    `tokens` tokens of every linear layer; GEMM FLOP of that slice / time."""
+    import numpy as np
+    import oracle
+    import synth
+    oracle.build(force=False)
+    flops = 0.0
+    t0 = time.perf_counter()
+    for spec, t in zip(specs, host_tensors):
+        x = synth.bits(t["x"][:tokens])
+        w = synth.bits(t["w"])
+        dy = synth.bits(t["dy"][:tokens])
+        qx, sx = oracle.quant_rowwise(x)
+        qtx, stx = oracle.quant_colwise(x)
+        qw, qtw, sw = oracle.quant_weight(w)
+        qdy, sdy = oracle.quant_rowwise(dy)
+        qtdy, stdy = oracle.quant_colwise(dy)
+        oracle.gemm_blockscaled(oracle.MODE_FWD, qx, sx, qw, sw)
+        oracle.gemm_blockscaled(oracle.MODE_DGRAD, qdy, sdy, qtw, sw)
+        oracle.gemm_blockscaled(oracle.MODE_WGRAD, qtdy, stdy, qtx, stx)
+        tp = qtx.shape[1]
+        flops += 2.0 * tokens * spec.d_out * spec.d_in * 2 + 2.0 * spec.d_out * spec.d_in * tp
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.get_threads(),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": (f"first {tokens} tokens of each of the {len(specs)} linear layers: "
+                       f"quantize X, dY (1x128 and 128x1), W (128x128) and the FWD, DGRAD and "
+                       f"WGRAD GEMMs of that slice ({flops / 1e9:.1f} GFLOP)")}
+
+
+# ---- main --------------------------------------------------------------------------
+
+def copy_calibration():
+    import torch
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print("copy calibration: 3 x 1 GiB device-to-device copies")
+
+
+def main():
+    args = parse_args()
+    if args.ingest_pmc:
+        ingest_pmc(*args.ingest_pmc)
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: the FP8 linear-layer path is measured on a single "
+              f"MI355X (--gpus {args.gpus} is not supported; data-parallel sharding only "
+              f"replicates this per-GPU work).", file=sys.stderr)
+        return 2
+    import torch
+    if args.copy_calibration:
+        copy_calibration()
+        return 0
+
+    import fp8_block_scaled_tile_amd as pf
+    import synth
+
+    wl = synth.workload(args.workload)
+    specs = list(wl.linears)
+    t_gen = time.perf_counter()
+    host_tensors = [synth.linear_inputs(s, seed=args.seed) for s in specs]
+    gen_s = time.perf_counter() - t_gen
+    layers = [Linear(torch, pf, s, t) for s, t in zip(specs, host_tensors)]
+    if args.no_cpu_baseline or args.cpu_tokens <= 0:
+        del host_tensors
+        host_tensors = None
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+    step_flops = sum(L.flops() for L in layers)
+
+    for _ in range(args.warmup):
+        run_step(pf, layers, stream)
+    torch.cuda.synchronize()
+
+    # timed region: K steps, every launch bracketed by events on its stream
+    events = []
+
+    def rec(name, work):
+        ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        events.append((name, work, ev))
+        return ev
+
+    pool = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run_step(pf, layers, stream, rec)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms_per_step = wall * 1e3 / args.steps
+    value = step_flops / (wall / args.steps) / 1e12
+
+    per = {}
+    for name, work, (e0, e1) in events:
+        d = per.setdefault(name, {"launches": 0, "ms": 0.0, "work": 0.0})
+        d["launches"] += 1
+        d["ms"] += e0.elapsed_time(e1)
+        d["work"] += work
+    kernels = {}
+    for name, d in per.items():
+        avg_ms = d["ms"] / d["launches"]
+        avg_work = d["work"] / d["launches"]
+        if name.startswith("gemm"):
+            rate = avg_work / (avg_ms * 1e-3) / 1e12
+            kernels[name] = {"symbol": KERNEL_SYMBOLS[name], "launches_per_step": d["launches"] // args.steps,
+                             "avg_ms": round(avg_ms, 4), "avg_gflop": round(avg_work / 1e9, 2),
+                             "tflops": round(rate, 1), "frac_fp8_peak": round(rate / FP8_PEAK_TFLOPS, 4),
+                             "ms_per_step": round(d["ms"] / args.steps, 4)}
+        else:
+            rate = avg_work / (avg_ms * 1e-3) / 1e9
+            kernels[name] = {"symbol": KERNEL_SYMBOLS[name], "launches_per_step": d["launches"] // args.steps,
+                             "avg_ms": round(avg_ms, 4), "avg_mb": round(avg_work / 1e6, 2),
+                             "gbps": round(rate, 1), "frac_hbm_peak": round(rate / HBM_PEAK_GBPS, 4),
+                             "ms_per_step": round(d["ms"] / args.steps, 4)}
+    dom = max((k for k in kernels if k.startswith("gemm") and "splitk" not in k),
+              key=lambda k: kernels[k]["ms_per_step"])
+    dk = kernels[dom]
+    traffic = traffic_for(dk["symbol"].replace("void ", ""))
+    roofline = {"bound": "mfma", "achieved": dk["tflops"], "peak": FP8_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(dk["tflops"] / FP8_PEAK_TFLOPS, 4),
+                "traffic": traffic, "kernel": dk["symbol"], "launch_class": dom,
+                "algorithmic_gflop_per_launch": dk["avg_gflop"], "avg_ms": dk["avg_ms"]}
+    gemm_ms = sum(v["ms_per_step"] for k, v in kernels.items() if k.startswith("gemm"))
+    quant_ms = sum(v["ms_per_step"] for k, v in kernels.items() if k.startswith("quant"))
+
+    cpu = None
+    if host_tensors is not None:
+        for L in layers:     # free nothing on the device; the oracle runs on the host
+            pass
+        cpu = cpu_baseline(specs, host_tensors, args.cpu_tokens)
+
+    spec0 = specs[0]
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": spec0.tokens, "hidden": 2048, "heads": 16,
+                   "ffn": 8192, "linears": {s.name: [s.d_in, s.d_out] for s in specs},
+                   "gemm_tflop_per_step": round(step_flops / 1e12, 4),
+                   "parallelism": "single GPU"},
+        "pct_of_fp8_peak": round(100.0 * value / FP8_PEAK_TFLOPS, 2),
+        "gemm_only_tflops": round(step_flops / (gemm_ms * 1e-3) / 1e12, 1) if gemm_ms else None,
+        "gemm_ms_per_step": round(gemm_ms, 4),
+        "quant_ms_per_step": round(quant_ms, 4),
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+        "input_generation_s": round(gen_s, 1),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,190 @@
+"""Fine-grained block-quantized FP8 linear layer for AMD MI355X (gfx950).
+
+Python binding of ``libpuro_fp8.so`` (C ABI in ``include/puro_fp8.h``).  This
+module only marshals arguments: every step of the quantizers and GEMM runs in
+the library's hand-written HIP kernels.  PyTorch supplies device memory and
+the current stream; codes travel as ``torch.uint8``.
+
+Two layers:
+
+* ``puro_fp8_*`` -- the C entry points under their own names, taking raw
+  device pointers (ints) and returning the status code.
+* ``quant_act`` / ``quant_weight`` / ``gemm_blockscaled`` -- allocate the
+  outputs with torch, call the entry points on the current stream, and raise
+  ``PuroError`` with the library's status string on failure.
+
+Importing this package does not touch the GPU.  If the shared library is
+missing the import fails loudly; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from . import _lib
+
+__all__ = [
+    "PuroError", "GEMM_FWD", "GEMM_DGRAD", "GEMM_WGRAD", "OUT_BF16", "OUT_FP32",
+    "puro_fp8_quant_act", "puro_fp8_quant_weight", "puro_fp8_gemm_blockscaled",
+    "puro_fp8_gemm_workspace_bytes", "puro_fp8_status_string", "puro_fp8_abi_version",
+    "puro_fp8_probe_encode", "quant_act", "quant_weight", "gemm_blockscaled",
+    "library_path",
+]
+
+GEMM_FWD, GEMM_DGRAD, GEMM_WGRAD = 0, 1, 2
+OUT_BF16, OUT_FP32 = 0, 1
+PURO_OK = 0
+
+
+class PuroError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = int(status)
+        super().__init__(puro_fp8_status_string(status))
+
+
+def library_path() -> str:
+    return _lib.path()
+
+
+# ---- the C entry points ------------------------------------------------------
+
+def puro_fp8_quant_act(x, rows, cols, q, s, qt, st, stream) -> int:
+    return _lib.get().puro_fp8_quant_act(x, rows, cols, q, s, qt, st, stream)
+
+
+def puro_fp8_quant_weight(w, n, k, q, qt, s, stream) -> int:
+    return _lib.get().puro_fp8_quant_weight(w, n, k, q, qt, s, stream)
+
+
+def puro_fp8_gemm_blockscaled(mode, M, N, K, a, sa, b, sb, c, c_dtype, accumulate, workspace,
+                              workspace_bytes, stream) -> int:
+    return _lib.get().puro_fp8_gemm_blockscaled(mode, M, N, K, a, sa, b, sb, c, c_dtype,
+                                                accumulate, workspace, workspace_bytes, stream)
+
+
+def puro_fp8_gemm_workspace_bytes(mode, M, N, K) -> int:
+    return int(_lib.get().puro_fp8_gemm_workspace_bytes(mode, M, N, K))
+
+
+def puro_fp8_status_string(status) -> str:
+    return _lib.get().puro_fp8_status_string(int(status)).decode()
+
+
+def puro_fp8_abi_version() -> int:
+    return int(_lib.get().puro_fp8_abi_version())
+
+
+def puro_fp8_probe_encode(first_bits, n, out, stream) -> int:
+    return _lib.get().puro_fp8_probe_encode(first_bits, n, out, stream)
+
+
+# ---- torch-facing wrappers --------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc):
+    if rc != PURO_OK:
+        raise PuroError(rc)
+
+
+def _need(t, dtype, shape, name):
+    torch = _torch()
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous() or t.device.type != "cuda":
+        raise ValueError(f"{name}: expected a contiguous CUDA tensor")
+    return t
+
+
+def quant_act(x, row: bool = True, col: bool = False, stream=None):
+    """1x128 (row) and/or 128x1 (col, transposed) quantization of a bf16
+    [rows, cols] CUDA tensor.  Returns a dict with ``q`` u8 [rows, cols] and
+    ``s`` f32 [cols/128, rows] (row), ``qt`` u8 [cols, rows_pad] and ``st``
+    f32 [rows_pad/128, cols] (col)."""
+    torch = _torch()
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise TypeError("quant_act expects a 2-D bfloat16 tensor")
+    x = x.contiguous()
+    rows, cols = x.shape
+    rp = (rows + 127) // 128 * 128
+    out = {}
+    dev = x.device
+    if row:
+        out["q"] = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+        out["s"] = torch.empty((cols // 128, rows), dtype=torch.float32, device=dev)
+    if col:
+        out["qt"] = torch.empty((cols, rp), dtype=torch.uint8, device=dev)
+        out["st"] = torch.empty((rp // 128, cols), dtype=torch.float32, device=dev)
+    _check(puro_fp8_quant_act(_ptr(x), rows, cols, _ptr(out.get("q")), _ptr(out.get("s")),
+                              _ptr(out.get("qt")), _ptr(out.get("st")), _stream(stream)))
+    return out
+
+
+def quant_weight(w, transpose: bool = True, stream=None):
+    """128x128 block quantization of a bf16 [n, k] CUDA tensor.  Returns a dict
+    with ``q`` u8 [n, k], ``s`` f32 [n/128, k/128] and ``qt`` u8 [k, n]."""
+    torch = _torch()
+    if w.dtype != torch.bfloat16 or w.dim() != 2:
+        raise TypeError("quant_weight expects a 2-D bfloat16 tensor")
+    w = w.contiguous()
+    n, k = w.shape
+    dev = w.device
+    out = {"q": torch.empty((n, k), dtype=torch.uint8, device=dev),
+           "s": torch.empty((n // 128, k // 128), dtype=torch.float32, device=dev)}
+    if transpose:
+        out["qt"] = torch.empty((k, n), dtype=torch.uint8, device=dev)
+    _check(puro_fp8_quant_weight(_ptr(w), n, k, _ptr(out["q"]), _ptr(out.get("qt")),
+                                 _ptr(out["s"]), _stream(stream)))
+    return out
+
+
+def gemm_blockscaled(mode: int, a, sa, b, sb, out_dtype=None, out=None, accumulate=False,
+                     workspace=None, stream=None):
+    """Block-scaled FP8 GEMM: C[M, N] (+)= blocks of a[M, K] . b[N, K]^T with
+    scales sa [K/128, M] and sb (see the C header for each mode's layout)."""
+    torch = _torch()
+    M, K = a.shape
+    N = b.shape[0]
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else torch.bfloat16
+    c_dtype = OUT_FP32 if out_dtype == torch.float32 else OUT_BF16
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be bfloat16 or float32")
+    _need(a, torch.uint8, (M, K), "a")
+    _need(b, torch.uint8, (N, K), "b")
+    _need(sa, torch.float32, (K // 128, M), "sa")
+    sb_shape = {GEMM_FWD: (N // 128, K // 128), GEMM_DGRAD: (K // 128, N // 128),
+                GEMM_WGRAD: (K // 128, N)}[mode]
+    _need(sb, torch.float32, sb_shape, "sb")
+    if out is None:
+        out = (torch.zeros if accumulate else torch.empty)((M, N), dtype=out_dtype, device=a.device)
+    else:
+        _need(out, out_dtype, (M, N), "out")
+    need = puro_fp8_gemm_workspace_bytes(mode, M, N, K)
+    ws_ptr, ws_bytes = None, 0
+    if need:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=a.device)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check(puro_fp8_gemm_blockscaled(mode, M, N, K, _ptr(a), _ptr(sa), _ptr(b), _ptr(sb),
+                                     _ptr(out), c_dtype, 1 if accumulate else 0, ws_ptr, ws_bytes,
+                                     _stream(stream)))
+    return out

@@ -1,0 +1,53 @@
+"""Loader of the in-tree libpuro_fp8.so with the C signatures of
+include/puro_fp8.h.  Fails loudly when the library has not been built."""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_PATH = os.path.join(_HERE, "libpuro_fp8.so")
+_lock = threading.Lock()
+_handle = None
+
+EXPORTS = (
+    "puro_fp8_quant_act", "puro_fp8_quant_weight", "puro_fp8_gemm_blockscaled",
+    "puro_fp8_gemm_workspace_bytes", "puro_fp8_status_string", "puro_fp8_abi_version",
+    "puro_fp8_probe_encode",
+)
+
+
+def path() -> str:
+    return _PATH
+
+
+def get():
+    global _handle
+    with _lock:
+        if _handle is not None:
+            return _handle
+        if not os.path.exists(_PATH):
+            raise ImportError(f"{_PATH} is missing: build it with "
+                              "`python -m fp8_block_scaled_tile_amd.build` (hipcc, gfx950)")
+        lib = ctypes.CDLL(_PATH)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        I = ctypes.c_int
+        lib.puro_fp8_quant_act.restype = I
+        lib.puro_fp8_quant_act.argtypes = [P, I64, I64, P, P, P, P, P]
+        lib.puro_fp8_quant_weight.restype = I
+        lib.puro_fp8_quant_weight.argtypes = [P, I64, I64, P, P, P, P]
+        lib.puro_fp8_gemm_blockscaled.restype = I
+        lib.puro_fp8_gemm_blockscaled.argtypes = [I, I64, I64, I64, P, P, P, P, P, I, I, P,
+                                                  ctypes.c_size_t, P]
+        lib.puro_fp8_gemm_workspace_bytes.restype = ctypes.c_size_t
+        lib.puro_fp8_gemm_workspace_bytes.argtypes = [I, I64, I64, I64]
+        lib.puro_fp8_status_string.restype = ctypes.c_char_p
+        lib.puro_fp8_status_string.argtypes = [I]
+        lib.puro_fp8_abi_version.restype = I
+        lib.puro_fp8_abi_version.argtypes = []
+        lib.puro_fp8_probe_encode.restype = I
+        lib.puro_fp8_probe_encode.argtypes = [ctypes.c_uint32, I64, P, P]
+        _handle = lib
+        return lib

@@ -1,0 +1,82 @@
+"""Build libpuro_fp8.so (hand-written HIP for gfx950) in-tree with hipcc.
+
+Every source under csrc/ is compiled for gfx950 only, without fast-math
+(the quantizer's per-tile divisions must stay correctly rounded), with the
+packed-FP32 VALU forms disabled, then linked into one shared library next to
+this file.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_NAME = "libpuro_fp8.so"
+LIB_PATH = os.path.join(HERE, LIB_NAME)
+ARCH = "gfx950"
+
+SOURCES = ["abi.hip", "quant.hip", "gemm.hip"]
+
+COMMON_FLAGS = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-fno-fast-math",
+    "-ffp-contract=off",            # FMAs only where written explicitly
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall",
+    "-Wno-unused-command-line-argument",
+    f"-I{INCLUDE}",
+    f"-I{CSRC}",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass warns that it does not know the packed-fp32 feature
+    noise = ("packed-fp32-ops", "is not a recognized feature for this target")
+    err = "\n".join(l for l in res.stderr.splitlines() if not any(n in l for n in noise))
+    if res.returncode != 0:
+        raise RuntimeError(f"command failed ({res.returncode}): {' '.join(cmd)}\n{err}")
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+
+
+def build(verbose: bool = False, jobs: int = 4) -> str:
+    """Compile every HIP source for gfx950 and link libpuro_fp8.so in-tree."""
+    cc = hipcc()
+    with tempfile.TemporaryDirectory(prefix="puro_build_") as tmp:
+        objs = []
+        cmds = []
+        for src in SOURCES:
+            obj = os.path.join(tmp, src.replace(".hip", ".o"))
+            objs.append(obj)
+            cmds.append([cc, *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(cmds)))) as ex:
+            list(ex.map(lambda c: _run(c, verbose), cmds))
+        tmp_lib = os.path.join(tmp, LIB_NAME)
+        _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib], verbose)
+        shutil.copyfile(tmp_lib, LIB_PATH + ".tmp")
+        os.replace(LIB_PATH + ".tmp", LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,178 @@
+// abi.hip -- the extern "C" entry points declared in include/puro_fp8.h:
+// argument validation (synchronous, before any enqueue), then the launch on
+// the caller's stream.  No exception crosses the boundary.
+#include "puro_fp8.h"
+
+#include <hip/hip_runtime.h>
+
+#include <limits>
+
+#include "launch.hpp"
+
+namespace {
+
+constexpr int64_t kMaxDim = std::numeric_limits<int32_t>::max();
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+puro_status_t from_hip(hipError_t e) { return e == hipSuccess ? PURO_OK : PURO_ERR_HIP; }
+
+template <typename F>
+puro_status_t guarded(F&& f)
+{
+    try {
+        return f();
+    } catch (...) {
+        return PURO_ERR_INTERNAL;
+    }
+}
+
+puro_status_t check_act(const void* x, int64_t rows, int64_t cols, const uint8_t* q,
+                        const float* s, const uint8_t* qt, const float* st)
+{
+    if (rows < 0 || cols <= 0 || cols % 128 != 0 || cols > kMaxDim)
+        return PURO_ERR_BAD_SHAPE;
+    // grid limits: rows_pad/128 blocks in x, cols/128 in y (< 65536)
+    if ((rows + 127) / 128 > kMaxDim || cols / 128 > 65535)
+        return PURO_ERR_BAD_SHAPE;
+    if (rows == 0)
+        return PURO_OK;                      // empty input: nothing to do
+    if (!x)
+        return PURO_ERR_NULL_POINTER;
+    const bool row = q || s, col = qt || st;
+    if (!row && !col)
+        return PURO_ERR_NULL_POINTER;
+    if ((q == nullptr) != (s == nullptr) || (qt == nullptr) != (st == nullptr))
+        return PURO_ERR_NULL_POINTER;
+    if (!aligned16(x) || (q && !aligned16(q)) || (s && !aligned16(s)) || (qt && !aligned16(qt)) ||
+        (st && !aligned16(st)))
+        return PURO_ERR_MISALIGNED;
+    return PURO_OK;
+}
+
+puro_status_t check_weight(const void* w, int64_t n, int64_t k, const uint8_t* q,
+                           const uint8_t* qt, const float* s)
+{
+    if (n <= 0 || k <= 0 || n % 128 != 0 || k % 128 != 0 || n > kMaxDim || k > kMaxDim ||
+        k / 128 > 65535)
+        return PURO_ERR_BAD_SHAPE;
+    if (!w || !q || !s)
+        return PURO_ERR_NULL_POINTER;
+    if (!aligned16(w) || !aligned16(q) || !aligned16(s) || (qt && !aligned16(qt)))
+        return PURO_ERR_MISALIGNED;
+    return PURO_OK;
+}
+
+bool gemm_shape_ok(int64_t M, int64_t N, int64_t K)
+{
+    if (M < 0 || N <= 0 || K <= 0 || N % 128 != 0 || K % 128 != 0)
+        return false;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim)
+        return false;
+    // the launch grid holds tiles_m * tiles_n * splits work-groups (int)
+    const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+    return tiles * 8 <= kMaxDim;
+}
+
+}  // namespace
+
+extern "C" {
+
+puro_status_t puro_fp8_quant_act(const void* x, int64_t rows, int64_t cols, uint8_t* q, float* s,
+                                 uint8_t* qt, float* st, void* stream)
+{
+    return guarded([&]() -> puro_status_t {
+        const puro_status_t rc = check_act(x, rows, cols, q, s, qt, st);
+        if (rc != PURO_OK || rows == 0)
+            return rc;
+        return from_hip(puro::launch_quant_act(x, rows, cols, q, s, qt, st,
+                                               static_cast<hipStream_t>(stream)));
+    });
+}
+
+puro_status_t puro_fp8_quant_weight(const void* w, int64_t n, int64_t k, uint8_t* q, uint8_t* qt,
+                                    float* s, void* stream)
+{
+    return guarded([&]() -> puro_status_t {
+        const puro_status_t rc = check_weight(w, n, k, q, qt, s);
+        if (rc != PURO_OK)
+            return rc;
+        return from_hip(puro::launch_quant_weight(w, n, k, q, qt, s,
+                                                  static_cast<hipStream_t>(stream)));
+    });
+}
+
+size_t puro_fp8_gemm_workspace_bytes(puro_gemm_mode_t mode, int64_t M, int64_t N, int64_t K)
+{
+    if ((int)mode < 0 || (int)mode > 2 || !gemm_shape_ok(M, N, K) || M == 0)
+        return 0;
+    return puro::gemm_workspace_bytes((int)mode, M, N, K);
+}
+
+puro_status_t puro_fp8_gemm_blockscaled(puro_gemm_mode_t mode, int64_t M, int64_t N, int64_t K,
+                                        const uint8_t* a, const float* sa, const uint8_t* b,
+                                        const float* sb, void* c, puro_out_dtype_t c_dtype,
+                                        int accumulate, void* workspace, size_t workspace_bytes,
+                                        void* stream)
+{
+    return guarded([&]() -> puro_status_t {
+        if ((int)mode < 0 || (int)mode > 2)
+            return PURO_ERR_BAD_ENUM;
+        if ((int)c_dtype != PURO_OUT_BF16 && (int)c_dtype != PURO_OUT_FP32)
+            return PURO_ERR_BAD_ENUM;
+        if (accumulate && c_dtype != PURO_OUT_FP32)
+            return PURO_ERR_BAD_ENUM;
+        if (!gemm_shape_ok(M, N, K))
+            return PURO_ERR_BAD_SHAPE;
+        if (M == 0)
+            return PURO_OK;
+        if (!a || !sa || !b || !sb || !c)
+            return PURO_ERR_NULL_POINTER;
+        if (!aligned16(a) || !aligned16(sa) || !aligned16(b) || !aligned16(sb) || !aligned16(c))
+            return PURO_ERR_MISALIGNED;
+        const size_t need = puro::gemm_workspace_bytes((int)mode, M, N, K);
+        if (need > 0) {
+            if (!workspace || workspace_bytes < need)
+                return PURO_ERR_WORKSPACE;
+            if (!aligned16(workspace))
+                return PURO_ERR_MISALIGNED;
+        }
+        return from_hip(puro::launch_gemm((int)mode, M, N, K, a, sa, b, sb, c,
+                                          c_dtype == PURO_OUT_FP32, accumulate ? 1 : 0, workspace,
+                                          static_cast<hipStream_t>(stream)));
+    });
+}
+
+puro_status_t puro_fp8_probe_encode(uint32_t first_bits, int64_t n, uint8_t* out, void* stream)
+{
+    return guarded([&]() -> puro_status_t {
+        if (n < 0)
+            return PURO_ERR_BAD_SHAPE;
+        if (n == 0)
+            return PURO_OK;
+        if (!out)
+            return PURO_ERR_NULL_POINTER;
+        return from_hip(puro::launch_probe_encode(first_bits, n, out,
+                                                  static_cast<hipStream_t>(stream)));
+    });
+}
+
+const char* puro_fp8_status_string(puro_status_t status)
+{
+    switch (status) {
+    case PURO_OK:                return "PURO_OK: success";
+    case PURO_ERR_NULL_POINTER:  return "PURO_ERR_NULL_POINTER: a required pointer is NULL";
+    case PURO_ERR_BAD_SHAPE:     return "PURO_ERR_BAD_SHAPE: size out of range or not a multiple of 128";
+    case PURO_ERR_MISALIGNED:    return "PURO_ERR_MISALIGNED: a pointer is not 16-byte aligned";
+    case PURO_ERR_BAD_ENUM:      return "PURO_ERR_BAD_ENUM: unknown mode or dtype, or a bad combination";
+    case PURO_ERR_WORKSPACE:     return "PURO_ERR_WORKSPACE: workspace smaller than required";
+    case PURO_ERR_UNIMPLEMENTED: return "PURO_ERR_UNIMPLEMENTED: not supported by this build";
+    case PURO_ERR_HIP:           return "PURO_ERR_HIP: the HIP runtime rejected a launch";
+    case PURO_ERR_INTERNAL:      return "PURO_ERR_INTERNAL: unexpected internal failure";
+    }
+    return "unknown puro_status_t";
+}
+
+int puro_fp8_abi_version(void) { return PURO_FP8_ABI_VERSION; }
+
+}  // extern "C"

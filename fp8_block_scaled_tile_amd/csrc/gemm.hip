@@ -1,0 +1,417 @@
+// gemm.hip -- block-scaled FP8 GEMM on gfx950 FP8 MFMA.
+//
+// The main linear-layer GEMMs of the recipe run on FP8 with fine-grained
+// block scales (arXiv report "Puro-2B" section 2.1; training.farm blog
+// section "FP8").  Every operand is E4M3 codes with one FP32 scale per
+// 128-deep K-block of each row (activations) or per 128x128 block (weights),
+// so the product is
+//     C[m][n] = sum_kb sA(kb, m) * sB(kb, n) * P_kb[m][n],
+//     P_kb    = sum over the 128 k of block kb of dec(a[m][k]) * dec(b[n][k]).
+//
+// Design (gfx950, 256 CUs in 8 XCDs, 160 KB LDS per CU):
+//  * One workgroup = 512 threads (8 waves, 2 per SIMD) computes a 256x256
+//    tile of C.  Each K-step is exactly one scale block (128 deep): A and B
+//    slices of 256x128 bytes are staged in LDS, double buffered (128 KB).
+//  * Each wave owns a 128(M) x 64(N) sub-tile as 8x4 MFMA tiles of 16x16.
+//    One v_mfma_f32_16x16x128_f8f6f4 covers a whole K-block, so the partial
+//    product P_kb of a 16x16 tile comes out of a single instruction and is
+//    folded into the FP32 accumulator with one FMA per element:
+//        acc = fma(P_kb, sA*sB, acc).
+//  * The MFMA is issued with the B-side fragment as its first operand, so
+//    each lane's 4 accumulator rows are 4 consecutive n of one m: the A-side
+//    scale sA(kb, m) is one value per lane per tile, and in FWD / DGRAD sB is
+//    constant over the wave's 64 columns (they sit inside one 128-wide
+//    weight block).  WGRAD's sB varies per column: one extra multiply.
+//  * LDS rows are 128 bytes with the 16-byte chunk index XOR-swizzled by
+//    (row & 7); fragment reads (16 rows x 32 bytes per instruction group)
+//    and the staging writes are then bank-conflict free.
+//  * Workgroup ids are remapped so the tiles that run concurrently on one
+//    XCD form a compact 8(M) x 4(N) group sharing that XCD's L2.
+//  * Small-output problems split K across workgroups; the FP32 partials go
+//    to the caller's workspace and a second kernel sums them in a fixed
+//    order (deterministic).
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace puro {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int BM = 256;
+constexpr int BN = 256;
+constexpr int BK = 128;
+constexpr int NTHREADS = 512;
+constexpr int WM = 128;              // wave tile rows (M)
+constexpr int WN = 64;               // wave tile cols (N)
+constexpr int TM = WM / 16;          // 8 MFMA tiles along M
+constexpr int TN = WN / 16;          // 4 MFMA tiles along N
+constexpr int TILE_BYTES = BM * BK;  // 32 KB per operand slice
+constexpr int GROUP_M = 8;
+
+enum { MODE_FWD = 0, MODE_DGRAD = 1, MODE_WGRAD = 2 };
+enum { OUT_BF16 = 0, OUT_FP32 = 1, OUT_FP32_ACC = 2, OUT_PARTIAL = 3 };
+
+__device__ __forceinline__ int lds_off(int row, int chunk)
+{
+    return row * BK + ((chunk ^ (row & 7)) << 4);
+}
+
+// 32-byte MFMA operand fragment of a 16x128 slice starting at row `base`:
+// lane l holds row base + (l & 15), logical chunks 2*(l>>4) and 2*(l>>4)+1.
+// The A-side and B-side fragments use the same k <-> (lane, byte) mapping, so
+// every product pairs a[m][k] with b[n][k] whatever order the hardware sums in.
+__device__ __forceinline__ v8i load_frag(const uint8_t* lds, int base, int lane)
+{
+    const int row = base + (lane & 15);
+    const int c0 = 2 * (lane >> 4);
+    const uint4 lo = *reinterpret_cast<const uint4*>(lds + lds_off(row, c0));
+    const uint4 hi = *reinterpret_cast<const uint4*>(lds + lds_off(row, c0 + 1));
+    v8i f;
+    f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
+    f[4] = (int)hi.x; f[5] = (int)hi.y; f[6] = (int)hi.z; f[7] = (int)hi.w;
+    return f;
+}
+
+template <int MODE, int OUT>
+__global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ SA,
+    const uint8_t* __restrict__ B, const float* __restrict__ SB,
+    void* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n, int splits,
+    int kb_per_split)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][TILE_BYTES];
+    // Scales of the staged K-block: sA for the tile's 256 rows; sB for its
+    // 256 columns (WGRAD) or its two 128-wide weight blocks (FWD / DGRAD).
+    __shared__ __attribute__((aligned(16))) float lds_sa[2][BM];
+    __shared__ __attribute__((aligned(16))) float lds_sb[2][BN];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 2;        // 0..1
+    const int wn = wave & 3;         // 0..3
+
+    // ---- tile assignment: XCD-compact, grouped along M -------------------
+    const int total = tiles_m * tiles_n * splits;
+    int w = blockIdx.x;
+    if ((total & 7) == 0)
+        w = (w & 7) * (total >> 3) + (w >> 3);
+    const int tiles = tiles_m * tiles_n;
+    const int split = w / tiles;
+    const int tile = w - split * tiles;
+    const int group_size = GROUP_M * tiles_n;
+    const int group = tile / group_size;
+    const int first_m = group * GROUP_M;
+    const int gm = min(tiles_m - first_m, GROUP_M);
+    const int in_group = tile - group * group_size;
+    const int tile_m = first_m + in_group % gm;
+    const int tile_n = in_group / gm;
+    const int m0 = tile_m * BM;
+    const int n0 = tile_n * BN;
+
+    const int KB = K / BK;
+    const int kb_begin = split * kb_per_split;
+    const int kb_end = min(KB, kb_begin + kb_per_split);
+
+    // ---- global -> register staging map: 4 chunks of A and of B ----------
+    const int lrow = tid >> 3;       // 0..63
+    const int lchunk = tid & 7;
+    // 32-bit byte offsets of this thread's 4 A rows and 4 B rows (rows past
+    // the end are clamped to the last row; their results are never stored).
+    // With a uniform 64-bit base per K-block the loads use the scalar-base +
+    // 32-bit vector-offset addressing form.
+    const uint32_t a_off0 = (uint32_t)min(m0 + lrow, M - 1) * (uint32_t)K + 16u * lchunk;
+    const uint32_t a_off1 = (uint32_t)min(m0 + lrow + 64, M - 1) * (uint32_t)K + 16u * lchunk;
+    const uint32_t a_off2 = (uint32_t)min(m0 + lrow + 128, M - 1) * (uint32_t)K + 16u * lchunk;
+    const uint32_t a_off3 = (uint32_t)min(m0 + lrow + 192, M - 1) * (uint32_t)K + 16u * lchunk;
+    const uint32_t b_off0 = (uint32_t)min(n0 + lrow, N - 1) * (uint32_t)K + 16u * lchunk;
+    const uint32_t b_off1 = (uint32_t)min(n0 + lrow + 64, N - 1) * (uint32_t)K + 16u * lchunk;
+    const uint32_t b_off2 = (uint32_t)min(n0 + lrow + 128, N - 1) * (uint32_t)K + 16u * lchunk;
+    const uint32_t b_off3 = (uint32_t)min(n0 + lrow + 192, N - 1) * (uint32_t)K + 16u * lchunk;
+    const int st_off0 = lds_off(lrow, lchunk);
+    const int st_off1 = lds_off(lrow + 64, lchunk);
+    const int st_off2 = lds_off(lrow + 128, lchunk);
+    const int st_off3 = lds_off(lrow + 192, lchunk);
+    uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
+
+#define PURO_LOAD_TILE(kb)                                                          \
+    do {                                                                            \
+        const uint8_t* ab = A + (size_t)(kb) * BK;                                  \
+        const uint8_t* bb = B + (size_t)(kb) * BK;                                  \
+        ra0 = *reinterpret_cast<const uint4*>(ab + a_off0);                         \
+        ra1 = *reinterpret_cast<const uint4*>(ab + a_off1);                         \
+        ra2 = *reinterpret_cast<const uint4*>(ab + a_off2);                         \
+        ra3 = *reinterpret_cast<const uint4*>(ab + a_off3);                         \
+        rb0 = *reinterpret_cast<const uint4*>(bb + b_off0);                         \
+        rb1 = *reinterpret_cast<const uint4*>(bb + b_off1);                         \
+        rb2 = *reinterpret_cast<const uint4*>(bb + b_off2);                         \
+        rb3 = *reinterpret_cast<const uint4*>(bb + b_off3);                         \
+    } while (0)
+#define PURO_STORE_TILE(buf)                                                        \
+    do {                                                                            \
+        *reinterpret_cast<uint4*>(&lds[buf][0][st_off0]) = ra0;                     \
+        *reinterpret_cast<uint4*>(&lds[buf][0][st_off1]) = ra1;                     \
+        *reinterpret_cast<uint4*>(&lds[buf][0][st_off2]) = ra2;                     \
+        *reinterpret_cast<uint4*>(&lds[buf][0][st_off3]) = ra3;                     \
+        *reinterpret_cast<uint4*>(&lds[buf][1][st_off0]) = rb0;                     \
+        *reinterpret_cast<uint4*>(&lds[buf][1][st_off1]) = rb1;                     \
+        *reinterpret_cast<uint4*>(&lds[buf][1][st_off2]) = rb2;                     \
+        *reinterpret_cast<uint4*>(&lds[buf][1][st_off3]) = rb3;                     \
+    } while (0)
+
+    // ---- scales: staged through LDS with the tiles -------------------------
+    // Threads 0..63 fetch the tile's 256 sA values as float4; threads 64..127
+    // fetch sB (256 per-column values in WGRAD, two block scales otherwise).
+    const bool wave_active = (n0 + wn * WN) < N;
+    const int m_lane = m0 + wm * WM + (lane & 15);        // + 16*sm
+    const int n_lane = n0 + wn * WN + 4 * (lane >> 4);    // + 16*tn, 4 consecutive
+    float4 rs = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+
+#define PURO_LOAD_SCALES(kb)                                                        \
+    do {                                                                            \
+        if (tid < 64) {                                                             \
+            const int mm = m0 + 4 * tid;                                            \
+            const float* src = SA + (size_t)(kb) * M + mm;                          \
+            if (mm + 3 < M && ((M & 3) == 0)) {                                     \
+                rs = *reinterpret_cast<const float4*>(src);                         \
+            } else {                                                                \
+                rs.x = (mm + 0 < M) ? src[0] : 0.0f;                                \
+                rs.y = (mm + 1 < M) ? src[1] : 0.0f;                                \
+                rs.z = (mm + 2 < M) ? src[2] : 0.0f;                                \
+                rs.w = (mm + 3 < M) ? src[3] : 0.0f;                                \
+            }                                                                       \
+        } else if (tid < 128) {                                                     \
+            const int nn = n0 + 4 * (tid - 64);                                     \
+            if constexpr (MODE == MODE_WGRAD) {                                     \
+                if (nn < N)                                                         \
+                    rs = *reinterpret_cast<const float4*>(SB + (size_t)(kb) * N + nn); \
+            } else if (tid < 66) {                                                  \
+                const int nb = n0 / BK + (tid - 64);                                \
+                if (nb < N / BK) {                                                  \
+                    if constexpr (MODE == MODE_FWD)                                 \
+                        rs.x = SB[(size_t)nb * KB + (kb)];                          \
+                    else                                                            \
+                        rs.x = SB[(size_t)(kb) * (N / BK) + nb];                    \
+                }                                                                   \
+            }                                                                       \
+        }                                                                           \
+    } while (0)
+#define PURO_STORE_SCALES(buf)                                                      \
+    do {                                                                            \
+        if (tid < 64)                                                               \
+            *reinterpret_cast<float4*>(&lds_sa[buf][4 * tid]) = rs;                 \
+        else if (tid < 128)                                                         \
+            *reinterpret_cast<float4*>(&lds_sb[buf][4 * (tid - 64)]) = rs;          \
+    } while (0)
+
+    v4f acc[TM][TN];
+#pragma unroll
+    for (int sm = 0; sm < TM; ++sm)
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+            acc[sm][tn] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    if (kb_begin < kb_end) {
+        PURO_LOAD_TILE(kb_begin);
+        PURO_LOAD_SCALES(kb_begin);
+        PURO_STORE_TILE(0);
+        PURO_STORE_SCALES(0);
+        __syncthreads();
+    }
+
+    for (int kb = kb_begin; kb < kb_end; ++kb) {
+        const int cur = (kb - kb_begin) & 1;
+        const bool has_next = kb + 1 < kb_end;
+        if (has_next) {
+            PURO_LOAD_TILE(kb + 1);
+            PURO_LOAD_SCALES(kb + 1);
+        }
+
+        if (wave_active) {
+            const uint8_t* la = &lds[cur][0][0];
+            const uint8_t* lb = &lds[cur][1][0];
+            v8i bf[TN];
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn)
+                bf[tn] = load_frag(lb, wn * WN + 16 * tn, lane);
+            // FWD / DGRAD: the wave's 64 columns sit in one weight block.
+            const float sb_wave = lds_sb[cur][(wn * WN) / BK];
+            v4f sb_col[TN];
+            if constexpr (MODE == MODE_WGRAD) {
+#pragma unroll
+                for (int tn = 0; tn < TN; ++tn)
+                    sb_col[tn] = *reinterpret_cast<const v4f*>(
+                        &lds_sb[cur][wn * WN + 16 * tn + 4 * (lane >> 4)]);
+            }
+#pragma unroll
+            for (int sm = 0; sm < TM; ++sm) {
+                const v8i af = load_frag(la, wm * WM + 16 * sm, lane);
+                const float sa = lds_sa[cur][wm * WM + 16 * sm + (lane & 15)];
+#pragma unroll
+                for (int tn = 0; tn < TN; ++tn) {
+                    const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+                    const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        bf[tn], af, zero, 0, 0, 0, 0, 0, 0);
+                    if constexpr (MODE == MODE_WGRAD) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            acc[sm][tn][r] = __builtin_fmaf(p[r], sa * sb_col[tn][r], acc[sm][tn][r]);
+                    } else {
+                        const float sc = sa * sb_wave;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            acc[sm][tn][r] = __builtin_fmaf(p[r], sc, acc[sm][tn][r]);
+                    }
+                }
+            }
+        }
+
+        if (has_next) {
+            PURO_STORE_TILE(cur ^ 1);
+            PURO_STORE_SCALES(cur ^ 1);
+        }
+        __syncthreads();
+    }
+#undef PURO_LOAD_TILE
+#undef PURO_STORE_TILE
+#undef PURO_LOAD_SCALES
+#undef PURO_STORE_SCALES
+
+    // ---- epilogue ----------------------------------------------------------
+    if (!wave_active)
+        return;
+#pragma unroll
+    for (int sm = 0; sm < TM; ++sm) {
+        const int m = m_lane + 16 * sm;
+        if (m >= M)
+            continue;
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+            const int n = n_lane + 16 * tn;
+            const v4f v = acc[sm][tn];
+            const size_t idx = (size_t)m * N + n;
+            if constexpr (OUT == OUT_BF16) {
+                uint2 o;
+                o.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+                o.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(C) + idx) = o;
+            } else if constexpr (OUT == OUT_FP32) {
+                *reinterpret_cast<v4f*>(static_cast<float*>(C) + idx) = v;
+            } else if constexpr (OUT == OUT_FP32_ACC) {
+                v4f* dst = reinterpret_cast<v4f*>(static_cast<float*>(C) + idx);
+                *dst = *dst + v;
+            } else {
+                float* ws = static_cast<float*>(C) + (size_t)split * M * N;
+                *reinterpret_cast<v4f*>(ws + idx) = v;
+            }
+        }
+    }
+}
+
+// Sum of the split-K partials in split order, then the requested output.
+template <int OUT>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws,
+                                                            void* __restrict__ C, int64_t count4,
+                                                            int splits, int64_t plane)
+{
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count4; i += stride) {
+        v4f s = *reinterpret_cast<const v4f*>(ws + 4 * i);
+        for (int z = 1; z < splits; ++z)
+            s = s + *reinterpret_cast<const v4f*>(ws + (size_t)z * plane + 4 * i);
+        if constexpr (OUT == OUT_BF16) {
+            uint2 o;
+            o.x = f32_to_bf16_bits(s[0]) | (f32_to_bf16_bits(s[1]) << 16);
+            o.y = f32_to_bf16_bits(s[2]) | (f32_to_bf16_bits(s[3]) << 16);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(C) + 4 * i) = o;
+        } else if constexpr (OUT == OUT_FP32) {
+            *reinterpret_cast<v4f*>(static_cast<float*>(C) + 4 * i) = s;
+        } else {
+            v4f* dst = reinterpret_cast<v4f*>(static_cast<float*>(C) + 4 * i);
+            *dst = *dst + s;
+        }
+    }
+}
+
+// Split-K factor: only when the tile grid leaves most of the 256 CUs idle.
+// Picks the smallest split that best fills whole waves of 256 workgroups
+// while keeping at least 8 K-blocks per split.
+static int choose_splits(int64_t M, int64_t N, int64_t K)
+{
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    const int64_t KB = K / BK;
+    if (tiles >= 256 || KB < 16)
+        return 1;
+    int best = 1;
+    double best_eff = 0.0;
+    for (int s = 1; s <= 8; ++s) {
+        if (KB / s < 8)
+            break;
+        const int64_t units = tiles * s;
+        const int64_t waves = (units + 255) / 256;
+        const double eff = (double)units / (double)(waves * 256);
+        if (eff > best_eff + 1e-9) {
+            best_eff = eff;
+            best = s;
+        }
+    }
+    return best;
+}
+
+size_t gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K)
+{
+    (void)mode;
+    const int s = choose_splits(M, N, K);
+    return s > 1 ? (size_t)s * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
+template <int MODE>
+static hipError_t launch_mode(int out, const uint8_t* a, const float* sa, const uint8_t* b,
+                              const float* sb, void* c, void* ws, int M, int N, int K,
+                              int splits, hipStream_t stream)
+{
+    const int tiles_m = (M + BM - 1) / BM;
+    const int tiles_n = (N + BN - 1) / BN;
+    const int KB = K / BK;
+    const int kbps = (KB + splits - 1) / splits;
+    const dim3 grid((unsigned)(tiles_m * tiles_n * splits));
+    if (splits > 1) {
+        gemm_bs_kernel<MODE, OUT_PARTIAL><<<grid, NTHREADS, 0, stream>>>(
+            a, sa, b, sb, ws, M, N, K, tiles_m, tiles_n, splits, kbps);
+        const int64_t count4 = (int64_t)M * N / 4;
+        const int64_t blocks = (count4 + 255) / 256;
+        const unsigned rgrid = (unsigned)(blocks < 8192 ? blocks : 8192);
+        const float* wsf = static_cast<const float*>(ws);
+        if (out == OUT_BF16)
+            splitk_reduce_kernel<OUT_BF16><<<rgrid, 256, 0, stream>>>(wsf, c, count4, splits, (int64_t)M * N);
+        else if (out == OUT_FP32)
+            splitk_reduce_kernel<OUT_FP32><<<rgrid, 256, 0, stream>>>(wsf, c, count4, splits, (int64_t)M * N);
+        else
+            splitk_reduce_kernel<OUT_FP32_ACC><<<rgrid, 256, 0, stream>>>(wsf, c, count4, splits, (int64_t)M * N);
+        return hipGetLastError();
+    }
+    if (out == OUT_BF16)
+        gemm_bs_kernel<MODE, OUT_BF16><<<grid, NTHREADS, 0, stream>>>(a, sa, b, sb, c, M, N, K, tiles_m, tiles_n, 1, KB);
+    else if (out == OUT_FP32)
+        gemm_bs_kernel<MODE, OUT_FP32><<<grid, NTHREADS, 0, stream>>>(a, sa, b, sb, c, M, N, K, tiles_m, tiles_n, 1, KB);
+    else
+        gemm_bs_kernel<MODE, OUT_FP32_ACC><<<grid, NTHREADS, 0, stream>>>(a, sa, b, sb, c, M, N, K, tiles_m, tiles_n, 1, KB);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* a,
+                       const float* sa, const uint8_t* b, const float* sb, void* c, int out_fp32,
+                       int accumulate, void* ws, hipStream_t stream)
+{
+    const int out = out_fp32 ? (accumulate ? OUT_FP32_ACC : OUT_FP32) : OUT_BF16;
+    const int splits = choose_splits(M, N, K);
+    const int m = (int)M, n = (int)N, k = (int)K;
+    switch (mode) {
+    case MODE_FWD:   return launch_mode<MODE_FWD>(out, a, sa, b, sb, c, ws, m, n, k, splits, stream);
+    case MODE_DGRAD: return launch_mode<MODE_DGRAD>(out, a, sa, b, sb, c, ws, m, n, k, splits, stream);
+    default:         return launch_mode<MODE_WGRAD>(out, a, sa, b, sb, c, ws, m, n, k, splits, stream);
+    }
+}
+
+}  // namespace puro

@@ -1,0 +1,22 @@
+// launch.hpp -- internal host-side launchers (not part of the C ABI).  Each
+// expects arguments already validated by the C entry points in abi.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace puro {
+
+hipError_t launch_quant_act(const void* x, int64_t rows, int64_t cols, uint8_t* q, float* s,
+                            uint8_t* qt, float* st, hipStream_t stream);
+hipError_t launch_quant_weight(const void* w, int64_t n, int64_t k, uint8_t* q, uint8_t* qt,
+                               float* s, hipStream_t stream);
+hipError_t launch_probe_encode(uint32_t first, int64_t n, uint8_t* out, hipStream_t stream);
+
+size_t gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* a,
+                       const float* sa, const uint8_t* b, const float* sb, void* c, int out_fp32,
+                       int accumulate, void* ws, hipStream_t stream);
+
+}  // namespace puro

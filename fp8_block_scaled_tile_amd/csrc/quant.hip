@@ -1,0 +1,220 @@
+// quant.hip -- tile-wise FP8 (E4M3) quantizers for gfx950.
+//
+// Fine-grained block quantization of the linear-layer GEMM operands (arXiv
+// report "Puro-2B" section 2.1; training.farm blog section "FP8"): one FP32
+// scale per tile, s = amax/448, codes = E4M3(x * 448/amax).  Activations and
+// gradients use 1x128 tiles along the contraction dimension (row-wise) and,
+// for the weight-gradient GEMM, 128x1 tiles along tokens with the codes
+// stored transposed (column-wise); weights use 128x128 blocks.
+//
+// One 256-thread workgroup owns a 128x128 block of the input.  Thread t
+// covers columns 8*(t%16) .. +7 and rows 8*(t/16) .. +7 of the block, so each
+// input row of the block lives in one 16-lane DPP row: the 1x128 amax is a
+// four-step DPP maximum with no LDS traffic.  Every lane issues its eight
+// 16-byte loads up front; row-wise codes are stored straight from registers
+// (16 lanes write one 128-byte line); the transposed copy goes through an
+// XOR-swizzled 16 KB LDS tile and leaves as 16-byte stores.  The input is
+// read from HBM exactly once whatever combination of outputs is requested.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace puro {
+
+template <bool ROW, bool COL, bool WEIGHT, bool WT>
+__global__ __launch_bounds__(256) void quant_block_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_t,
+    uint8_t* __restrict__ q, float* __restrict__ s, uint8_t* __restrict__ qt,
+    float* __restrict__ st)
+{
+    constexpr bool TRANS = COL || WT;
+    __shared__ int colmax[COL ? 16 : 1][COL ? 128 : 1];
+    __shared__ float col_r[COL ? 128 : 1];
+    __shared__ float col_pre[COL ? 128 : 1];
+    __shared__ __attribute__((aligned(16))) uint8_t tbuf[TRANS ? 128 * 128 : 16];
+    __shared__ int wmax[16];
+
+    const int t = threadIdx.x;
+    const int qd = t & 15;       // column chunk of 8 elements
+    const int g = t >> 4;        // row group of 8 rows
+    const int64_t rb = blockIdx.x;
+    const int64_t cb = blockIdx.y;
+    const int64_t row0 = rb * 128 + 8 * g;
+    const int64_t col0 = cb * 128 + 8 * qd;
+
+    uint4 v[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const int64_t r = row0 + p;
+        if (r < rows)
+            v[p] = *reinterpret_cast<const uint4*>(x + r * cols + col0);
+        else
+            v[p] = make_uint4(0u, 0u, 0u, 0u);
+    }
+
+    // ---- 128x128 block scale (weights) ----------------------------------
+    TileQ wq = {0.0f, 0.0f, 1.0f};
+    if constexpr (WEIGHT) {
+        int m = 0;
+#pragma unroll
+        for (int p = 0; p < 8; ++p)
+            m = max(m, mag8(v[p]));
+        m = dpp_row_max(m);
+        if (qd == 0)
+            wmax[g] = m;
+        __syncthreads();
+        int bm = wmax[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i)
+            bm = max(bm, wmax[i]);
+        wq = tile_params(bm);
+        if (t == 0)
+            s[rb * (cols / 128) + cb] = wq.s;
+    }
+
+    // ---- codes in input orientation (1x128 tiles, or the weight block) --
+    if constexpr (ROW || WEIGHT) {
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const int64_t r = row0 + p;
+            TileQ tq = wq;
+            if constexpr (!WEIGHT)
+                tq = tile_params(dpp_row_max(mag8(v[p])));
+            if (r < rows) {
+                if (!WEIGHT && qd == 0)
+                    s[cb * rows + r] = tq.s;
+                *reinterpret_cast<uint2*>(q + r * cols + col0) = encode8(v[p], tq.pre, tq.r);
+            }
+        }
+    }
+
+    // ---- transposed codes (128x1 tiles, or the weight block transposed) -
+    if constexpr (TRANS) {
+        if constexpr (COL) {
+            int cm[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                cm[i] = 0;
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+                cm[0] = max(cm[0], (int)(v[p].x & 0x7FFFu));
+                cm[1] = max(cm[1], (int)((v[p].x >> 16) & 0x7FFFu));
+                cm[2] = max(cm[2], (int)(v[p].y & 0x7FFFu));
+                cm[3] = max(cm[3], (int)((v[p].y >> 16) & 0x7FFFu));
+                cm[4] = max(cm[4], (int)(v[p].z & 0x7FFFu));
+                cm[5] = max(cm[5], (int)((v[p].z >> 16) & 0x7FFFu));
+                cm[6] = max(cm[6], (int)(v[p].w & 0x7FFFu));
+                cm[7] = max(cm[7], (int)((v[p].w >> 16) & 0x7FFFu));
+            }
+            *reinterpret_cast<int4*>(&colmax[g][8 * qd]) = make_int4(cm[0], cm[1], cm[2], cm[3]);
+            *reinterpret_cast<int4*>(&colmax[g][8 * qd + 4]) = make_int4(cm[4], cm[5], cm[6], cm[7]);
+            __syncthreads();
+            if (t < 128) {
+                int m = colmax[0][t];
+#pragma unroll
+                for (int j = 1; j < 16; ++j)
+                    m = max(m, colmax[j][t]);
+                const TileQ tq = tile_params(m);
+                col_r[t] = tq.r;
+                col_pre[t] = tq.pre;
+                st[rb * cols + cb * 128 + t] = tq.s;
+            }
+            __syncthreads();
+        }
+        // Column i of this thread's 8x8 patch: 8 codes for rows 8g .. 8g+7,
+        // stored as one 8-byte chunk of LDS row c = 8*qd + i.  The chunk index
+        // is XOR-swizzled with qd so the 16 lanes of a DPP row hit distinct
+        // banks.
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float r = wq.r, pre = wq.pre;
+            if constexpr (COL) {
+                r = col_r[8 * qd + i];
+                pre = col_pre[8 * qd + i];
+            }
+            float f[8];
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+                const uint32_t w = (i < 2) ? v[p].x : (i < 4) ? v[p].y : (i < 6) ? v[p].z : v[p].w;
+                f[p] = (i & 1) ? bf16_hi(w) : bf16_lo(w);
+            }
+            int lo = cvt2_lo((f[0] * pre) * r, (f[1] * pre) * r, 0);
+            lo = cvt2_hi((f[2] * pre) * r, (f[3] * pre) * r, lo);
+            int hi = cvt2_lo((f[4] * pre) * r, (f[5] * pre) * r, 0);
+            hi = cvt2_hi((f[6] * pre) * r, (f[7] * pre) * r, hi);
+            const int c = 8 * qd + i;
+            *reinterpret_cast<uint2*>(tbuf + c * 128 + 8 * (g ^ qd)) = make_uint2((uint32_t)lo, (uint32_t)hi);
+        }
+        __syncthreads();
+        // Read back 16 bytes (two logical chunks 2h, 2h+1) of LDS row c.  They
+        // sit in the aligned pair h ^ (qc >> 1), swapped when qc is odd.
+#pragma unroll
+        for (int pass = 0; pass < 4; ++pass) {
+            const int c = (t >> 3) + 32 * pass;
+            const int h = t & 7;
+            const int qc = (c >> 3) & 15;
+            uint4 w = *reinterpret_cast<const uint4*>(tbuf + c * 128 + 16 * (h ^ (qc >> 1)));
+            if (qc & 1)
+                w = make_uint4(w.z, w.w, w.x, w.y);
+            *reinterpret_cast<uint4*>(qt + (cb * 128 + c) * ld_t + rb * 128 + 16 * h) = w;
+        }
+    }
+}
+
+// Diagnostic: E4M3 code of every binary32 bit pattern first + i, i < n.
+__global__ __launch_bounds__(256) void probe_encode_kernel(uint32_t first, int64_t n,
+                                                           uint8_t* __restrict__ out)
+{
+    const int64_t stride = (int64_t)gridDim.x * 256 * 4;
+    for (int64_t base = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; base < n; base += stride) {
+        float f[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            f[j] = __uint_as_float(first + (uint32_t)(base + j));
+        int c = cvt2_lo(f[0], f[1], 0);
+        c = cvt2_hi(f[2], f[3], c);
+        if (base + 4 <= n && ((reinterpret_cast<uintptr_t>(out) + base) & 3) == 0) {
+            *reinterpret_cast<uint32_t*>(out + base) = (uint32_t)c;
+        } else {
+            for (int j = 0; j < 4 && base + j < n; ++j)
+                out[base + j] = (uint8_t)((uint32_t)c >> (8 * j));
+        }
+    }
+}
+
+hipError_t launch_quant_act(const void* x, int64_t rows, int64_t cols, uint8_t* q, float* s,
+                            uint8_t* qt, float* st, hipStream_t stream)
+{
+    const int64_t rows_pad = (rows + 127) / 128 * 128;
+    const dim3 grid((unsigned)(rows_pad / 128), (unsigned)(cols / 128));
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    const bool row = q != nullptr, col = qt != nullptr;
+    if (row && col)
+        quant_block_kernel<true, true, false, false><<<grid, 256, 0, stream>>>(xb, rows, cols, rows_pad, q, s, qt, st);
+    else if (row)
+        quant_block_kernel<true, false, false, false><<<grid, 256, 0, stream>>>(xb, rows, cols, rows_pad, q, s, qt, st);
+    else
+        quant_block_kernel<false, true, false, false><<<grid, 256, 0, stream>>>(xb, rows, cols, rows_pad, q, s, qt, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_weight(const void* w, int64_t n, int64_t k, uint8_t* q, uint8_t* qt,
+                               float* s, hipStream_t stream)
+{
+    const dim3 grid((unsigned)(n / 128), (unsigned)(k / 128));
+    const uint16_t* wb = static_cast<const uint16_t*>(w);
+    if (qt)
+        quant_block_kernel<false, false, true, true><<<grid, 256, 0, stream>>>(wb, n, k, n, q, s, qt, nullptr);
+    else
+        quant_block_kernel<false, false, true, false><<<grid, 256, 0, stream>>>(wb, n, k, n, q, s, nullptr, nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_probe_encode(uint32_t first, int64_t n, uint8_t* out, hipStream_t stream)
+{
+    const int64_t blocks_needed = (n + 1023) / 1024;
+    const unsigned grid = (unsigned)(blocks_needed < 65536 ? blocks_needed : 65536);
+    probe_encode_kernel<<<grid, 256, 0, stream>>>(first, n, out);
+    return hipGetLastError();
+}
+
+}  // namespace puro

@@ -1,0 +1,177 @@
+/*
+ * puro_fp8.h -- C ABI of the fine-grained block-quantized FP8 linear layer
+ * for AMD Instinct MI355X (CDNA4, gfx950).
+ *
+ * What is computed.  The Puro-2B pretraining recipe puts the main Transformer
+ * linear-layer GEMMs on an FP8 path using DeepSeek-V3-style fine-grained
+ * block quantization, while numerically sensitive operations and training
+ * state stay in BF16/FP32 (arXiv report "Puro-2B", section 2.1 "Pipeline at a
+ * Glance"; training.farm blog, section "FP8"; bit.fan article, section "FP8
+ * training and its trade-off").  The pages give no tile shape, format or
+ * rounding; this library fixes them as follows:
+ *   - codes: OCP FP8 E4M3 (bias 7, max 448, no infinity), one byte each;
+ *   - one FP32 scale per tile: s = RN32(amax / 448), amax = max |x| over the
+ *     tile; each element is v = RN32(x * RN32(448 / amax)) and its code is
+ *     E4M3 round-to-nearest-even of v with saturation at 448.  When
+ *     amax < 2^-64, x and amax are first multiplied by 2^64 (exact) so the
+ *     reciprocal cannot overflow; amax == 0 gives s = 0 and signed-zero codes;
+ *   - tiles: 1x128 along the contraction dimension for activations and
+ *     output gradients, 128x1 along tokens for the weight-gradient operands,
+ *     128x128 for weights;
+ *   - GEMM: C = sum over 128-deep K-blocks of (A_kb . B_kb^T) * sA * sB,
+ *     with the per-block partial product in FP32 and the scale applied to
+ *     every K-block before FP32 accumulation across blocks.
+ *
+ * Conventions for every entry point:
+ *   - Every pointer argument except `stream` is a DEVICE pointer; `stream` is
+ *     a hipStream_t (NULL = the null stream).  The caller owns every buffer;
+ *     the library never allocates, frees or synchronizes, keeps no mutable
+ *     global state, and is safe to call from several host threads.
+ *   - Calls are asynchronous: they validate arguments, enqueue kernels on
+ *     `stream` and return.  Argument errors return synchronously before any
+ *     work is enqueued and have no side effects.  A launch failure returns
+ *     PURO_ERR_HIP.  A device fault surfaces at the caller's next
+ *     synchronization.  No C++ exception crosses this boundary.
+ *   - Tensors are dense and row-major.  Every base pointer must be 16-byte
+ *     aligned.  Outputs must not alias inputs.  NaN / Inf inputs give
+ *     undefined codes (not checked).
+ *   - Sizes are int64_t element counts.  A dimension of 0 where allowed
+ *     makes the call a no-op that returns PURO_OK.
+ */
+#ifndef PURO_FP8_H
+#define PURO_FP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PURO_FP8_ABI_VERSION 1
+
+typedef enum {
+    PURO_OK = 0,
+    PURO_ERR_NULL_POINTER = 1,  /* a required pointer is NULL                 */
+    PURO_ERR_BAD_SHAPE = 2,     /* negative size, or not a multiple of 128    */
+    PURO_ERR_MISALIGNED = 3,    /* a base pointer is not 16-byte aligned      */
+    PURO_ERR_BAD_ENUM = 4,      /* unknown mode / dtype, or a bad combination */
+    PURO_ERR_WORKSPACE = 5,     /* workspace smaller than required            */
+    PURO_ERR_UNIMPLEMENTED = 6, /* valid request this build does not serve    */
+    PURO_ERR_HIP = 7,           /* the HIP runtime rejected a launch          */
+    PURO_ERR_INTERNAL = 8       /* unexpected failure inside the library      */
+} puro_status_t;
+
+typedef enum {
+    PURO_GEMM_FWD = 0,   /* Y  = X . W^T   : M = tokens, N = out, K = in      */
+    PURO_GEMM_DGRAD = 1, /* dX = dY . W    : M = tokens, N = in,  K = out     */
+    PURO_GEMM_WGRAD = 2  /* dW = dY^T . X  : M = out,    N = in,  K = tokens  */
+} puro_gemm_mode_t;
+
+typedef enum {
+    PURO_OUT_BF16 = 0,   /* FP32 result rounded to bf16, nearest-even        */
+    PURO_OUT_FP32 = 1
+} puro_out_dtype_t;
+
+/*
+ * Activation / gradient quantizer (1x128 and 128x1 tiles).
+ *
+ *   x   bf16 [rows][cols]                       input (raw bf16 bits)
+ *   q   u8   [rows][cols]                       1x128 codes (tiles along cols)
+ *   s   f32  [cols/128][rows]                   one scale per 1x128 tile,
+ *                                               block-major so a GEMM reads
+ *                                               the scales of one K-block for
+ *                                               consecutive rows contiguously
+ *   qt  u8   [cols][rows_pad]                   128x1 codes, TRANSPOSED
+ *                                               (tiles along rows)
+ *   st  f32  [rows_pad/128][cols]               one scale per 128x1 tile
+ *
+ * rows_pad = ceil(rows / 128) * 128.  In the transposed copy, rows beyond
+ * `rows` hold zero codes and do not enter the tile amax, so a WGRAD GEMM can
+ * use K = rows_pad.  Either pair (q, s) or (qt, st) may be NULL (skipped);
+ * not both.  Requires cols > 0, cols % 128 == 0, rows >= 0.
+ * Defined by: the fine-grained block quantization of linear-layer GEMM
+ * operands (arXiv report section 2.1; blog section "FP8").
+ */
+puro_status_t puro_fp8_quant_act(const void* x, int64_t rows, int64_t cols,
+                                 uint8_t* q, float* s, uint8_t* qt, float* st,
+                                 void* stream);
+
+/*
+ * Weight quantizer (128x128 blocks).
+ *
+ *   w   bf16 [n][k]          input weight (out features n, in features k)
+ *   q   u8   [n][k]          codes
+ *   qt  u8   [k][n]          the same codes transposed (NULL = skip); DGRAD
+ *                            uses it as its K-contiguous B operand
+ *   s   f32  [n/128][k/128]  one scale per block
+ *
+ * Requires n, k > 0 and multiples of 128.
+ * Defined by: the same passages as puro_fp8_quant_act.
+ */
+puro_status_t puro_fp8_quant_weight(const void* w, int64_t n, int64_t k,
+                                    uint8_t* q, uint8_t* qt, float* s,
+                                    void* stream);
+
+/*
+ * Block-scaled FP8 GEMM.
+ *
+ *   C[m][n] (+)= sum over kb < K/128 of
+ *                  sA(kb, m) * sB(kb, n) * sum_{k in kb} dec(a[m][k]) * dec(b[n][k])
+ *
+ *   a   u8  [M][K]   E4M3 codes, K-contiguous
+ *   sa  f32 [K/128][M]
+ *   b   u8  [N][K]   E4M3 codes, K-contiguous
+ *   sb  f32 FWD   [N/128][K/128]   (the weight's block scales)
+ *           DGRAD [K/128][N/128]   (the weight's block scales as stored for
+ *                                   W [K][N]; b is the transposed code copy)
+ *           WGRAD [K/128][N]       (per-column 128x1 scales)
+ *   c   bf16 or f32 [M][N] according to c_dtype
+ *
+ * How a linear layer with W [out][in] and T tokens maps onto the modes:
+ *   FWD:   a = q(X) [T][in],   sa = s(X),  b = q(W) [out][in],  sb = s(W)
+ *   DGRAD: a = q(dY) [T][out], sa = s(dY), b = qt(W) [in][out], sb = s(W)
+ *   WGRAD: a = qt(dY) [out][T_pad], sa = st(dY), b = qt(X) [in][T_pad],
+ *          sb = st(X)
+ *
+ * Requires M >= 0, N > 0 and K > 0 with N % 128 == 0 and K % 128 == 0.
+ * accumulate != 0 adds into the existing contents of c and needs
+ * c_dtype == PURO_OUT_FP32.  workspace must hold at least
+ * puro_fp8_gemm_workspace_bytes(mode, M, N, K) bytes (it may be NULL when
+ * that is 0); its contents are scratch.
+ * Defined by: the FP8 GEMMs of the main linear layers (arXiv report section
+ * 2.1; blog section "FP8"), forward and the two backward products.
+ */
+puro_status_t puro_fp8_gemm_blockscaled(puro_gemm_mode_t mode, int64_t M, int64_t N,
+                                        int64_t K, const uint8_t* a, const float* sa,
+                                        const uint8_t* b, const float* sb, void* c,
+                                        puro_out_dtype_t c_dtype, int accumulate,
+                                        void* workspace, size_t workspace_bytes,
+                                        void* stream);
+
+/* Workspace bytes puro_fp8_gemm_blockscaled needs for this problem (0 if
+ * none, or if the arguments are invalid). */
+size_t puro_fp8_gemm_workspace_bytes(puro_gemm_mode_t mode, int64_t M, int64_t N,
+                                     int64_t K);
+
+/* Static, NUL-terminated description of a status code. */
+const char* puro_fp8_status_string(puro_status_t status);
+
+/* PURO_FP8_ABI_VERSION of the built library. */
+int puro_fp8_abi_version(void);
+
+/*
+ * Diagnostic: the device E4M3 encoder the quantizers use, applied to the
+ * binary32 values whose bit patterns are first_bits, first_bits + 1, ...,
+ * first_bits + n - 1 (wrapping modulo 2^32).  out: u8 [n] device buffer.
+ * Lets a test compare the hardware conversion against a reference over whole
+ * ranges of inputs.  Requires n >= 0.
+ */
+puro_status_t puro_fp8_probe_encode(uint32_t first_bits, int64_t n, uint8_t* out,
+                                    void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PURO_FP8_H */

@@ -66,6 +66,8 @@ def _load():
         lib.orc_e4m3_encode.argtypes = [ctypes.c_float]
         lib.orc_e4m3_decode.restype = ctypes.c_double
         lib.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
+        lib.orc_e4m3_encode_range.restype = None
+        lib.orc_e4m3_encode_range.argtypes = [ctypes.c_uint32, I64, P]
         lib.orc_tile_scale.restype = ctypes.c_float
         lib.orc_tile_scale.argtypes = [ctypes.c_float]
         lib.orc_scaled_value.restype = ctypes.c_float
@@ -131,6 +133,13 @@ def e4m3_decode(code: int) -> float:
 def e4m3_decode_table() -> np.ndarray:
     """float64[256]: the exact value of every code (NaN for 0x7F/0xFF)."""
     return np.array([e4m3_decode(c) for c in range(256)], dtype=np.float64)
+
+
+def e4m3_encode_range(first_bits: int, n: int) -> np.ndarray:
+    """Codes of the binary32 values with bit patterns first_bits .. +n-1."""
+    out = np.empty(int(n), np.uint8)
+    _load().orc_e4m3_encode_range(int(first_bits) & 0xFFFFFFFF, int(n), _ptr(out))
+    return out
 
 
 def tile_scale(amax: float) -> float:

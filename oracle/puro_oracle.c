@@ -163,6 +163,28 @@ static void parallel_for(int64_t n, range_fn fn, void* ctx)
             pthread_join(th[t], NULL);
 }
 
+typedef struct {
+    uint32_t first;
+    uint8_t* out;
+} enc_ctx;
+
+static void enc_range(void* p, int64_t b, int64_t e)
+{
+    const enc_ctx* c = (const enc_ctx*)p;
+    for (int64_t i = b; i < e; ++i) {
+        const uint32_t u = c->first + (uint32_t)i;
+        float v;
+        memcpy(&v, &u, sizeof v);
+        c->out[i] = orc_e4m3_encode(v);
+    }
+}
+
+void orc_e4m3_encode_range(uint32_t first_bits, int64_t n, uint8_t* out)
+{
+    enc_ctx c = {first_bits, out};
+    parallel_for(n, enc_range, &c);
+}
+
 /* ------------------------------------------------------------------------ */
 /* Quantizers. */
 

@@ -37,6 +37,9 @@ extern "C" {
 /* ---- E4M3 codec (OCP OFP8 E4M3) ---------------------------------------- */
 uint8_t orc_e4m3_encode(float v);          /* RNE, saturate |v|>448 to +-448 */
 double  orc_e4m3_decode(uint8_t code);     /* exact value; NaN for 0x7F/0xFF */
+/* out[i] = orc_e4m3_encode(binary32 with bit pattern first_bits + i), the bit
+ * pattern wrapping modulo 2^32; i < n. */
+void    orc_e4m3_encode_range(uint32_t first_bits, int64_t n, uint8_t* out);
 
 /* ---- tile scale ---------------------------------------------------------- */
 /* For a tile with absolute maximum amax (a bf16 value widened to float):

@@ -1,0 +1,127 @@
+"""The C-ABI library loads on a machine without a GPU, exports every symbol
+include/puro_fp8.h declares, and rejects bad arguments synchronously with the
+documented status codes (these calls return before any HIP call, so no
+kernel is launched and no GPU is needed)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "puro_fp8.h")
+
+OK, NULLP, SHAPE, ALIGN, ENUM, WS = 0, 1, 2, 3, 4, 5
+
+# fake device addresses: never dereferenced, since validation fails first
+P16 = 0x7F0000000000          # 16-byte aligned
+P_ODD = 0x7F0000000008        # 8-byte aligned only
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(puro_fp8_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import fp8_block_scaled_tile_amd as pf
+    if not os.path.exists(pf.library_path()):
+        from fp8_block_scaled_tile_amd import build
+        build.build()
+    return pf
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for n in ("puro_fp8_quant_act", "puro_fp8_quant_weight", "puro_fp8_gemm_blockscaled",
+              "puro_fp8_gemm_workspace_bytes", "puro_fp8_status_string",
+              "puro_fp8_abi_version", "puro_fp8_probe_encode"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    handle = ctypes.CDLL(lib.library_path())
+    for name in _declared_functions():
+        assert hasattr(handle, name), f"{name} not exported"
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.puro_fp8_abi_version() == 1
+    for code in range(9):
+        s = lib.puro_fp8_status_string(code)
+        assert s.startswith("PURO_")
+    assert "unknown" in lib.puro_fp8_status_string(77)
+
+
+def test_quant_act_validation(lib):
+    f = lib.puro_fp8_quant_act
+    assert f(P16, 16, 100, P16, P16, None, None, None) == SHAPE       # cols % 128
+    assert f(P16, -1, 128, P16, P16, None, None, None) == SHAPE
+    assert f(P16, 16, 0, P16, P16, None, None, None) == SHAPE
+    assert f(None, 16, 128, P16, P16, None, None, None) == NULLP
+    assert f(P16, 16, 128, None, None, None, None, None) == NULLP     # no output
+    assert f(P16, 16, 128, P16, None, None, None, None) == NULLP      # half a pair
+    assert f(P16, 16, 128, None, None, P16, None, None) == NULLP
+    assert f(P_ODD, 16, 128, P16, P16, None, None, None) == ALIGN
+    assert f(P16, 16, 128, P16, P_ODD, None, None, None) == ALIGN
+    assert f(P16, 16, 128, None, None, P16, P_ODD, None) == ALIGN
+    assert f(P16, 0, 128, P16, P16, P16, P16, None) == OK             # empty: no-op
+
+
+def test_quant_weight_validation(lib):
+    f = lib.puro_fp8_quant_weight
+    assert f(P16, 100, 128, P16, None, P16, None) == SHAPE
+    assert f(P16, 128, 0, P16, None, P16, None) == SHAPE
+    assert f(None, 128, 128, P16, None, P16, None) == NULLP
+    assert f(P16, 128, 128, None, None, P16, None) == NULLP
+    assert f(P16, 128, 128, P16, None, None, None) == NULLP
+    assert f(P16, 128, 128, P16, P_ODD, P16, None) == ALIGN
+
+
+def test_gemm_validation(lib):
+    f = lib.puro_fp8_gemm_blockscaled
+    args = lambda **kw: dict(dict(mode=0, M=256, N=256, K=256, a=P16, sa=P16, b=P16, sb=P16,
+                                  c=P16, c_dtype=0, acc=0, ws=None, wsb=0), **kw)
+
+    def call(**kw):
+        d = args(**kw)
+        return f(d["mode"], d["M"], d["N"], d["K"], d["a"], d["sa"], d["b"], d["sb"], d["c"],
+                 d["c_dtype"], d["acc"], d["ws"], d["wsb"], None)
+
+    assert call(mode=3) == ENUM
+    assert call(mode=-1) == ENUM
+    assert call(c_dtype=2) == ENUM
+    assert call(acc=1, c_dtype=0) == ENUM                  # accumulate needs FP32
+    assert call(N=200) == SHAPE
+    assert call(K=100) == SHAPE
+    assert call(M=-5) == SHAPE
+    assert call(K=0) == SHAPE
+    assert call(a=None) == NULLP
+    assert call(sb=None) == NULLP
+    assert call(c=None) == NULLP
+    assert call(b=P_ODD) == ALIGN
+    assert call(M=0) == OK                                  # empty: no-op
+    # a problem that splits K needs a workspace
+    need = lib.puro_fp8_gemm_workspace_bytes(2, 2048, 2048, 32768)
+    assert need > 0
+    assert call(mode=2, M=2048, N=2048, K=32768, c_dtype=1) == WS
+    assert call(mode=2, M=2048, N=2048, K=32768, c_dtype=1, ws=P16, wsb=need - 16) == WS
+    assert call(mode=2, M=2048, N=2048, K=32768, c_dtype=1, ws=P_ODD, wsb=need) == ALIGN
+
+
+def test_workspace_query(lib):
+    q = lib.puro_fp8_gemm_workspace_bytes
+    assert q(0, 16384, 6144, 2048) == 0                    # enough tiles: no split
+    assert q(2, 2048, 2048, 32768) % (2048 * 2048 * 4) == 0
+    assert q(0, 256, 100, 256) == 0                        # invalid shape -> 0
+    assert q(5, 256, 256, 256) == 0
+
+
+def test_probe_validation(lib):
+    assert lib.puro_fp8_probe_encode(0, -1, P16, None) == SHAPE
+    assert lib.puro_fp8_probe_encode(0, 10, None, None) == NULLP
+    assert lib.puro_fp8_probe_encode(0, 0, None, None) == OK

@@ -1,0 +1,174 @@
+"""GPU parity of the quantizers and the device E4M3 conversion against the
+CPU oracle: codes and scales bit-exact.  Calls go through the C ABI."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity import bf16_host_bits, dev, host, random_bf16, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pf():
+    import fp8_block_scaled_tile_amd as pf
+    assert torch.cuda.is_available()
+    return pf
+
+
+def _check_act(pf, x_cpu, row=True, col=True, tag=""):
+    rows, cols = x_cpu.shape
+    say("quant_act", tag, rows, cols, "row" if row else "", "col" if col else "")
+    out = pf.quant_act(dev(x_cpu), row=row, col=col)
+    xb = synth.bits(x_cpu)
+    if row:
+        q, s = oracle.quant_rowwise(xb)
+        assert np.array_equal(host(out["q"]), q), "row codes differ"
+        assert np.array_equal(host(out["s"]).view(np.uint32), s.view(np.uint32)), "row scales differ"
+    if col:
+        qt, st = oracle.quant_colwise(xb)
+        assert np.array_equal(host(out["qt"]), qt), "column codes differ"
+        assert np.array_equal(host(out["st"]).view(np.uint32), st.view(np.uint32)), "column scales differ"
+
+
+# ---- the device conversion itself ------------------------------------------
+
+def test_probe_encode_exhaustive_below_464(pf):
+    """Every binary32 bit pattern with |v| < 464 (both signs): the hardware
+    E4M3 conversion equals the oracle's round-to-nearest-even encoder.  These
+    cover every scaled value a quantizer can produce (|v| <= 448 * (1+2^-23))."""
+    chunk = 1 << 28
+    buf = torch.empty(chunk, dtype=torch.uint8, device="cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    for sign in (0, 0x80000000):
+        start, end = sign, sign + 0x43E80000          # 464.0f = 0x43E80000
+        for first in range(start, end, chunk):
+            n = min(chunk, end - first)
+            say("probe_encode", hex(first), n)
+            assert pf.puro_fp8_probe_encode(first, n, buf.data_ptr(), stream) == 0
+            got = host(buf[:n])
+            exp = oracle.e4m3_encode_range(first, n)
+            bad = np.nonzero(got != exp)[0]
+            assert bad.size == 0, (f"first mismatch bits {first + int(bad[0]):#010x}: "
+                                   f"device {got[bad[0]]:#04x} oracle {exp[bad[0]]:#04x}")
+
+
+# ---- activation quantizer ----------------------------------------------------
+
+@pytest.mark.parametrize("rows,cols", [(1, 128), (37, 256), (128, 128), (129, 384),
+                                       (300, 512), (1000, 1024), (4096, 2048)])
+@pytest.mark.parametrize("mode", ["row", "col", "dual"])
+def test_quant_act_small(pf, rows, cols, mode):
+    x = random_bf16((rows, cols), seed=rows * 7 + cols, stream=f"act/{rows}x{cols}")
+    _check_act(pf, x, row=mode in ("row", "dual"), col=mode in ("col", "dual"),
+               tag=f"small-{mode}")
+
+
+@pytest.mark.parametrize("name,which,row,col", [
+    ("tiny_fwd", "x", True, False),
+    ("qkv_fwd", "x", True, False),
+    ("upgate_fwd", "x", True, False),
+    ("down_bwd", "dy", True, True),
+    ("down_bwd", "x", False, True),
+])
+def test_quant_act_workloads(pf, name, which, row, col):
+    spec = synth.workload(name).linears[0]
+    t = synth.linear_inputs(spec, need=(which,))[which]
+    _check_act(pf, t, row=row, col=col, tag=f"{name}/{which}")
+
+
+def test_quant_act_largest_block_stack_gradient(pf):
+    """The largest tensor of the transformer-block workload: the up/gate
+    output gradient dY [32768 x 16384], dual row + column quantization."""
+    spec = synth.workload("block_stack").linears[2]
+    t = synth.linear_inputs(spec, need=("dy",))["dy"]
+    _check_act(pf, t, row=True, col=True, tag="block_stack/up_gate/dy")
+
+
+def test_quant_act_special_tiles(pf):
+    """Zero tiles, negative zeros, bf16 subnormal amax (the 2^64 rescale),
+    huge values, exact power-of-two amax, one outlier per tile."""
+    rows, cols = 256, 512
+    xb = np.zeros((rows, cols), np.uint16)
+    xb[1, :] = 0x8000                                   # all -0.0
+    xb[2, :128] = 0x0001                                # smallest subnormal
+    xb[2, 128:256] = np.arange(128, dtype=np.uint16) | 0x8000
+    xb[3, :] = 0x7F7F                                   # bf16 max
+    xb[3, ::3] = 0xFF7F
+    xb[4, :] = 0x43E0                                   # 448.0
+    xb[5, :] = 0x3F80                                   # 1.0 with one 2.0
+    xb[5, 5] = 0x4000
+    rng = np.random.default_rng(5)
+    xb[6:, :] = (rng.integers(0, 0x7F80, size=(rows - 6, cols)) |
+                 (rng.integers(0, 2, size=(rows - 6, cols)) << 15)).astype(np.uint16)
+    x = synth.from_bits(xb)
+    _check_act(pf, x, row=True, col=True, tag="special")
+
+
+def test_quant_act_exhaustive_amax_x_pairs(pf):
+    """Every non-negative finite bf16 amax (32,640 values) against every bf16
+    magnitude x <= amax (about 5.3e8 pairs, alternating signs): one tile per
+    row holds amax at position 0 and 127 x values; the row-wise codes and
+    scales equal the oracle's bit for bit."""
+    amax_bits = np.arange(0, 0x7F80, dtype=np.int64)
+    ntile = (amax_bits + 1 + 126) // 127                 # tiles needed per amax
+    total = int(ntile.sum())
+    say("exhaustive pairs: rows", total)
+    tile_amax = np.repeat(amax_bits, ntile).astype(np.int32)
+    first = np.concatenate([[0], np.cumsum(ntile)[:-1]])
+    tile_idx = (np.arange(total) - np.repeat(first, ntile)).astype(np.int32)  # k-th tile of its amax
+    xb = np.empty((total, 128), np.uint16)
+    xb[:, 0] = tile_amax.astype(np.uint16)
+    lane = np.arange(127, dtype=np.int32)[None, :]
+    step = 1 << 18
+    for r0 in range(0, total, step):                    # build in chunks (bounded memory)
+        ti = tile_idx[r0:r0 + step, None]
+        am = tile_amax[r0:r0 + step, None]
+        x = np.minimum(ti * 127 + lane, am)              # every magnitude <= amax
+        sign = ((lane + ti) & 1) << 15
+        xb[r0:r0 + step, 1:] = (x | sign).astype(np.uint16)
+    del tile_idx, tile_amax
+    xt = synth.from_bits(xb)
+    out = pf.quant_act(dev(xt), row=True, col=False)
+    q_dev = host(out["q"])
+    s_dev = host(out["s"])
+    del out
+    q, s = oracle.quant_rowwise(xb)
+    assert np.array_equal(s_dev.view(np.uint32), s.view(np.uint32))
+    bad = np.argwhere(q_dev != q)
+    assert bad.size == 0, (bad[:4], xb[tuple(bad[0])])
+
+
+def test_quant_act_deterministic(pf):
+    x = dev(random_bf16((2048, 1024), seed=9, stream="det"))
+    say("quant_act determinism")
+    a = pf.quant_act(x, row=True, col=True)
+    b = pf.quant_act(x, row=True, col=True)
+    for k in a:
+        assert torch.equal(a[k], b[k])
+
+
+def test_quant_act_empty(pf):
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda:0")
+    out = pf.quant_act(x, row=True, col=True)
+    assert out["q"].shape == (0, 256) and out["qt"].shape == (256, 0)
+
+
+# ---- weight quantizer ----------------------------------------------------------
+
+@pytest.mark.parametrize("n,k", [(128, 128), (512, 512), (384, 256), (6144, 2048),
+                                 (16384, 2048), (2048, 8192), (2048, 2048)])
+def test_quant_weight(pf, n, k):
+    w = random_bf16((n, k), std=0.02, seed=n + k, stream=f"w/{n}x{k}")
+    say("quant_weight", n, k)
+    out = pf.quant_weight(dev(w), transpose=True)
+    q, qt, s = oracle.quant_weight(synth.bits(w))
+    assert np.array_equal(host(out["q"]), q)
+    assert np.array_equal(host(out["qt"]), qt)
+    assert np.array_equal(host(out["s"]).view(np.uint32), s.view(np.uint32))
+    out2 = pf.quant_weight(dev(w), transpose=False)
+    assert np.array_equal(host(out2["q"]), q) and "qt" not in out2
