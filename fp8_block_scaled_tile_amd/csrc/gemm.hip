@@ -38,6 +38,8 @@ namespace puro {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
+typedef __attribute__((address_space(3))) void lds_void;
+
 constexpr int BM = 256;
 constexpr int BN = 256;
 constexpr int BK = 128;
@@ -52,10 +54,13 @@ constexpr int GROUP_M = 8;
 enum { MODE_FWD = 0, MODE_DGRAD = 1, MODE_WGRAD = 2 };
 enum { OUT_BF16 = 0, OUT_FP32 = 1, OUT_FP32_ACC = 2, OUT_PARTIAL = 3 };
 
-__device__ __forceinline__ int lds_off(int row, int chunk)
-{
-    return row * BK + ((chunk ^ (row & 7)) << 4);
-}
+// LDS rows are 128 bytes (one K-block of one row).  The 16-byte chunk c of
+// row r is stored at chunk position c ^ (r & 7) ^ ((r >> 3) & 1): a fragment
+// read (16 consecutive rows, one chunk each per 16-lane phase) and the
+// staging writes (8 chunks of 2 consecutive rows per phase) then touch 16
+// distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int lds_off(int row, int chunk) { return row * BK + ((chunk ^ swz(row)) << 4); }
 
 // 32-byte MFMA operand fragment of a 16x128 slice starting at row `base`:
 // lane l holds row base + (l & 15), logical chunks 2*(l>>4) and 2*(l>>4)+1.
@@ -73,6 +78,68 @@ __device__ __forceinline__ v8i load_frag(const uint8_t* lds, int base, int lane)
     return f;
 }
 
+// One K-block (128 deep) staged in LDS: A and B code slices and their scales.
+struct Stage {
+    uint8_t a[TILE_BYTES];
+    uint8_t b[TILE_BYTES];
+    float sa[BM];        // sA of the tile's 256 rows
+    float sb[BN];        // WGRAD: sB of the tile's 256 columns; else [0], [1]
+};
+
+// A wave-uniform pointer held in scalar registers.  Going through
+// readfirstlane keeps the compiler from folding per-lane offsets into the
+// base (which would hoist 64-bit per-lane addresses out of the K loop); the
+// loads then use the scalar-base + 32-bit vector-offset form.
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p)
+{
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<const T*>(((uint64_t)hi << 32) | lo);
+}
+
+// Staging of one K-block: every wave copies 32 rows of A and 32 rows of B
+// (4 + 4 LDS-DMA instructions of 1 KB, 16 bytes per lane).  Lane L of
+// instruction i fills LDS row 32*wave + 8*i + L/8 at chunk position L%8, so it
+// fetches the logical chunk the swizzle stores there; rows past the end of
+// the matrix read the last row instead (their results are never stored).
+// Wave 0 also copies the 256 sA values, wave 1 the sB values.
+template <int MODE>
+__device__ __forceinline__ void issue_stage(Stage& st, const uint8_t* A, const float* SA,
+                                            const uint8_t* B, const float* SB, int kb, int m0,
+                                            int n0, int M, int N, int K, int KB, int wave, int lane)
+{
+    const uint8_t* ab = uniform_ptr(A + (size_t)kb * BK);
+    const uint8_t* bb = uniform_ptr(B + (size_t)kb * BK);
+    const int r0 = 32 * wave + (lane >> 3);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = r0 + 8 * i;
+        const uint32_t c = 16u * (uint32_t)((lane & 7) ^ swz(row));
+        const uint32_t ao = (uint32_t)min(m0 + row, M - 1) * (uint32_t)K + c;
+        const uint32_t bo = (uint32_t)min(n0 + row, N - 1) * (uint32_t)K + c;
+        __builtin_amdgcn_global_load_lds(ab + ao, (lds_void*)(st.a + (32 * wave + 8 * i) * BK), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(bb + bo, (lds_void*)(st.b + (32 * wave + 8 * i) * BK), 16, 0, 0);
+    }
+    if (wave == 0) {
+        const float* sab = uniform_ptr(SA + (size_t)kb * M);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            __builtin_amdgcn_global_load_lds(sab + min(m0 + 64 * j + lane, M - 1),
+                                             (lds_void*)(st.sa + 64 * j), 4, 0, 0);
+    } else if (wave == 1) {
+        if constexpr (MODE == MODE_WGRAD) {
+            __builtin_amdgcn_global_load_lds(uniform_ptr(SB + (size_t)kb * N) + min(n0 + 4 * lane, N - 4),
+                                             (lds_void*)(st.sb), 16, 0, 0);
+        } else if (lane < 2) {
+            const int nb = min(n0 / BK + lane, N / BK - 1);
+            const size_t idx = (MODE == MODE_FWD) ? (size_t)nb * KB + kb : (size_t)kb * (N / BK) + nb;
+            __builtin_amdgcn_global_load_lds(SB + idx, (lds_void*)(st.sb), 4, 0, 0);
+        }
+    }
+}
+
 template <int MODE, int OUT>
 __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ SA,
@@ -80,15 +147,12 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
     void* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n, int splits,
     int kb_per_split)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][TILE_BYTES];
-    // Scales of the staged K-block: sA for the tile's 256 rows; sB for its
-    // 256 columns (WGRAD) or its two 128-wide weight blocks (FWD / DGRAD).
-    __shared__ __attribute__((aligned(16))) float lds_sa[2][BM];
-    __shared__ __attribute__((aligned(16))) float lds_sb[2][BN];
+    __shared__ __attribute__((aligned(16))) Stage stage0;
+    __shared__ __attribute__((aligned(16))) Stage stage1;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 2;        // 0..1
     const int wn = wave & 3;         // 0..3
 
@@ -114,96 +178,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
     const int kb_begin = split * kb_per_split;
     const int kb_end = min(KB, kb_begin + kb_per_split);
 
-    // ---- global -> register staging map: 4 chunks of A and of B ----------
-    const int lrow = tid >> 3;       // 0..63
-    const int lchunk = tid & 7;
-    // 32-bit byte offsets of this thread's 4 A rows and 4 B rows (rows past
-    // the end are clamped to the last row; their results are never stored).
-    // With a uniform 64-bit base per K-block the loads use the scalar-base +
-    // 32-bit vector-offset addressing form.
-    const uint32_t a_off0 = (uint32_t)min(m0 + lrow, M - 1) * (uint32_t)K + 16u * lchunk;
-    const uint32_t a_off1 = (uint32_t)min(m0 + lrow + 64, M - 1) * (uint32_t)K + 16u * lchunk;
-    const uint32_t a_off2 = (uint32_t)min(m0 + lrow + 128, M - 1) * (uint32_t)K + 16u * lchunk;
-    const uint32_t a_off3 = (uint32_t)min(m0 + lrow + 192, M - 1) * (uint32_t)K + 16u * lchunk;
-    const uint32_t b_off0 = (uint32_t)min(n0 + lrow, N - 1) * (uint32_t)K + 16u * lchunk;
-    const uint32_t b_off1 = (uint32_t)min(n0 + lrow + 64, N - 1) * (uint32_t)K + 16u * lchunk;
-    const uint32_t b_off2 = (uint32_t)min(n0 + lrow + 128, N - 1) * (uint32_t)K + 16u * lchunk;
-    const uint32_t b_off3 = (uint32_t)min(n0 + lrow + 192, N - 1) * (uint32_t)K + 16u * lchunk;
-    const int st_off0 = lds_off(lrow, lchunk);
-    const int st_off1 = lds_off(lrow + 64, lchunk);
-    const int st_off2 = lds_off(lrow + 128, lchunk);
-    const int st_off3 = lds_off(lrow + 192, lchunk);
-    uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
-
-#define PURO_LOAD_TILE(kb)                                                          \
-    do {                                                                            \
-        const uint8_t* ab = A + (size_t)(kb) * BK;                                  \
-        const uint8_t* bb = B + (size_t)(kb) * BK;                                  \
-        ra0 = *reinterpret_cast<const uint4*>(ab + a_off0);                         \
-        ra1 = *reinterpret_cast<const uint4*>(ab + a_off1);                         \
-        ra2 = *reinterpret_cast<const uint4*>(ab + a_off2);                         \
-        ra3 = *reinterpret_cast<const uint4*>(ab + a_off3);                         \
-        rb0 = *reinterpret_cast<const uint4*>(bb + b_off0);                         \
-        rb1 = *reinterpret_cast<const uint4*>(bb + b_off1);                         \
-        rb2 = *reinterpret_cast<const uint4*>(bb + b_off2);                         \
-        rb3 = *reinterpret_cast<const uint4*>(bb + b_off3);                         \
-    } while (0)
-#define PURO_STORE_TILE(buf)                                                        \
-    do {                                                                            \
-        *reinterpret_cast<uint4*>(&lds[buf][0][st_off0]) = ra0;                     \
-        *reinterpret_cast<uint4*>(&lds[buf][0][st_off1]) = ra1;                     \
-        *reinterpret_cast<uint4*>(&lds[buf][0][st_off2]) = ra2;                     \
-        *reinterpret_cast<uint4*>(&lds[buf][0][st_off3]) = ra3;                     \
-        *reinterpret_cast<uint4*>(&lds[buf][1][st_off0]) = rb0;                     \
-        *reinterpret_cast<uint4*>(&lds[buf][1][st_off1]) = rb1;                     \
-        *reinterpret_cast<uint4*>(&lds[buf][1][st_off2]) = rb2;                     \
-        *reinterpret_cast<uint4*>(&lds[buf][1][st_off3]) = rb3;                     \
-    } while (0)
-
-    // ---- scales: staged through LDS with the tiles -------------------------
-    // Threads 0..63 fetch the tile's 256 sA values as float4; threads 64..127
-    // fetch sB (256 per-column values in WGRAD, two block scales otherwise).
     const bool wave_active = (n0 + wn * WN) < N;
-    const int m_lane = m0 + wm * WM + (lane & 15);        // + 16*sm
-    const int n_lane = n0 + wn * WN + 4 * (lane >> 4);    // + 16*tn, 4 consecutive
-    float4 rs = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-
-#define PURO_LOAD_SCALES(kb)                                                        \
-    do {                                                                            \
-        if (tid < 64) {                                                             \
-            const int mm = m0 + 4 * tid;                                            \
-            const float* src = SA + (size_t)(kb) * M + mm;                          \
-            if (mm + 3 < M && ((M & 3) == 0)) {                                     \
-                rs = *reinterpret_cast<const float4*>(src);                         \
-            } else {                                                                \
-                rs.x = (mm + 0 < M) ? src[0] : 0.0f;                                \
-                rs.y = (mm + 1 < M) ? src[1] : 0.0f;                                \
-                rs.z = (mm + 2 < M) ? src[2] : 0.0f;                                \
-                rs.w = (mm + 3 < M) ? src[3] : 0.0f;                                \
-            }                                                                       \
-        } else if (tid < 128) {                                                     \
-            const int nn = n0 + 4 * (tid - 64);                                     \
-            if constexpr (MODE == MODE_WGRAD) {                                     \
-                if (nn < N)                                                         \
-                    rs = *reinterpret_cast<const float4*>(SB + (size_t)(kb) * N + nn); \
-            } else if (tid < 66) {                                                  \
-                const int nb = n0 / BK + (tid - 64);                                \
-                if (nb < N / BK) {                                                  \
-                    if constexpr (MODE == MODE_FWD)                                 \
-                        rs.x = SB[(size_t)nb * KB + (kb)];                          \
-                    else                                                            \
-                        rs.x = SB[(size_t)(kb) * (N / BK) + nb];                    \
-                }                                                                   \
-            }                                                                       \
-        }                                                                           \
-    } while (0)
-#define PURO_STORE_SCALES(buf)                                                      \
-    do {                                                                            \
-        if (tid < 64)                                                               \
-            *reinterpret_cast<float4*>(&lds_sa[buf][4 * tid]) = rs;                 \
-        else if (tid < 128)                                                         \
-            *reinterpret_cast<float4*>(&lds_sb[buf][4 * (tid - 64)]) = rs;          \
-    } while (0)
 
     v4f acc[TM][TN];
 #pragma unroll
@@ -212,75 +187,91 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
         for (int tn = 0; tn < TN; ++tn)
             acc[sm][tn] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    if (kb_begin < kb_end) {
-        PURO_LOAD_TILE(kb_begin);
-        PURO_LOAD_SCALES(kb_begin);
-        PURO_STORE_TILE(0);
-        PURO_STORE_SCALES(0);
-        __syncthreads();
-    }
-
-    for (int kb = kb_begin; kb < kb_end; ++kb) {
-        const int cur = (kb - kb_begin) & 1;
-        const bool has_next = kb + 1 < kb_end;
-        if (has_next) {
-            PURO_LOAD_TILE(kb + 1);
-            PURO_LOAD_SCALES(kb + 1);
-        }
-
-        if (wave_active) {
-            const uint8_t* la = &lds[cur][0][0];
-            const uint8_t* lb = &lds[cur][1][0];
-            v8i bf[TN];
+    // One K-block from a staged buffer: 32 MFMAs.  The partial of MFMA tile
+    // (sm, tn) is folded into its accumulator (one FMA per element with the
+    // block scale) just before MFMA (sm+1, tn) overwrites it, i.e. four MFMAs
+    // later, so the matrix core always has independent work queued and the
+    // partials need a single set of registers.
+    auto compute = [&](const Stage& st) {
+        v8i bf[TN];
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+            bf[tn] = load_frag(st.b, wn * WN + 16 * tn, lane);
+        float sb_wave = 0.0f;
+        v4f sb_col[TN];
+        if constexpr (MODE == MODE_WGRAD) {
 #pragma unroll
             for (int tn = 0; tn < TN; ++tn)
-                bf[tn] = load_frag(lb, wn * WN + 16 * tn, lane);
-            // FWD / DGRAD: the wave's 64 columns sit in one weight block.
-            const float sb_wave = lds_sb[cur][(wn * WN) / BK];
-            v4f sb_col[TN];
-            if constexpr (MODE == MODE_WGRAD) {
+                sb_col[tn] = *reinterpret_cast<const v4f*>(&st.sb[wn * WN + 16 * tn + 4 * (lane >> 4)]);
+        } else {
+            sb_wave = st.sb[(wn * WN) / BK];
+        }
+        v4f p[TN];
+        float sa_prev = 0.0f;
 #pragma unroll
-                for (int tn = 0; tn < TN; ++tn)
-                    sb_col[tn] = *reinterpret_cast<const v4f*>(
-                        &lds_sb[cur][wn * WN + 16 * tn + 4 * (lane >> 4)]);
-            }
+        for (int sm = 0; sm < TM; ++sm) {
+            const v8i af = load_frag(st.a, wm * WM + 16 * sm, lane);
+            const float sa = st.sa[wm * WM + 16 * sm + (lane & 15)];
 #pragma unroll
-            for (int sm = 0; sm < TM; ++sm) {
-                const v8i af = load_frag(la, wm * WM + 16 * sm, lane);
-                const float sa = lds_sa[cur][wm * WM + 16 * sm + (lane & 15)];
-#pragma unroll
-                for (int tn = 0; tn < TN; ++tn) {
-                    const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-                    const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        bf[tn], af, zero, 0, 0, 0, 0, 0, 0);
+            for (int tn = 0; tn < TN; ++tn) {
+                if (sm > 0) {
                     if constexpr (MODE == MODE_WGRAD) {
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
-                            acc[sm][tn][r] = __builtin_fmaf(p[r], sa * sb_col[tn][r], acc[sm][tn][r]);
+                            acc[sm - 1][tn][r] = __builtin_fmaf(p[tn][r], sa_prev * sb_col[tn][r], acc[sm - 1][tn][r]);
                     } else {
-                        const float sc = sa * sb_wave;
+                        const float sc = sa_prev * sb_wave;
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
-                            acc[sm][tn][r] = __builtin_fmaf(p[r], sc, acc[sm][tn][r]);
+                            acc[sm - 1][tn][r] = __builtin_fmaf(p[tn][r], sc, acc[sm - 1][tn][r]);
                     }
                 }
+                const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+                p[tn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[tn], af, zero, 0, 0, 0, 0, 0, 0);
+            }
+            sa_prev = sa;
+        }
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+            if constexpr (MODE == MODE_WGRAD) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[TM - 1][tn][r] = __builtin_fmaf(p[tn][r], sa_prev * sb_col[tn][r], acc[TM - 1][tn][r]);
+            } else {
+                const float sc = sa_prev * sb_wave;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[TM - 1][tn][r] = __builtin_fmaf(p[tn][r], sc, acc[TM - 1][tn][r]);
             }
         }
+    };
 
-        if (has_next) {
-            PURO_STORE_TILE(cur ^ 1);
-            PURO_STORE_SCALES(cur ^ 1);
-        }
-        __syncthreads();
+    // ---- main loop: two statically named LDS stages, one barrier per K-block.
+    // The DMA of block kb+1 is in flight while block kb is multiplied.
+    if (kb_begin < kb_end)
+        issue_stage<MODE>(stage0, A, SA, B, SB, kb_begin, m0, n0, M, N, K, KB, wave, lane);
+    for (int kb = kb_begin; kb < kb_end; kb += 2) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): this wave's DMA landed
+        __syncthreads();                          // every wave's DMA landed; stage1 free
+        if (kb + 1 < kb_end)
+            issue_stage<MODE>(stage1, A, SA, B, SB, kb + 1, m0, n0, M, N, K, KB, wave, lane);
+        if (wave_active)
+            compute(stage0);
+        if (kb + 1 >= kb_end)
+            break;
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();                          // stage0 free, stage1 landed
+        if (kb + 2 < kb_end)
+            issue_stage<MODE>(stage0, A, SA, B, SB, kb + 2, m0, n0, M, N, K, KB, wave, lane);
+        if (wave_active)
+            compute(stage1);
     }
-#undef PURO_LOAD_TILE
-#undef PURO_STORE_TILE
-#undef PURO_LOAD_SCALES
-#undef PURO_STORE_SCALES
 
     // ---- epilogue ----------------------------------------------------------
     if (!wave_active)
         return;
+    const int m_lane = m0 + wm * WM + (lane & 15);        // + 16*sm
+    const int n_lane = n0 + wn * WN + 4 * (lane >> 4);    // + 16*tn, 4 consecutive
 #pragma unroll
     for (int sm = 0; sm < TM; ++sm) {
         const int m = m_lane + 16 * sm;
