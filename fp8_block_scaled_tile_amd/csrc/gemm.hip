@@ -192,57 +192,71 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
     // block scale) just before MFMA (sm+1, tn) overwrites it, i.e. four MFMAs
     // later, so the matrix core always has independent work queued and the
     // partials need a single set of registers.
+    //
+    // FWD / DGRAD issue the MFMA with the B-side fragment first: a lane's 4
+    // accumulator rows are 4 consecutive n of one m, sA is one value per lane
+    // and tile, sB one value per wave.  WGRAD (per-column sB) issues it with
+    // the A-side fragment first: a lane's 4 rows are 4 consecutive m of one n,
+    // so it holds 4 sB values per K-block and one float4 of sA per tile.
     auto compute = [&](const Stage& st) {
         v8i bf[TN];
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn)
             bf[tn] = load_frag(st.b, wn * WN + 16 * tn, lane);
-        float sb_wave = 0.0f;
-        v4f sb_col[TN];
+        v4f p[TN];
         if constexpr (MODE == MODE_WGRAD) {
+            float sbn[TN];
 #pragma unroll
             for (int tn = 0; tn < TN; ++tn)
-                sb_col[tn] = *reinterpret_cast<const v4f*>(&st.sb[wn * WN + 16 * tn + 4 * (lane >> 4)]);
-        } else {
-            sb_wave = st.sb[(wn * WN) / BK];
-        }
-        v4f p[TN];
-        float sa_prev = 0.0f;
+                sbn[tn] = st.sb[wn * WN + 16 * tn + (lane & 15)];
+            v4f sa_prev = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int sm = 0; sm < TM; ++sm) {
-            const v8i af = load_frag(st.a, wm * WM + 16 * sm, lane);
-            const float sa = st.sa[wm * WM + 16 * sm + (lane & 15)];
+            for (int sm = 0; sm < TM; ++sm) {
+                const v8i af = load_frag(st.a, wm * WM + 16 * sm, lane);
+                const v4f sa4 = *reinterpret_cast<const v4f*>(&st.sa[wm * WM + 16 * sm + 4 * (lane >> 4)]);
 #pragma unroll
-            for (int tn = 0; tn < TN; ++tn) {
-                if (sm > 0) {
-                    if constexpr (MODE == MODE_WGRAD) {
+                for (int tn = 0; tn < TN; ++tn) {
+                    if (sm > 0) {
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
-                            acc[sm - 1][tn][r] = __builtin_fmaf(p[tn][r], sa_prev * sb_col[tn][r], acc[sm - 1][tn][r]);
-                    } else {
-                        const float sc = sa_prev * sb_wave;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            acc[sm - 1][tn][r] = __builtin_fmaf(p[tn][r], sc, acc[sm - 1][tn][r]);
+                            acc[sm - 1][tn][r] = __builtin_fmaf(p[tn][r], sa_prev[r] * sbn[tn], acc[sm - 1][tn][r]);
                     }
+                    const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+                    p[tn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[tn], zero, 0, 0, 0, 0, 0, 0);
                 }
-                const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-                p[tn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[tn], af, zero, 0, 0, 0, 0, 0, 0);
+                sa_prev = sa4;
             }
-            sa_prev = sa;
-        }
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-            if constexpr (MODE == MODE_WGRAD) {
+            for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    acc[TM - 1][tn][r] = __builtin_fmaf(p[tn][r], sa_prev * sb_col[tn][r], acc[TM - 1][tn][r]);
-            } else {
-                const float sc = sa_prev * sb_wave;
+                    acc[TM - 1][tn][r] = __builtin_fmaf(p[tn][r], sa_prev[r] * sbn[tn], acc[TM - 1][tn][r]);
+        } else {
+            const float sb_wave = st.sb[(wn * WN) / BK];
+            float sa_prev = 0.0f;
+#pragma unroll
+            for (int sm = 0; sm < TM; ++sm) {
+                const v8i af = load_frag(st.a, wm * WM + 16 * sm, lane);
+                const float sa = st.sa[wm * WM + 16 * sm + (lane & 15)];
+                const float sc_prev = sa_prev * sb_wave;
+#pragma unroll
+                for (int tn = 0; tn < TN; ++tn) {
+                    if (sm > 0) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            acc[sm - 1][tn][r] = __builtin_fmaf(p[tn][r], sc_prev, acc[sm - 1][tn][r]);
+                    }
+                    const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+                    p[tn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[tn], af, zero, 0, 0, 0, 0, 0, 0);
+                }
+                sa_prev = sa;
+            }
+            const float sc_last = sa_prev * sb_wave;
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    acc[TM - 1][tn][r] = __builtin_fmaf(p[tn][r], sc, acc[TM - 1][tn][r]);
-            }
+                    acc[TM - 1][tn][r] = __builtin_fmaf(p[tn][r], sc_last, acc[TM - 1][tn][r]);
         }
     };
 
@@ -270,6 +284,38 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
     // ---- epilogue ----------------------------------------------------------
     if (!wave_active)
         return;
+    if constexpr (MODE == MODE_WGRAD) {
+        // lane: column n = ... + (lane & 15), rows m = ... + 4*(lane>>4) + r
+        const int n_lane = n0 + wn * WN + (lane & 15);       // + 16*tn
+        const int m_lane = m0 + wm * WM + 4 * (lane >> 4);   // + 16*sm + r
+#pragma unroll
+        for (int sm = 0; sm < TM; ++sm) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m_lane + 16 * sm + r;
+                if (m >= M)
+                    continue;
+#pragma unroll
+                for (int tn = 0; tn < TN; ++tn) {
+                    const int n = n_lane + 16 * tn;
+                    const float v = acc[sm][tn][r];
+                    const size_t idx = (size_t)m * N + n;
+                    if constexpr (OUT == OUT_BF16) {
+                        static_cast<uint16_t*>(C)[idx] = (uint16_t)f32_to_bf16_bits(v);
+                    } else if constexpr (OUT == OUT_FP32) {
+                        static_cast<float*>(C)[idx] = v;
+                    } else if constexpr (OUT == OUT_FP32_ACC) {
+                        float* dst = static_cast<float*>(C) + idx;
+                        *dst = *dst + v;
+                    } else {
+                        static_cast<float*>(C)[(size_t)split * M * N + idx] = v;
+                    }
+                }
+            }
+        }
+        return;
+    }
+    // lane: row m = ... + (lane & 15), columns n = ... + 4*(lane>>4) .. +3
     const int m_lane = m0 + wm * WM + (lane & 15);        // + 16*sm
     const int n_lane = n0 + wn * WN + 4 * (lane >> 4);    // + 16*tn, 4 consecutive
 #pragma unroll
