@@ -62,16 +62,32 @@ enum { OUT_BF16 = 0, OUT_FP32 = 1, OUT_FP32_ACC = 2, OUT_PARTIAL = 3 };
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 __device__ __forceinline__ int lds_off(int row, int chunk) { return row * BK + ((chunk ^ swz(row)) << 4); }
 
-// 32-byte MFMA operand fragment of a 16x128 slice starting at row `base`:
-// lane l holds row base + (l & 15), logical chunks 2*(l>>4) and 2*(l>>4)+1.
-// The A-side and B-side fragments use the same k <-> (lane, byte) mapping, so
-// every product pairs a[m][k] with b[n][k] whatever order the hardware sums in.
-__device__ __forceinline__ v8i load_frag(const uint8_t* lds, int base, int lane)
+// 32-byte MFMA operand fragment of a 16x128 slice whose first row is a
+// multiple of 16: lane l holds row (l & 15) of the slice, logical chunks
+// 2*(l>>4) and 2*(l>>4)+1.  The swizzle of a row depends only on its low 4
+// bits, i.e. on the lane, so each lane's two byte offsets within any slice
+// are fixed (FragOff) and the slice base folds into the instruction's
+// immediate offset.  The A-side and B-side fragments use the same
+// k <-> (lane, byte) mapping, so every product pairs a[m][k] with b[n][k]
+// whatever order the hardware sums in.
+struct FragOff {
+    int lo, hi;
+};
+
+__device__ __forceinline__ FragOff frag_off(int lane)
 {
-    const int row = base + (lane & 15);
+    const int r = lane & 15;
     const int c0 = 2 * (lane >> 4);
-    const uint4 lo = *reinterpret_cast<const uint4*>(lds + lds_off(row, c0));
-    const uint4 hi = *reinterpret_cast<const uint4*>(lds + lds_off(row, c0 + 1));
+    return {r * BK + ((c0 ^ swz(r)) << 4), r * BK + (((c0 + 1) ^ swz(r)) << 4)};
+}
+
+// `base` is an LDS array and `off` the slice's byte offset in it; each read
+// is a single offset from the array so the compiler keeps track of which LDS
+// object it touches (and does not wait for copies into the other stage).
+__device__ __forceinline__ v8i load_frag(const uint8_t* base, int off, FragOff fo)
+{
+    const uint4 lo = *reinterpret_cast<const uint4*>(&base[off + fo.lo]);
+    const uint4 hi = *reinterpret_cast<const uint4*>(&base[off + fo.hi]);
     v8i f;
     f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
     f[4] = (int)hi.x; f[5] = (int)hi.y; f[6] = (int)hi.z; f[7] = (int)hi.w;
@@ -198,11 +214,14 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
     // and tile, sB one value per wave.  WGRAD (per-column sB) issues it with
     // the A-side fragment first: a lane's 4 rows are 4 consecutive m of one n,
     // so it holds 4 sB values per K-block and one float4 of sA per tile.
+    const FragOff fo = frag_off(lane);
     auto compute = [&](const Stage& st) {
+        const int a_off = wm * WM * BK;    // this wave's 128 A rows
+        const int b_off = wn * WN * BK;    // this wave's 64 B rows
         v8i bf[TN];
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn)
-            bf[tn] = load_frag(st.b, wn * WN + 16 * tn, lane);
+            bf[tn] = load_frag(st.b, b_off + 16 * tn * BK, fo);
         v4f p[TN];
         if constexpr (MODE == MODE_WGRAD) {
             float sbn[TN];
@@ -212,7 +231,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
             v4f sa_prev = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int sm = 0; sm < TM; ++sm) {
-                const v8i af = load_frag(st.a, wm * WM + 16 * sm, lane);
+                const v8i af = load_frag(st.a, a_off + 16 * sm * BK, fo);
                 const v4f sa4 = *reinterpret_cast<const v4f*>(&st.sa[wm * WM + 16 * sm + 4 * (lane >> 4)]);
 #pragma unroll
                 for (int tn = 0; tn < TN; ++tn) {
@@ -236,7 +255,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
             float sa_prev = 0.0f;
 #pragma unroll
             for (int sm = 0; sm < TM; ++sm) {
-                const v8i af = load_frag(st.a, wm * WM + 16 * sm, lane);
+                const v8i af = load_frag(st.a, a_off + 16 * sm * BK, fo);
                 const float sa = st.sa[wm * WM + 16 * sm + (lane & 15)];
                 const float sc_prev = sa_prev * sb_wave;
 #pragma unroll
@@ -261,25 +280,31 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
     };
 
     // ---- main loop: two statically named LDS stages, one barrier per K-block.
-    // The DMA of block kb+1 is in flight while block kb is multiplied.
+    // The DMA of block kb+1 is in flight while block kb is multiplied.  The
+    // wait covers this wave's share of the stage, the barrier the other
+    // waves' (a plain s_barrier: every LDS read of the previous stage has been
+    // consumed by an MFMA before it, so no LDS wait is needed).
+    auto wait_stage = [&]() {
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        __builtin_amdgcn_s_barrier();
+    };
     if (kb_begin < kb_end)
         issue_stage<MODE>(stage0, A, SA, B, SB, kb_begin, m0, n0, M, N, K, KB, wave, lane);
     for (int kb = kb_begin; kb < kb_end; kb += 2) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): this wave's DMA landed
-        __syncthreads();                          // every wave's DMA landed; stage1 free
+        wait_stage();
         if (kb + 1 < kb_end)
             issue_stage<MODE>(stage1, A, SA, B, SB, kb + 1, m0, n0, M, N, K, KB, wave, lane);
         if (wave_active)
             compute(stage0);
         if (kb + 1 >= kb_end)
             break;
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-        __syncthreads();                          // stage0 free, stage1 landed
+        wait_stage();
         if (kb + 2 < kb_end)
             issue_stage<MODE>(stage0, A, SA, B, SB, kb + 2, m0, n0, M, N, K, KB, wave, lane);
         if (wave_active)
             compute(stage1);
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);           // vmcnt(0): no copy outlives the block
 
     // ---- epilogue ----------------------------------------------------------
     if (!wave_active)
