@@ -63,11 +63,13 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="block_stack")
     p.add_argument("--seed", type=int, default=0)
-    p.add_argument("--cpu-tokens", type=int, default=512,
+    p.add_argument("--cpu-tokens", type=int, default=3072,
                    help="token slice for the CPU-oracle baseline (0 = skip)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--ingest-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_DIR"),
-                   help="turn rocprofv3 --pmc counter CSVs into the traffic file and exit")
+    p.add_argument("--ingest-pmc", nargs=4,
+                   metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                   help="turn rocprofv3 --pmc counter CSVs (bench run, then the copy "
+                        "calibration run) into the traffic file and exit")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain 1 GiB device copy (counter calibration) and exit")
     return p.parse_args()
@@ -183,18 +185,17 @@ def _read_pmc_csv(path):
     return out
 
 
-def ingest_pmc(fetch_csv, write_csv, copy_dir):
+def ingest_pmc(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     """Write the traffic file: per kernel, FETCH_SIZE and WRITE_SIZE (KiB per
     dispatch) scaled by the factor a plain copy of known size reads on the
     same counters (bytes expected / bytes counted)."""
     fetch = _read_pmc_csv(fetch_csv)
     write = _read_pmc_csv(write_csv)
-    cf = _read_pmc_csv(os.path.join(copy_dir, "fetch.csv"))
-    cw = _read_pmc_csv(os.path.join(copy_dir, "write.csv"))
+    cf = _read_pmc_csv(copy_fetch_csv)
+    cw = _read_pmc_csv(copy_write_csv)
     copy_bytes = float(1 << 30)
     def copy_factor(tbl):
-        vals = [v for k, vs in tbl.items() if "copy" in k.lower() or "elementwise" in k.lower()
-                for v in vs]
+        vals = [v for k, vs in tbl.items() if "neg" in k.lower() for v in vs]
         if not vals:
             return None
         return copy_bytes / (max(vals) * 1024.0)
@@ -247,6 +248,8 @@ def cpu_baseline(specs, host_tensors, tokens):
     import oracle
     import synth
     oracle.build(force=False)
+    # the host's share of cores: OMP_NUM_THREADS where the host sets it
+    oracle.set_threads(max(1, min(os.cpu_count() or 1, int(os.environ.get("OMP_NUM_THREADS", "16")))))
     flops = 0.0
     t0 = time.perf_counter()
     for spec, t in zip(specs, host_tensors):
@@ -274,15 +277,16 @@ def cpu_baseline(specs, host_tensors, tokens):
 # ---- main --------------------------------------------------------------------------
 
 def copy_calibration():
+    """A plain elementwise copy of known size for calibrating the HBM byte
+    counters: y = -x over 2^28 float32 (1 GiB read, 1 GiB written)."""
     import torch
-    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
-    a.fill_(1)
+    a = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
     b = torch.empty_like(a)
     torch.cuda.synchronize()
     for _ in range(3):
-        b.copy_(a)
+        torch.neg(a, out=b)
     torch.cuda.synchronize()
-    print("copy calibration: 3 x 1 GiB device-to-device copies")
+    print("copy calibration: 3 x neg over 1 GiB float32", flush=True)
 
 
 def main():
@@ -364,7 +368,7 @@ def main():
     dom = max((k for k in kernels if k.startswith("gemm") and "splitk" not in k),
               key=lambda k: kernels[k]["ms_per_step"])
     dk = kernels[dom]
-    traffic = traffic_for(dk["symbol"].replace("void ", ""))
+    traffic = traffic_for(dk["symbol"])
     roofline = {"bound": "mfma", "achieved": dk["tflops"], "peak": FP8_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(dk["tflops"] / FP8_PEAK_TFLOPS, 4),
                 "traffic": traffic, "kernel": dk["symbol"], "launch_class": dom,

@@ -225,6 +225,24 @@ def _sampled_check(mode, c_dev, out_dtype, oa, osa, ob, osb, n_samples, seed):
     return gemm_gates(device_values(c_dev)[ii, jj], ref, bound, out_dtype == torch.bfloat16)
 
 
+def _unquantized_at(mode, t, ii, jj, chunk=512):
+    """The product of the unquantized bf16 operands at (ii[s], jj[s]), in
+    double: the error of the whole FP8 path against a plain matmul is
+    reported, not gated (the pages give no bound for it)."""
+    if mode == FWD:                    # Y[i,j] = x[i,:] . w[j,:]
+        L, R = t["x"].float().numpy(), t["w"].float().numpy()
+    elif mode == DGRAD:                # dX[i,j] = dy[i,:] . w[:,j]
+        L, R = t["dy"].float().numpy(), t["w"].float().numpy().T
+    else:                              # dW[i,j] = dy[:,i] . x[:,j]
+        L, R = t["dy"].float().numpy().T, t["x"].float().numpy().T
+    out = np.empty(len(ii), np.float64)
+    for s0 in range(0, len(ii), chunk):
+        li = L[ii[s0:s0 + chunk]].astype(np.float64)
+        rj = R[jj[s0:s0 + chunk]].astype(np.float64)
+        out[s0:s0 + chunk] = np.einsum("sk,sk->s", li, rj)
+    return out
+
+
 @pytest.mark.parametrize("name,mode,out_dtype", [
     ("qkv_fwd", FWD, torch.bfloat16),
     ("upgate_fwd", FWD, torch.bfloat16),
@@ -244,6 +262,12 @@ def test_workload_full_size_sampled(pf, name, mode, out_dtype):
     g = _sampled_check(mode, c, out_dtype, oa, osa, ob, osb, 20000, 1)
     say("   sampled " + fmt(g))
     assert g["ok"], g
+    rng = np.random.default_rng(5)
+    ii = rng.integers(0, c.shape[0], 4000)
+    jj = rng.integers(0, c.shape[1], 4000)
+    exact = _unquantized_at(mode, t, ii, jj)
+    say(f"   vs unquantized matmul (4000 samples): "
+        f"rel_fro={oracle.rel_fro(device_values(c)[ii, jj], exact):.3e}")
 
 
 def test_block_stack_wgrad_split_sampled(pf):
