@@ -12,6 +12,9 @@
 namespace {
 
 constexpr int64_t kMaxDim = std::numeric_limits<int32_t>::max();
+// The GEMM addresses a row of a 256-row tile with a 32-bit offset
+// row * K + k from the tile's 64-bit base, so K is limited to 2^24.
+constexpr int64_t kMaxGemmK = int64_t(1) << 24;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -67,7 +70,7 @@ bool gemm_shape_ok(int64_t M, int64_t N, int64_t K)
 {
     if (M < 0 || N <= 0 || K <= 0 || N % 128 != 0 || K % 128 != 0)
         return false;
-    if (M > kMaxDim || N > kMaxDim || K > kMaxDim)
+    if (M > kMaxDim || N > kMaxDim || K > kMaxGemmK)
         return false;
     // the launch grid holds tiles_m * tiles_n * splits work-groups (int)
     const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);

@@ -119,22 +119,26 @@ __device__ __forceinline__ const T* uniform_ptr(const T* p)
 // (4 + 4 LDS-DMA instructions of 1 KB, 16 bytes per lane).  Lane L of
 // instruction i fills LDS row 32*wave + 8*i + L/8 at chunk position L%8, so it
 // fetches the logical chunk the swizzle stores there; rows past the end of
-// the matrix read the last row instead (their results are never stored).
+// the matrix read the tile's last row instead (their results are never
+// stored).  `At` / `Bt` point at the tile's first row; the 64-bit row base
+// and K-block offset stay in scalar registers and each lane adds a 32-bit
+// offset (row < 256 and K <= 2^24 keep it below 2^32).
 // Wave 0 also copies the 256 sA values, wave 1 the sB values.
 template <int MODE>
-__device__ __forceinline__ void issue_stage(Stage& st, const uint8_t* A, const float* SA,
-                                            const uint8_t* B, const float* SB, int kb, int m0,
-                                            int n0, int M, int N, int K, int KB, int wave, int lane)
+__device__ __forceinline__ void issue_stage(Stage& st, const uint8_t* At, const float* SA,
+                                            const uint8_t* Bt, const float* SB, int kb, int m0,
+                                            int n0, int rows_a, int rows_b, int M, int N, int K,
+                                            int KB, int wave, int lane)
 {
-    const uint8_t* ab = uniform_ptr(A + (size_t)kb * BK);
-    const uint8_t* bb = uniform_ptr(B + (size_t)kb * BK);
+    const uint8_t* ab = uniform_ptr(At + (size_t)kb * BK);
+    const uint8_t* bb = uniform_ptr(Bt + (size_t)kb * BK);
     const int r0 = 32 * wave + (lane >> 3);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int row = r0 + 8 * i;
         const uint32_t c = 16u * (uint32_t)((lane & 7) ^ swz(row));
-        const uint32_t ao = (uint32_t)min(m0 + row, M - 1) * (uint32_t)K + c;
-        const uint32_t bo = (uint32_t)min(n0 + row, N - 1) * (uint32_t)K + c;
+        const uint32_t ao = (uint32_t)min(row, rows_a - 1) * (uint32_t)K + c;
+        const uint32_t bo = (uint32_t)min(row, rows_b - 1) * (uint32_t)K + c;
         __builtin_amdgcn_global_load_lds(ab + ao, (lds_void*)(st.a + (32 * wave + 8 * i) * BK), 16, 0, 0);
         __builtin_amdgcn_global_load_lds(bb + bo, (lds_void*)(st.b + (32 * wave + 8 * i) * BK), 16, 0, 0);
     }
@@ -195,6 +199,10 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
     const int kb_end = min(KB, kb_begin + kb_per_split);
 
     const bool wave_active = (n0 + wn * WN) < N;
+    const uint8_t* At = A + (size_t)m0 * K;
+    const uint8_t* Bt = B + (size_t)n0 * K;
+    const int rows_a = min(M - m0, BM);
+    const int rows_b = min(N - n0, BN);
 
     v4f acc[TM][TN];
 #pragma unroll
@@ -280,27 +288,30 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
     };
 
     // ---- main loop: two statically named LDS stages, one barrier per K-block.
-    // The DMA of block kb+1 is in flight while block kb is multiplied.  The
-    // wait covers this wave's share of the stage, the barrier the other
+    // The LDS copy of block kb+1 is in flight while block kb is multiplied.
+    // The wait covers this wave's share of the stage, the barrier the other
     // waves' (a plain s_barrier: every LDS read of the previous stage has been
     // consumed by an MFMA before it, so no LDS wait is needed).
+    auto issue = [&](Stage& st, int kb) {
+        issue_stage<MODE>(st, At, SA, Bt, SB, kb, m0, n0, rows_a, rows_b, M, N, K, KB, wave, lane);
+    };
     auto wait_stage = [&]() {
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
         __builtin_amdgcn_s_barrier();
     };
     if (kb_begin < kb_end)
-        issue_stage<MODE>(stage0, A, SA, B, SB, kb_begin, m0, n0, M, N, K, KB, wave, lane);
+        issue(stage0, kb_begin);
     for (int kb = kb_begin; kb < kb_end; kb += 2) {
         wait_stage();
         if (kb + 1 < kb_end)
-            issue_stage<MODE>(stage1, A, SA, B, SB, kb + 1, m0, n0, M, N, K, KB, wave, lane);
+            issue(stage1, kb + 1);
         if (wave_active)
             compute(stage0);
         if (kb + 1 >= kb_end)
             break;
         wait_stage();
         if (kb + 2 < kb_end)
-            issue_stage<MODE>(stage0, A, SA, B, SB, kb + 2, m0, n0, M, N, K, KB, wave, lane);
+            issue(stage0, kb + 2);
         if (wave_active)
             compute(stage1);
     }

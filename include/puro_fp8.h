@@ -134,7 +134,8 @@ puro_status_t puro_fp8_quant_weight(const void* w, int64_t n, int64_t k,
  *   WGRAD: a = qt(dY) [out][T_pad], sa = st(dY), b = qt(X) [in][T_pad],
  *          sb = st(X)
  *
- * Requires M >= 0, N > 0 and K > 0 with N % 128 == 0 and K % 128 == 0.
+ * Requires M >= 0, N > 0 and K > 0 with N % 128 == 0 and K % 128 == 0, and
+ * K <= 2^24 (16,777,216; PURO_ERR_BAD_SHAPE otherwise).
  * accumulate != 0 adds into the existing contents of c and needs
  * c_dtype == PURO_OUT_FP32.  workspace must hold at least
  * puro_fp8_gemm_workspace_bytes(mode, M, N, K) bytes (it may be NULL when

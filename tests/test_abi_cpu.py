@@ -100,6 +100,7 @@ def test_gemm_validation(lib):
     assert call(K=100) == SHAPE
     assert call(M=-5) == SHAPE
     assert call(K=0) == SHAPE
+    assert call(K=(1 << 24) + 128) == SHAPE                 # contraction limit
     assert call(a=None) == NULLP
     assert call(sb=None) == NULLP
     assert call(c=None) == NULLP

@@ -283,3 +283,45 @@ def test_block_stack_wgrad_split_sampled(pf):
     g = _sampled_check(WGRAD, c, torch.float32, oa, osa, ob, osb, 4000, 2)
     say("   sampled " + fmt(g))
     assert g["ok"], g
+
+
+def test_operand_offsets_beyond_4gib(pf):
+    """A [1280 x 2^22] codes (5 GiB): rows 1024 and up start more than 2^32
+    bytes into A.  Only a few rows of A and B hold codes (seeded, both signs);
+    every other output element is exactly zero, so a wrong row offset shows
+    either as a mismatch or as a non-zero where zero is due."""
+    M, N, K = 1280, 256, 1 << 22
+    rows = np.array([0, 1, 700, 1100, 1279])
+    cols = np.array([0, 5, 255])
+    rng = np.random.default_rng(7)
+
+    def codes(n):
+        c = rng.integers(0, 0xFF, (n, K), dtype=np.uint8)
+        c[c == 0x7F] = 0x7E                      # no NaN codes
+        return c
+
+    a_rows, b_rows = codes(len(rows)), codes(len(cols))
+    sa = rng.uniform(0.5, 2.0, (K // 128, M)).astype(np.float32)
+    sb = rng.uniform(0.5, 2.0, (N // 128, K // 128)).astype(np.float32)
+    say("large offsets: FWD M=1280 N=256 K=2^22")
+    A = torch.zeros((M, K), dtype=torch.uint8, device="cuda:0")
+    A[torch.from_numpy(rows).cuda()] = torch.from_numpy(a_rows).cuda()
+    B = torch.zeros((N, K), dtype=torch.uint8, device="cuda:0")
+    B[torch.from_numpy(cols).cuda()] = torch.from_numpy(b_rows).cuda()
+    c = pf.gemm_blockscaled(FWD, A, dev(torch.from_numpy(sa)), B, dev(torch.from_numpy(sb)),
+                            out_dtype=torch.float32)
+    got = host(c)
+    del A, B
+    a = np.zeros((M, K), np.uint8)
+    a[rows] = a_rows
+    b = np.zeros((N, K), np.uint8)
+    b[cols] = b_rows
+    ii, jj = (g.ravel() for g in np.meshgrid(rows, cols, indexing="ij"))
+    ref = oracle.gemm_blockscaled_at(FWD, a, sa, b, sb, ii, jj)
+    bound = hw_accum.bounds(FWD, a, sa, b, sb, ii, jj, ref, chunk=1)
+    g = gemm_gates(got[ii, jj], ref, bound, False)
+    say("   " + fmt(g))
+    assert g["ok"], g
+    nonzero = np.zeros((M, N), bool)
+    nonzero[ii, jj] = True
+    assert not np.any(got[~nonzero]), "output outside the populated rows/columns is not zero"
