@@ -60,7 +60,16 @@ enum { OUT_BF16 = 0, OUT_FP32 = 1, OUT_FP32_ACC = 2, OUT_PARTIAL = 3 };
 // staging writes (8 chunks of 2 consecutive rows per phase) then touch 16
 // distinct 16-byte bank groups.
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
-__device__ __forceinline__ int lds_off(int row, int chunk) { return row * BK + ((chunk ^ swz(row)) << 4); }
+
+// FWD / DGRAD read their B slice in a permuted row order (see frag_off_b)
+// and store it with a swizzle built from row bits 1, 4 and 5 instead:
+// position = c ^ (2 * ((r >> 4) & 3) + ((r >> 1) & 1)).  Within a 16-lane
+// fragment phase the rows of equal parity then carry 8 distinct masks, so
+// the reads stay conflict-free; any per-row XOR keeps the staging writes
+// conflict-free.
+__device__ __forceinline__ int swz_b(int row) { return (((row >> 4) & 3) << 1) | ((row >> 1) & 1); }
+template <int MODE>
+__device__ __forceinline__ int swz_stage_b(int row) { return MODE == 2 ? swz(row) : swz_b(row); }
 
 // 32-byte MFMA operand fragment of a 16x128 slice whose first row is a
 // multiple of 16: lane l holds row (l & 15) of the slice, logical chunks
@@ -79,6 +88,20 @@ __device__ __forceinline__ FragOff frag_off(int lane)
     const int r = lane & 15;
     const int c0 = 2 * (lane >> 4);
     return {r * BK + ((c0 ^ swz(r)) << 4), r * BK + (((c0 + 1) ^ swz(r)) << 4)};
+}
+
+// B-side fragments of FWD / DGRAD: fragment row i of MFMA tile tn is B row
+// 16*(i>>2) + 4*tn + (i&3) of the wave's 64, so the lanes with
+// (lane >> 4) == g end up holding output columns 16*g .. 16*g+15 (4 per
+// tile, tiles side by side): 32 contiguous bytes of bf16 per row for the
+// epilogue.  The row's swizzle mask does not depend on tn, so tile tn is the
+// tn = 0 offsets plus 4*tn rows.
+__device__ __forceinline__ FragOff frag_off_b(int lane)
+{
+    const int i = lane & 15;
+    const int r = 16 * (i >> 2) + (i & 3);
+    const int c0 = 2 * (lane >> 4);
+    return {r * BK + ((c0 ^ swz_b(r)) << 4), r * BK + (((c0 + 1) ^ swz_b(r)) << 4)};
 }
 
 // `base` is an LDS array and `off` the slice's byte offset in it; each read
@@ -136,9 +159,10 @@ __device__ __forceinline__ void issue_stage(Stage& st, const uint8_t* At, const 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int row = r0 + 8 * i;
-        const uint32_t c = 16u * (uint32_t)((lane & 7) ^ swz(row));
-        const uint32_t ao = (uint32_t)min(row, rows_a - 1) * (uint32_t)K + c;
-        const uint32_t bo = (uint32_t)min(row, rows_b - 1) * (uint32_t)K + c;
+        const uint32_t ca = 16u * (uint32_t)((lane & 7) ^ swz(row));
+        const uint32_t cb = 16u * (uint32_t)((lane & 7) ^ swz_stage_b<MODE>(row));
+        const uint32_t ao = (uint32_t)min(row, rows_a - 1) * (uint32_t)K + ca;
+        const uint32_t bo = (uint32_t)min(row, rows_b - 1) * (uint32_t)K + cb;
         __builtin_amdgcn_global_load_lds(ab + ao, (lds_void*)(st.a + (32 * wave + 8 * i) * BK), 16, 0, 0);
         __builtin_amdgcn_global_load_lds(bb + bo, (lds_void*)(st.b + (32 * wave + 8 * i) * BK), 16, 0, 0);
     }
@@ -211,27 +235,48 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
         for (int tn = 0; tn < TN; ++tn)
             acc[sm][tn] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // One K-block from a staged buffer: 32 MFMAs.  The partial of MFMA tile
-    // (sm, tn) is folded into its accumulator (one FMA per element with the
-    // block scale) just before MFMA (sm+1, tn) overwrites it, i.e. four MFMAs
-    // later, so the matrix core always has independent work queued and the
-    // partials need a single set of registers.
+    // One K-block from a staged buffer: 32 MFMAs in 8 rows of 4 (one row =
+    // one 16-row A fragment against the wave's 4 B fragments).  The partial
+    // of MFMA tile (sm, tn) is folded into its accumulator (one FMA per
+    // element with the block scale) in the next row, just before MFMA
+    // (sm+1, tn) overwrites it: four MFMAs after it was issued, so the fold
+    // never waits for the matrix core and the partials need a single set of
+    // registers.  The A fragment of row sm+1 is read from LDS while row sm is
+    // multiplied.
     //
     // FWD / DGRAD issue the MFMA with the B-side fragment first: a lane's 4
     // accumulator rows are 4 consecutive n of one m, sA is one value per lane
-    // and tile, sB one value per wave.  WGRAD (per-column sB) issues it with
-    // the A-side fragment first: a lane's 4 rows are 4 consecutive m of one n,
-    // so it holds 4 sB values per K-block and one float4 of sA per tile.
+    // and tile, sB one value per wave.  The last row's partials are carried
+    // into the next K-block and folded during its first row (with the scale
+    // of the block they belong to), so no K-block ends on a chain of FMAs
+    // waiting for its last MFMAs.  The carried partials start at zero with a
+    // zero scale, and the first fold adds +0 to +0.
+    //
+    // WGRAD (per-column sB) issues it with the A-side fragment first: a
+    // lane's 4 rows are 4 consecutive m of one n, so it holds 4 sB values per
+    // K-block and one float4 of sA per tile.
     const FragOff fo = frag_off(lane);
-    auto compute = [&](const Stage& st) {
-        const int a_off = wm * WM * BK;    // this wave's 128 A rows
-        const int b_off = wn * WN * BK;    // this wave's 64 B rows
-        v8i bf[TN];
+    const FragOff fob = (MODE == MODE_WGRAD) ? fo : frag_off_b(lane);
+    const int a_off = wm * WM * BK;    // this wave's 128 A rows
+    const int b_off = wn * WN * BK;    // this wave's 64 B rows
+    v4f p[TN];
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+        p[tn] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    float sc_carry = 0.0f;
+    auto fold_row = [&](int sm, float sc) {
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn)
-            bf[tn] = load_frag(st.b, b_off + 16 * tn * BK, fo);
-        v4f p[TN];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                acc[sm][tn][r] = __builtin_fmaf(p[tn][r], sc, acc[sm][tn][r]);
+    };
+    auto compute = [&](const Stage& st) {
         if constexpr (MODE == MODE_WGRAD) {
+            v8i bf[TN];
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn)
+                bf[tn] = load_frag(st.b, b_off + 16 * tn * BK, fo);
             float sbn[TN];
 #pragma unroll
             for (int tn = 0; tn < TN; ++tn)
@@ -259,31 +304,41 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
                 for (int r = 0; r < 4; ++r)
                     acc[TM - 1][tn][r] = __builtin_fmaf(p[tn][r], sa_prev[r] * sbn[tn], acc[TM - 1][tn][r]);
         } else {
+            // row 0's A fragment first: the first MFMA waits only for it and B[0]
+            v8i af = load_frag(st.a, a_off, fo);
+            v8i bf[TN];
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn)
+                bf[tn] = load_frag(st.b, b_off + 4 * tn * BK, fob);
             const float sb_wave = st.sb[(wn * WN) / BK];
-            float sa_prev = 0.0f;
+            float sa = st.sa[wm * WM + (lane & 15)];
 #pragma unroll
             for (int sm = 0; sm < TM; ++sm) {
-                const v8i af = load_frag(st.a, a_off + 16 * sm * BK, fo);
-                const float sa = st.sa[wm * WM + 16 * sm + (lane & 15)];
-                const float sc_prev = sa_prev * sb_wave;
+                __builtin_amdgcn_sched_barrier(0);
+                v8i af_next;
+                float sa_next = 0.0f;
+                if (sm + 1 < TM) {
+                    af_next = load_frag(st.a, a_off + 16 * (sm + 1) * BK, fo);
+                    sa_next = st.sa[wm * WM + 16 * (sm + 1) + (lane & 15)];
+                }
+                // fold row sm-1 (row TM-1 of the previous K-block when sm == 0)
+                const float sc_prev = sc_carry;
+                const int fold_sm = (sm == 0) ? TM - 1 : sm - 1;
 #pragma unroll
                 for (int tn = 0; tn < TN; ++tn) {
-                    if (sm > 0) {
 #pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            acc[sm - 1][tn][r] = __builtin_fmaf(p[tn][r], sc_prev, acc[sm - 1][tn][r]);
-                    }
+                    for (int r = 0; r < 4; ++r)
+                        acc[fold_sm][tn][r] = __builtin_fmaf(p[tn][r], sc_prev, acc[fold_sm][tn][r]);
                     const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
                     p[tn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[tn], af, zero, 0, 0, 0, 0, 0, 0);
                 }
-                sa_prev = sa;
+                sc_carry = sa * sb_wave;
+                if (sm + 1 < TM) {
+                    af = af_next;
+                    sa = sa_next;
+                }
             }
-            const float sc_last = sa_prev * sb_wave;
-#pragma unroll
-            for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    acc[TM - 1][tn][r] = __builtin_fmaf(p[tn][r], sc_last, acc[TM - 1][tn][r]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
@@ -316,6 +371,10 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
             compute(stage1);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);           // vmcnt(0): no copy outlives the block
+    if constexpr (MODE != MODE_WGRAD) {
+        if (wave_active)
+            fold_row(TM - 1, sc_carry);               // the last K-block's last row
+    }
 
     // ---- epilogue ----------------------------------------------------------
     if (!wave_active)
@@ -351,32 +410,39 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
         }
         return;
     }
-    // lane: row m = ... + (lane & 15), columns n = ... + 4*(lane>>4) .. +3
+    // lane: row m = ... + (lane & 15); columns n = n_lane + 4*tn + r, i.e. 16
+    // consecutive columns (the B fragments' row order, frag_off_b)
     const int m_lane = m0 + wm * WM + (lane & 15);        // + 16*sm
-    const int n_lane = n0 + wn * WN + 4 * (lane >> 4);    // + 16*tn, 4 consecutive
+    const int n_lane = n0 + wn * WN + 16 * (lane >> 4);
 #pragma unroll
     for (int sm = 0; sm < TM; ++sm) {
         const int m = m_lane + 16 * sm;
         if (m >= M)
             continue;
+        const size_t idx = (size_t)m * N + n_lane;
+        if constexpr (OUT == OUT_BF16) {
+            uint32_t w[8];
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-            const int n = n_lane + 16 * tn;
-            const v4f v = acc[sm][tn];
-            const size_t idx = (size_t)m * N + n;
-            if constexpr (OUT == OUT_BF16) {
-                uint2 o;
-                o.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-                o.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
-                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(C) + idx) = o;
-            } else if constexpr (OUT == OUT_FP32) {
-                *reinterpret_cast<v4f*>(static_cast<float*>(C) + idx) = v;
-            } else if constexpr (OUT == OUT_FP32_ACC) {
-                v4f* dst = reinterpret_cast<v4f*>(static_cast<float*>(C) + idx);
-                *dst = *dst + v;
-            } else {
-                float* ws = static_cast<float*>(C) + (size_t)split * M * N;
-                *reinterpret_cast<v4f*>(ws + idx) = v;
+            for (int tn = 0; tn < TN; ++tn) {
+                w[2 * tn] = f32_to_bf16_bits(acc[sm][tn][0]) | (f32_to_bf16_bits(acc[sm][tn][1]) << 16);
+                w[2 * tn + 1] = f32_to_bf16_bits(acc[sm][tn][2]) | (f32_to_bf16_bits(acc[sm][tn][3]) << 16);
+            }
+            uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(C) + idx);
+            dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+            dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        } else {
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) {
+                const v4f v = acc[sm][tn];
+                if constexpr (OUT == OUT_FP32) {
+                    *reinterpret_cast<v4f*>(static_cast<float*>(C) + idx + 4 * tn) = v;
+                } else if constexpr (OUT == OUT_FP32_ACC) {
+                    v4f* dst = reinterpret_cast<v4f*>(static_cast<float*>(C) + idx + 4 * tn);
+                    *dst = *dst + v;
+                } else {
+                    float* ws = static_cast<float*>(C) + (size_t)split * M * N;
+                    *reinterpret_cast<v4f*>(ws + idx + 4 * tn) = v;
+                }
             }
         }
     }
