@@ -89,13 +89,16 @@ __device__ __forceinline__ uint2 encode8(const uint4& v, float pre, float r)
     return o;
 }
 
-// FP32 -> bf16 bits, round to nearest even (finite inputs; overflow rounds
-// to infinity).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
+// Two FP32 values -> packed bf16 (a in the low half), round to nearest even,
+// denormals kept: one v_cvt_pk_bf16_f32.  For every non-NaN input this is
+// the integer rounding u + 0x7FFF + ((u >> 16) & 1), upper half (checked on
+// the device over all 2^32 patterns).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b)
 {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
+    const bf16x2_t h = __builtin_convertvector((f32x2_t){a, b}, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, h);
 }
 
 }  // namespace puro

@@ -200,33 +200,34 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
     const int wm = wave >> 2;        // 0..1
     const int wn = wave & 3;         // 0..3
 
-    // ---- tile assignment: XCD-compact, grouped along M -------------------
+    // ---- work units: (split, output tile), XCD-compact and grouped along M.
+    // The grid is persistent: work-group g takes units g, g + G, g + 2G, ...
+    // (G = gridDim.x, a multiple of 8 whenever it is below the unit count).
+    // Work-groups are dealt to the 8 XCDs round-robin, so unit u runs on XCD
+    // u % 8; the remap below gives each XCD a contiguous range of units, so
+    // the tiles that run together on one XCD share A and B panels in its L2.
     const int total = tiles_m * tiles_n * splits;
-    int w = blockIdx.x;
-    if ((total & 7) == 0)
-        w = (w & 7) * (total >> 3) + (w >> 3);
     const int tiles = tiles_m * tiles_n;
-    const int split = w / tiles;
-    const int tile = w - split * tiles;
-    const int group_size = GROUP_M * tiles_n;
-    const int group = tile / group_size;
-    const int first_m = group * GROUP_M;
-    const int gm = min(tiles_m - first_m, GROUP_M);
-    const int in_group = tile - group * group_size;
-    const int tile_m = first_m + in_group % gm;
-    const int tile_n = in_group / gm;
-    const int m0 = tile_m * BM;
-    const int n0 = tile_n * BN;
-
     const int KB = K / BK;
-    const int kb_begin = split * kb_per_split;
-    const int kb_end = min(KB, kb_begin + kb_per_split);
-
-    const bool wave_active = (n0 + wn * WN) < N;
-    const uint8_t* At = A + (size_t)m0 * K;
-    const uint8_t* Bt = B + (size_t)n0 * K;
-    const int rows_a = min(M - m0, BM);
-    const int rows_b = min(N - n0, BN);
+    struct Unit {
+        int m0, n0, split, kb_begin, kb_end;
+    };
+    auto unit_of = [&](int u) __attribute__((always_inline)) -> Unit {
+        int w = u;
+        if ((total & 7) == 0)
+            w = (w & 7) * (total >> 3) + (w >> 3);
+        const int split = w / tiles;
+        const int tile = w - split * tiles;
+        const int group_size = GROUP_M * tiles_n;
+        const int group = tile / group_size;
+        const int first_m = group * GROUP_M;
+        const int gm = min(tiles_m - first_m, GROUP_M);
+        const int in_group = tile - group * group_size;
+        const int tile_m = first_m + in_group % gm;
+        const int tile_n = in_group / gm;
+        const int kb_begin = split * kb_per_split;
+        return {tile_m * BM, tile_n * BN, split, kb_begin, min(KB, kb_begin + kb_per_split)};
+    };
 
     v4f acc[TM][TN];
 #pragma unroll
@@ -264,14 +265,14 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
     for (int tn = 0; tn < TN; ++tn)
         p[tn] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     float sc_carry = 0.0f;
-    auto fold_row = [&](int sm, float sc) {
+    auto fold_row = [&](int sm, float sc) __attribute__((always_inline)) {
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 acc[sm][tn][r] = __builtin_fmaf(p[tn][r], sc, acc[sm][tn][r]);
     };
-    auto compute = [&](const Stage& st) {
+    auto compute = [&](const Stage& st) __attribute__((always_inline)) {
         if constexpr (MODE == MODE_WGRAD) {
             v8i bf[TN];
 #pragma unroll
@@ -342,110 +343,152 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
         }
     };
 
-    // ---- main loop: two statically named LDS stages, one barrier per K-block.
-    // The LDS copy of block kb+1 is in flight while block kb is multiplied.
-    // The wait covers this wave's share of the stage, the barrier the other
-    // waves' (a plain s_barrier: every LDS read of the previous stage has been
-    // consumed by an MFMA before it, so no LDS wait is needed).
-    auto issue = [&](Stage& st, int kb) {
-        issue_stage<MODE>(st, At, SA, Bt, SB, kb, m0, n0, rows_a, rows_b, M, N, K, KB, wave, lane);
+    // ---- epilogue of one unit: C (+)= acc ------------------------------------
+    // OUT_PARTIAL writes the unit's split-K partial to plane `split` of C.
+    auto store4 = [&](size_t idx, int split, v4f v) __attribute__((always_inline)) {   // 4 consecutive FP32
+        if constexpr (OUT == OUT_FP32) {
+            *reinterpret_cast<v4f*>(static_cast<float*>(C) + idx) = v;
+        } else if constexpr (OUT == OUT_FP32_ACC) {
+            v4f* dst = reinterpret_cast<v4f*>(static_cast<float*>(C) + idx);
+            *dst = *dst + v;
+        } else if constexpr (OUT == OUT_PARTIAL) {
+            *reinterpret_cast<v4f*>(static_cast<float*>(C) + (size_t)split * M * N + idx) = v;
+        }
     };
-    auto wait_stage = [&]() {
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-        __builtin_amdgcn_s_barrier();
+    auto store1 = [&](size_t idx, int split, float v) __attribute__((always_inline)) {        // one element
+        if constexpr (OUT == OUT_BF16) {
+            static_cast<uint16_t*>(C)[idx] = (uint16_t)pack_bf16(v, 0.0f);
+        } else if constexpr (OUT == OUT_FP32) {
+            static_cast<float*>(C)[idx] = v;
+        } else if constexpr (OUT == OUT_FP32_ACC) {
+            float* dst = static_cast<float*>(C) + idx;
+            *dst = *dst + v;
+        } else {
+            static_cast<float*>(C)[(size_t)split * M * N + idx] = v;
+        }
     };
-    if (kb_begin < kb_end)
-        issue(stage0, kb_begin);
-    for (int kb = kb_begin; kb < kb_end; kb += 2) {
-        wait_stage();
-        if (kb + 1 < kb_end)
-            issue(stage1, kb + 1);
-        if (wave_active)
-            compute(stage0);
-        if (kb + 1 >= kb_end)
-            break;
-        wait_stage();
-        if (kb + 2 < kb_end)
-            issue(stage0, kb + 2);
-        if (wave_active)
-            compute(stage1);
-    }
-    __builtin_amdgcn_s_waitcnt(0x0F70);           // vmcnt(0): no copy outlives the block
-    if constexpr (MODE != MODE_WGRAD) {
-        if (wave_active)
-            fold_row(TM - 1, sc_carry);               // the last K-block's last row
-    }
-
-    // ---- epilogue ----------------------------------------------------------
-    if (!wave_active)
-        return;
-    if constexpr (MODE == MODE_WGRAD) {
-        // lane: column n = ... + (lane & 15), rows m = ... + 4*(lane>>4) + r
-        const int n_lane = n0 + wn * WN + (lane & 15);       // + 16*tn
-        const int m_lane = m0 + wm * WM + 4 * (lane >> 4);   // + 16*sm + r
+    auto epilogue = [&](const Unit& t) __attribute__((always_inline)) {
+        if constexpr (MODE != MODE_WGRAD)
+            fold_row(TM - 1, sc_carry);               // the unit's last row
+        if ((t.n0 + wn * WN) >= N)
+            return;
+        if constexpr (MODE == MODE_WGRAD) {
+            // lane: column n = n_lane + 16*tn, rows m = m_lane + 16*sm + r
+            const int n_lane = t.n0 + wn * WN + (lane & 15);
+            const int m_lane = t.m0 + wm * WM + 4 * (lane >> 4);
 #pragma unroll
-        for (int sm = 0; sm < TM; ++sm) {
+            for (int sm = 0; sm < TM; ++sm)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = m_lane + 16 * sm + r;
-                if (m >= M)
-                    continue;
+                for (int r = 0; r < 4; ++r) {
+                    const int m = m_lane + 16 * sm + r;
+                    if (m < M) {
 #pragma unroll
-                for (int tn = 0; tn < TN; ++tn) {
-                    const int n = n_lane + 16 * tn;
-                    const float v = acc[sm][tn][r];
-                    const size_t idx = (size_t)m * N + n;
-                    if constexpr (OUT == OUT_BF16) {
-                        static_cast<uint16_t*>(C)[idx] = (uint16_t)f32_to_bf16_bits(v);
-                    } else if constexpr (OUT == OUT_FP32) {
-                        static_cast<float*>(C)[idx] = v;
-                    } else if constexpr (OUT == OUT_FP32_ACC) {
-                        float* dst = static_cast<float*>(C) + idx;
-                        *dst = *dst + v;
-                    } else {
-                        static_cast<float*>(C)[(size_t)split * M * N + idx] = v;
+                        for (int tn = 0; tn < TN; ++tn)
+                            store1((size_t)m * N + n_lane + 16 * tn, t.split, acc[sm][tn][r]);
                     }
                 }
-            }
-        }
-        return;
-    }
-    // lane: row m = ... + (lane & 15); columns n = n_lane + 4*tn + r, i.e. 16
-    // consecutive columns (the B fragments' row order, frag_off_b)
-    const int m_lane = m0 + wm * WM + (lane & 15);        // + 16*sm
-    const int n_lane = n0 + wn * WN + 16 * (lane >> 4);
-#pragma unroll
-    for (int sm = 0; sm < TM; ++sm) {
-        const int m = m_lane + 16 * sm;
-        if (m >= M)
-            continue;
-        const size_t idx = (size_t)m * N + n_lane;
-        if constexpr (OUT == OUT_BF16) {
-            uint32_t w[8];
-#pragma unroll
-            for (int tn = 0; tn < TN; ++tn) {
-                w[2 * tn] = f32_to_bf16_bits(acc[sm][tn][0]) | (f32_to_bf16_bits(acc[sm][tn][1]) << 16);
-                w[2 * tn + 1] = f32_to_bf16_bits(acc[sm][tn][2]) | (f32_to_bf16_bits(acc[sm][tn][3]) << 16);
-            }
-            uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(C) + idx);
-            dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-            dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
         } else {
+            // lane: row m = m_lane + 16*sm; columns n_lane + 4*tn + r, i.e. 16
+            // consecutive columns (the B fragments' row order, frag_off_b)
+            const int m_lane = t.m0 + wm * WM + (lane & 15);
+            const int n_lane = t.n0 + wn * WN + 16 * (lane >> 4);
 #pragma unroll
-            for (int tn = 0; tn < TN; ++tn) {
-                const v4f v = acc[sm][tn];
-                if constexpr (OUT == OUT_FP32) {
-                    *reinterpret_cast<v4f*>(static_cast<float*>(C) + idx + 4 * tn) = v;
-                } else if constexpr (OUT == OUT_FP32_ACC) {
-                    v4f* dst = reinterpret_cast<v4f*>(static_cast<float*>(C) + idx + 4 * tn);
-                    *dst = *dst + v;
+            for (int sm = 0; sm < TM; ++sm) {
+                const int m = m_lane + 16 * sm;
+                if (m >= M)
+                    continue;
+                const size_t idx = (size_t)m * N + n_lane;
+                if constexpr (OUT == OUT_BF16) {
+                    uint32_t w[8];
+#pragma unroll
+                    for (int tn = 0; tn < TN; ++tn) {
+                        w[2 * tn] = pack_bf16(acc[sm][tn][0], acc[sm][tn][1]);
+                        w[2 * tn + 1] = pack_bf16(acc[sm][tn][2], acc[sm][tn][3]);
+                    }
+                    uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(C) + idx);
+                    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+                    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
                 } else {
-                    float* ws = static_cast<float*>(C) + (size_t)split * M * N;
-                    *reinterpret_cast<v4f*>(ws + idx + 4 * tn) = v;
+#pragma unroll
+                    for (int tn = 0; tn < TN; ++tn)
+                        store4(idx + 4 * tn, t.split, acc[sm][tn]);
                 }
             }
         }
+    };
+    auto reset = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int sm = 0; sm < TM; ++sm)
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn)
+                acc[sm][tn] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+            p[tn] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        sc_carry = 0.0f;
+    };
+
+    // ---- main loop over the steps (unit, K-block) of this work-group -------
+    // Two statically named LDS stages alternate, one barrier per step.  At
+    // the top of a step the wait covers this wave's share of the stage and
+    // the barrier the other waves' (a plain s_barrier: every LDS read of the
+    // previous stage was consumed by an MFMA before it).  Then
+    //   * the previous unit's epilogue runs if it is due, so its stores drain
+    //     while this block is multiplied, and the accumulators restart;
+    //   * the LDS copy of the next step's block -- the next K-block, or the
+    //     first one of the next unit -- is issued into the other stage;
+    //   * the block is multiplied.
+    // A work-group therefore never idles between units: the next unit's
+    // first block is already in LDS when the last block of a unit is done.
+    auto issue = [&](Stage& st, const Unit& t, int kb) __attribute__((always_inline)) {
+        const uint8_t* At = A + (size_t)t.m0 * K;
+        const uint8_t* Bt = B + (size_t)t.n0 * K;
+        issue_stage<MODE>(st, At, SA, Bt, SB, kb, t.m0, t.n0, min(M - t.m0, BM),
+                          min(N - t.n0, BN), M, N, K, KB, wave, lane);
+    };
+    const int G = gridDim.x;
+    int u = blockIdx.x;
+    Unit cur = unit_of(u);
+    int kb = cur.kb_begin;
+    bool have_next = u + G < total;
+    Unit nxt = unit_of(have_next ? u + G : u);
+    Unit done = cur;
+    bool pending = false;
+    issue(stage0, cur, kb);
+    auto step = [&](Stage& st, Stage& other) __attribute__((always_inline)) -> bool {
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        if (pending) {
+            epilogue(done);
+            reset();
+            pending = false;
+        }
+        const bool unit_ends = kb + 1 >= cur.kb_end;
+        if (!unit_ends)
+            issue(other, cur, kb + 1);
+        else if (have_next)
+            issue(other, nxt, nxt.kb_begin);
+        if ((cur.n0 + wn * WN) < N)
+            compute(st);
+        if (!unit_ends) {
+            ++kb;
+            return true;
+        }
+        done = cur;
+        pending = true;
+        if (!have_next)
+            return false;
+        u += G;
+        cur = nxt;
+        kb = cur.kb_begin;
+        have_next = u + G < total;
+        nxt = unit_of(have_next ? u + G : u);
+        return true;
+    };
+    while (step(stage0, stage1) && step(stage1, stage0)) {
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0)
+    epilogue(done);
 }
 
 // Sum of the split-K partials in split order, then the requested output.
@@ -461,8 +504,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
             s = s + *reinterpret_cast<const v4f*>(ws + (size_t)z * plane + 4 * i);
         if constexpr (OUT == OUT_BF16) {
             uint2 o;
-            o.x = f32_to_bf16_bits(s[0]) | (f32_to_bf16_bits(s[1]) << 16);
-            o.y = f32_to_bf16_bits(s[2]) | (f32_to_bf16_bits(s[3]) << 16);
+            o.x = pack_bf16(s[0], s[1]);
+            o.y = pack_bf16(s[2], s[3]);
             *reinterpret_cast<uint2*>(static_cast<uint16_t*>(C) + 4 * i) = o;
         } else if constexpr (OUT == OUT_FP32) {
             *reinterpret_cast<v4f*>(static_cast<float*>(C) + 4 * i) = s;
@@ -505,6 +548,24 @@ size_t gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K)
     return s > 1 ? (size_t)s * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
+// Persistent grid: one work-group per compute unit of the stream's device
+// (the kernel holds one work-group per CU), a multiple of 8 so the units of
+// one XCD stay contiguous; fewer when there are fewer units.
+static int persistent_grid(int units, hipStream_t stream)
+{
+    int dev = 0;
+    if (stream == nullptr || hipStreamGetDevice(stream, &dev) != hipSuccess) {
+        if (hipGetDevice(&dev) != hipSuccess)
+            dev = 0;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    if (units <= cus)
+        return units;
+    return cus >= 8 ? cus / 8 * 8 : cus;
+}
+
 template <int MODE>
 static hipError_t launch_mode(int out, const uint8_t* a, const float* sa, const uint8_t* b,
                               const float* sb, void* c, void* ws, int M, int N, int K,
@@ -514,7 +575,9 @@ static hipError_t launch_mode(int out, const uint8_t* a, const float* sa, const 
     const int tiles_n = (N + BN - 1) / BN;
     const int KB = K / BK;
     const int kbps = (KB + splits - 1) / splits;
-    const dim3 grid((unsigned)(tiles_m * tiles_n * splits));
+    if (KB <= 0 || (splits - 1) * kbps >= KB)   // every unit needs a K-block
+        return hipErrorInvalidValue;
+    const dim3 grid((unsigned)persistent_grid(tiles_m * tiles_n * splits, stream));
     if (splits > 1) {
         gemm_bs_kernel<MODE, OUT_PARTIAL><<<grid, NTHREADS, 0, stream>>>(
             a, sa, b, sb, ws, M, N, K, tiles_m, tiles_n, splits, kbps);

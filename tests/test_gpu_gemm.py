@@ -149,6 +149,25 @@ def test_split_k_paths(pf, mode):
     run_case(pf, mode, T, d_in, d_out, torch.float32, accumulate=True)
 
 
+@pytest.mark.parametrize("mode,T,d_in,d_out", [
+    (FWD, 1000, 768, 512),
+    (DGRAD, 513, 384, 640),
+    (FWD, 256, 2048, 256),      # split-K: the reduce kernel rounds
+])
+def test_bf16_output_is_rne_of_fp32(pf, mode, T, d_in, d_out):
+    """The bf16 epilogue rounds the FP32 accumulator to nearest even: the
+    bf16 output equals the oracle's RNE of the same GEMM's FP32 output, bit
+    for bit (the tolerance gates alone would not tell RNE from truncation)."""
+    x, w, dy = make_inputs(T, d_in, d_out, 21)
+    say("bf16 rounding", ["fwd", "dgrad", "wgrad"][mode], f"T={T} in={d_in} out={d_out}")
+    a, sa, b, sb = device_operands(pf, mode, x, w, dy)
+    c32 = pf.gemm_blockscaled(mode, a, sa, b, sb, out_dtype=torch.float32)
+    c16 = pf.gemm_blockscaled(mode, a, sa, b, sb, out_dtype=torch.bfloat16)
+    want = oracle.f32_to_bf16_bits(host(c32).ravel())
+    got = bf16_host_bits(c16).ravel()
+    assert np.array_equal(got, want), f"{int(np.sum(got != want))} elements differ"
+
+
 def test_tiny_forward_workload(pf):
     """X[256x512] N(0,1) with 4 outlier channels x50, W[512x512] N(0,0.02),
     seed 0: the complete output, FP32 and bf16."""
