@@ -35,8 +35,9 @@ puro_status_t check_act(const void* x, int64_t rows, int64_t cols, const uint8_t
 {
     if (rows < 0 || cols <= 0 || cols % 128 != 0 || cols > kMaxDim)
         return PURO_ERR_BAD_SHAPE;
-    // grid limits: rows_pad/128 blocks in x, cols/128 in y (< 65536)
-    if ((rows + 127) / 128 > kMaxDim || cols / 128 > 65535)
+    // grid limit: one work-group per 128x128 block, a 1-D grid (each factor
+    // is bounded first so the product cannot overflow)
+    if (rows > kMaxDim * 128 || ((rows + 127) / 128) * (cols / 128) > kMaxDim)
         return PURO_ERR_BAD_SHAPE;
     if (rows == 0)
         return PURO_OK;                      // empty input: nothing to do
@@ -57,7 +58,7 @@ puro_status_t check_weight(const void* w, int64_t n, int64_t k, const uint8_t* q
                            const uint8_t* qt, const float* s)
 {
     if (n <= 0 || k <= 0 || n % 128 != 0 || k % 128 != 0 || n > kMaxDim || k > kMaxDim ||
-        k / 128 > 65535)
+        (n / 128) * (k / 128) > kMaxDim)
         return PURO_ERR_BAD_SHAPE;
     if (!w || !q || !s)
         return PURO_ERR_NULL_POINTER;

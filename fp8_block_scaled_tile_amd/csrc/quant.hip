@@ -20,6 +20,17 @@
 
 namespace puro {
 
+#ifndef PURO_QUANT_GROUP_ROWS
+#define PURO_QUANT_GROUP_ROWS 8
+#endif
+// Block order: the grid is 1-D and walks the 128x128 blocks in groups of
+// kGroupRows block rows, column block by column block inside a group, so
+// the work-groups in flight at any moment read a few contiguous row bands
+// and write contiguous runs of the transposed copy (a plain row-major or
+// column-major walk concentrates the reads or the transposed writes on a
+// few HBM channels when rows are 8 KB or more apart).
+constexpr int kGroupRows = PURO_QUANT_GROUP_ROWS;
+
 template <bool ROW, bool COL, bool WEIGHT, bool WT>
 __global__ __launch_bounds__(256) void quant_block_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_t,
@@ -36,8 +47,20 @@ __global__ __launch_bounds__(256) void quant_block_kernel(
     const int t = threadIdx.x;
     const int qd = t & 15;       // column chunk of 8 elements
     const int g = t >> 4;        // row group of 8 rows
-    const int64_t rb = blockIdx.x;
-    const int64_t cb = blockIdx.y;
+    const int64_t nrb = (WEIGHT ? rows : ld_t) / 128;   // block rows
+    const int64_t ncb = cols / 128;                      // block columns
+    int64_t rb, cb;
+    if (kGroupRows <= 0) {            // column blocks fastest
+        rb = blockIdx.x / ncb;
+        cb = blockIdx.x - rb * ncb;
+    } else {
+        const int64_t per_group = (int64_t)kGroupRows * ncb;
+        const int64_t group = blockIdx.x / per_group;
+        const int64_t j = blockIdx.x - group * per_group;
+        const int64_t gr = min((int64_t)kGroupRows, nrb - group * kGroupRows);
+        cb = j / gr;
+        rb = group * kGroupRows + (j - cb * gr);
+    }
     const int64_t row0 = rb * 128 + 8 * g;
     const int64_t col0 = cb * 128 + 8 * qd;
 
@@ -185,7 +208,7 @@ hipError_t launch_quant_act(const void* x, int64_t rows, int64_t cols, uint8_t* 
                             uint8_t* qt, float* st, hipStream_t stream)
 {
     const int64_t rows_pad = (rows + 127) / 128 * 128;
-    const dim3 grid((unsigned)(rows_pad / 128), (unsigned)(cols / 128));
+    const dim3 grid((unsigned)((rows_pad / 128) * (cols / 128)));
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     const bool row = q != nullptr, col = qt != nullptr;
     if (row && col)
@@ -200,7 +223,7 @@ hipError_t launch_quant_act(const void* x, int64_t rows, int64_t cols, uint8_t* 
 hipError_t launch_quant_weight(const void* w, int64_t n, int64_t k, uint8_t* q, uint8_t* qt,
                                float* s, hipStream_t stream)
 {
-    const dim3 grid((unsigned)(n / 128), (unsigned)(k / 128));
+    const dim3 grid((unsigned)((n / 128) * (k / 128)));
     const uint16_t* wb = static_cast<const uint16_t*>(w);
     if (qt)
         quant_block_kernel<false, false, true, true><<<grid, 256, 0, stream>>>(wb, n, k, n, q, s, qt, nullptr);
