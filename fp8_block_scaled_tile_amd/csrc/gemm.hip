@@ -272,7 +272,11 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
             for (int r = 0; r < 4; ++r)
                 acc[sm][tn][r] = __builtin_fmaf(p[tn][r], sc, acc[sm][tn][r]);
     };
-    auto compute = [&](const Stage& st) __attribute__((always_inline)) {
+    // `after_row0` (the next stage's LDS copy) runs once row 0's MFMAs are
+    // issued: with no copy outstanding the compiler can wait for each of the
+    // block's first fragments individually (while an LDS-DMA copy is in
+    // flight it makes every LDS-read wait a full lgkmcnt(0)).
+    auto compute = [&](const Stage& st, auto&& after_row0) __attribute__((always_inline)) {
         if constexpr (MODE == MODE_WGRAD) {
             v8i bf[TN];
 #pragma unroll
@@ -298,6 +302,11 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
                     p[tn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[tn], zero, 0, 0, 0, 0, 0, 0);
                 }
                 sa_prev = sa4;
+                if (sm == 0) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    after_row0();
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
 #pragma unroll
             for (int tn = 0; tn < TN; ++tn)
@@ -305,12 +314,17 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
                 for (int r = 0; r < 4; ++r)
                     acc[TM - 1][tn][r] = __builtin_fmaf(p[tn][r], sa_prev[r] * sbn[tn], acc[TM - 1][tn][r]);
         } else {
-            // row 0's A fragment first: the first MFMA waits only for it and B[0]
+            // Row 0's A fragment, then B[0..3] in MFMA order, each group fenced:
+            // LDS reads complete in issue order, so MFMA (0, tn) waits only
+            // for A and B[0..tn], not for every read of the block's head.
             v8i af = load_frag(st.a, a_off, fo);
             v8i bf[TN];
 #pragma unroll
-            for (int tn = 0; tn < TN; ++tn)
+            for (int tn = 0; tn < TN; ++tn) {
+                __builtin_amdgcn_sched_barrier(0);
                 bf[tn] = load_frag(st.b, b_off + 4 * tn * BK, fob);
+            }
+            __builtin_amdgcn_sched_barrier(0);
             const float sb_wave = st.sb[(wn * WN) / BK];
             float sa = st.sa[wm * WM + (lane & 15)];
 #pragma unroll
@@ -332,11 +346,16 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
                         acc[fold_sm][tn][r] = __builtin_fmaf(p[tn][r], sc_prev, acc[fold_sm][tn][r]);
                     const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
                     p[tn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[tn], af, zero, 0, 0, 0, 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);   // MFMAs in tn order
                 }
                 sc_carry = sa * sb_wave;
                 if (sm + 1 < TM) {
                     af = af_next;
                     sa = sa_next;
+                }
+                if (sm == 0) {
+                    after_row0();
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -456,7 +475,14 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
     bool pending = false;
     issue(stage0, cur, kb);
     auto step = [&](Stage& st, Stage& other) __attribute__((always_inline)) -> bool {
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        // vmcnt(0): this wave's share of the stage has landed.  lgkmcnt(0)
+        // costs nothing here (every LDS read of the previous step was
+        // consumed by an MFMA) but clears the compiler's view of the last
+        // copy as a pending LDS event, which would otherwise turn the block
+        // head's per-fragment waits into full ones.  The hardware tracks
+        // LDS-DMA copies with vmcnt only (checked on the device: LDS still
+        // holds the old data after lgkmcnt(0), the new data after vmcnt(0)).
+        __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
         if (pending) {
             epilogue(done);
@@ -464,12 +490,21 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
             pending = false;
         }
         const bool unit_ends = kb + 1 >= cur.kb_end;
-        if (!unit_ends)
-            issue(other, cur, kb + 1);
-        else if (have_next)
-            issue(other, nxt, nxt.kb_begin);
-        if ((cur.n0 + wn * WN) < N)
-            compute(st);
+        auto copy_next = [&]() __attribute__((always_inline)) {
+            if (!unit_ends)
+                issue(other, cur, kb + 1);
+            else if (have_next)
+                issue(other, nxt, nxt.kb_begin);
+        };
+        // Waves whose columns lie beyond N only copy.  Their copy comes after
+        // the compute region: an LDS copy on any path into the block head
+        // would make the compiler wait for all of the head's reads at once.
+        const bool active = (cur.n0 + wn * WN) < N;
+        if (active)
+            compute(st, copy_next);
+        __builtin_amdgcn_sched_barrier(0);
+        if (!active)
+            copy_next();
         if (!unit_ends) {
             ++kb;
             return true;
