@@ -19,6 +19,10 @@ launch inside the timed region, on the stream the kernels run on; the
 dominant kernel's achieved rate is reported against the MI355X dense FP8
 MFMA peak (5.0 PFLOP/s), the quantizers' against HBM (8 TB/s).
 
+For context, the same 12 products are also timed as plain BF16 GEMMs of the
+vendor library (torch.matmul), after the FP8 timed region ("bf16_reference",
+with the FP8/BF16 step speedup).
+
 The CPU baseline times the plain CPU oracle (quantize + block-scaled GEMM in
 all three modes) on a bounded slice of the same workload: the first
 `--cpu-tokens` tokens of every linear layer, all host cores.
@@ -66,6 +70,8 @@ def parse_args():
     p.add_argument("--cpu-tokens", type=int, default=3072,
                    help="token slice for the CPU-oracle baseline (0 = skip)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-bf16-reference", action="store_true",
+                   help="skip the vendor BF16 GEMM comparison (context only)")
     p.add_argument("--ingest-pmc", nargs=4,
                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                    help="turn rocprofv3 --pmc counter CSVs (bench run, then the copy "
@@ -239,6 +245,40 @@ def traffic_for(symbol_prefix):
     return None
 
 
+# ---- BF16 comparator ------------------------------------------------------------
+
+def bf16_reference(torch, layers, steps):
+    """The same 12 products as plain BF16 GEMMs of the vendor library
+    (torch.matmul -> hipBLASLt / rocBLAS), bf16 outputs, with the transposed
+    operands materialized beforehand (outside the timing).  This is the
+    unquantized linear layer the FP8 path replaces; it is context for the
+    FP8/BF16 speedup, not part of the measured step."""
+    bufs = []
+    for L in layers:
+        bufs.append((L.x, L.w.t().contiguous(), L.dy, L.w, L.dy.t().contiguous(),
+                     torch.empty_like(L.y), torch.empty_like(L.dx),
+                     torch.empty((L.dout, L.din), dtype=torch.bfloat16, device="cuda:0")))
+
+    def step():
+        for x, wt, dy, w, dyt, y, dx, dw in bufs:
+            torch.matmul(x, wt, out=y)          # Y  = X . W^T
+            torch.matmul(dy, w, out=dx)         # dX = dY . W
+            torch.matmul(dyt, x, out=dw)        # dW = dY^T . X
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = sum(2.0 * L.T * L.din * L.dout * 3 for L in layers)
+    del bufs
+    return ms, flops / (ms * 1e-3) / 1e12
+
+
 # ---- CPU baseline --------------------------------------------------------------
 
 def cpu_baseline(specs, host_tensors, tokens):
@@ -376,6 +416,15 @@ def main():
     gemm_ms = sum(v["ms_per_step"] for k, v in kernels.items() if k.startswith("gemm"))
     quant_ms = sum(v["ms_per_step"] for k, v in kernels.items() if k.startswith("quant"))
 
+    bf16 = None
+    if not args.no_bf16_reference:
+        bms, btf = bf16_reference(torch, layers, args.steps)
+        bf16 = {"value": round(btf, 1), "unit": "TFLOP/s", "ms_per_step": round(bms, 4),
+                "kind": "vendor BF16 GEMM (torch.matmul -> hipBLASLt/rocBLAS), same 12 products, "
+                        "bf16 outputs, transposed operands pre-materialized; context, not timed above",
+                "fp8_step_speedup": round(bms / ms_per_step, 3),
+                "fp8_gemm_speedup": round(bms / gemm_ms, 3) if gemm_ms else None}
+
     cpu = None
     if host_tensors is not None:
         for L in layers:     # free nothing on the device; the oracle runs on the host
@@ -407,6 +456,7 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "cpu_baseline": cpu,
+        "bf16_reference": bf16,
         "input_generation_s": round(gen_s, 1),
     }
     print(json.dumps(line), flush=True)
