@@ -344,3 +344,104 @@ def test_operand_offsets_beyond_4gib(pf):
     nonzero = np.zeros((M, N), bool)
     nonzero[ii, jj] = True
     assert not np.any(got[~nonzero]), "output outside the populated rows/columns is not zero"
+
+
+# ---- persistent launch: several units per work-group ---------------------------
+
+def _operands_codes(rng, M, N, K, mode):
+    """Random E4M3 codes (both signs, no NaN) and positive scales in the
+    layouts of `mode`, host and device copies."""
+    def codes(r, c):
+        q = rng.integers(0, 0xFF, (r, c), dtype=np.uint8)
+        q[(q & 0x7F) == 0x7F] = 0x7E
+        return q
+    a, b = codes(M, K), codes(N, K)
+    sa = rng.uniform(0.25, 4.0, (K // 128, M)).astype(np.float32)
+    sb_shape = {FWD: (N // 128, K // 128), DGRAD: (K // 128, N // 128), WGRAD: (K // 128, N)}[mode]
+    sb = rng.uniform(0.25, 4.0, sb_shape).astype(np.float32)
+    return a, sa, b, sb
+
+
+@pytest.mark.parametrize("mode,M,N,K,out_dtype,accumulate", [
+    (FWD, 70000, 1152, 512, torch.bfloat16, False),    # ragged M, half-inactive last column
+    (DGRAD, 70000, 1152, 512, torch.float32, False),
+    (WGRAD, 8192, 8192, 256, torch.float32, False),    # 1024 units, 4 per work-group
+    (WGRAD, 8192, 8192, 256, torch.float32, True),
+    (WGRAD, 4000, 4224, 1024, torch.bfloat16, False),  # ragged M, N % 256 == 128
+])
+def test_persistent_multi_unit(pf, mode, M, N, K, out_dtype, accumulate):
+    """More output tiles than compute units: every work-group runs several
+    units back to back (the next unit's first K-block staged during the
+    previous unit's last one, its epilogue overlapped with the next block).
+    Sampled elements, whole first / last rows and a whole column."""
+    rng = np.random.default_rng(M + N + K + mode)
+    a, sa, b, sb = _operands_codes(rng, M, N, K, mode)
+    say("persistent multi-unit", ["fwd", "dgrad", "wgrad"][mode], M, N, K, out_dtype,
+        "acc" if accumulate else "")
+    out = None
+    c0 = None
+    if accumulate:
+        c0 = rng.normal(0.0, 1.0, (M, N)).astype(np.float32)
+        out = dev(torch.from_numpy(c0))
+    c = pf.gemm_blockscaled(mode, dev(torch.from_numpy(a)), dev(torch.from_numpy(sa)),
+                            dev(torch.from_numpy(b)), dev(torch.from_numpy(sb)),
+                            out_dtype=out_dtype, out=out, accumulate=accumulate)
+    ii = rng.integers(0, M, 6000)
+    jj = rng.integers(0, N, 6000)
+    ii = np.concatenate([ii, np.zeros(N, np.int64), np.full(N, M - 1), np.arange(M)])
+    jj = np.concatenate([jj, np.arange(N), np.arange(N), np.full(M, N - 1)])
+    ref = oracle.gemm_blockscaled_at(mode, a, sa, b, sb, ii, jj)
+    bound = hw_accum.bounds(mode, a, sa, b, sb, ii, jj, ref)
+    if accumulate:
+        ref = (c0[ii, jj] + ref).astype(np.float32)
+        extra = 2.0 ** -22 * np.abs(ref)
+        bound = (bound[0] + extra, bound[1] + extra)
+    g = gemm_gates(device_values(c)[ii, jj], ref, bound, out_dtype == torch.bfloat16)
+    say("   " + fmt(g))
+    assert g["ok"], g
+
+
+# ---- streams and host threads ---------------------------------------------------
+
+def _layer_on_stream(pf, x, w, stream):
+    with torch.cuda.stream(stream):
+        qa = pf.quant_act(x, row=True)
+        qw = pf.quant_weight(w, transpose=False)
+        y = pf.gemm_blockscaled(FWD, qa["q"], qa["s"], qw["q"], qw["s"], out_dtype=torch.bfloat16)
+    return y
+
+
+def test_non_default_stream_and_host_threads(pf):
+    """Every call runs on the stream it is given (torch's current stream in
+    the binding): a layer on a side stream, and four host threads each
+    driving its own stream, reproduce the default-stream result bit for bit
+    (the library keeps no mutable global state)."""
+    import threading
+    inputs = [make_inputs(1024, 1024, 1536, 40 + i)[:2] for i in range(4)]
+    inputs = [(dev(x), dev(w)) for x, w in inputs]
+    say("streams / host threads")
+    ref = [_layer_on_stream(pf, x, w, torch.cuda.current_stream()) for x, w in inputs]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    got = _layer_on_stream(pf, inputs[0][0], inputs[0][1], side)
+    side.synchronize()
+    assert torch.equal(got.view(torch.int16), ref[0].view(torch.int16))
+    results = [None] * 4
+    errors = []
+
+    def worker(i):
+        try:
+            s = torch.cuda.Stream()
+            for _ in range(3):
+                results[i] = _layer_on_stream(pf, inputs[i][0], inputs[i][1], s)
+            s.synchronize()
+        except Exception as e:          # reported below
+            errors.append(e)
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for i in range(4):
+        assert torch.equal(results[i].view(torch.int16), ref[i].view(torch.int16)), i
