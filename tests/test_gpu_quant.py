@@ -60,7 +60,9 @@ def test_probe_encode_exhaustive_below_464(pf):
 # ---- activation quantizer ----------------------------------------------------
 
 @pytest.mark.parametrize("rows,cols", [(1, 128), (37, 256), (128, 128), (129, 384),
-                                       (300, 512), (1000, 1024), (4096, 2048)])
+                                       (300, 512), (1000, 1024), (4096, 2048),
+                                       # block rows in groups of 8: 8 + 3, and 8 + 8 + 1
+                                       (1300, 640), (2100, 1152)])
 @pytest.mark.parametrize("mode", ["row", "col", "dual"])
 def test_quant_act_small(pf, rows, cols, mode):
     x = random_bf16((rows, cols), seed=rows * 7 + cols, stream=f"act/{rows}x{cols}")
@@ -161,7 +163,7 @@ def test_quant_act_empty(pf):
 # ---- weight quantizer ----------------------------------------------------------
 
 @pytest.mark.parametrize("n,k", [(128, 128), (512, 512), (384, 256), (6144, 2048),
-                                 (16384, 2048), (2048, 8192), (2048, 2048)])
+                                 (16384, 2048), (2048, 8192), (2048, 2048), (1280, 384)])
 def test_quant_weight(pf, n, k):
     w = random_bf16((n, k), std=0.02, seed=n + k, stream=f"w/{n}x{k}")
     say("quant_weight", n, k)
