@@ -76,6 +76,21 @@ __device__ __forceinline__ int cvt2_hi(float a, float b, int old)
     return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, true);
 }
 
+// Codes of the 8 bf16 values in `v` for a tile with pre == 1, as 8 bytes:
+// the same bytes as encode8(v, 1.0f, r), since a product with 1 is exact.
+// Callers take this form when no tile in the wave has amax < 2^-64.
+__device__ __forceinline__ uint2 encode8_r(const uint4& v, float r)
+{
+    uint2 o;
+    int lo = cvt2_lo(bf16_lo(v.x) * r, bf16_hi(v.x) * r, 0);
+    lo = cvt2_hi(bf16_lo(v.y) * r, bf16_hi(v.y) * r, lo);
+    int hi = cvt2_lo(bf16_lo(v.z) * r, bf16_hi(v.z) * r, 0);
+    hi = cvt2_hi(bf16_lo(v.w) * r, bf16_hi(v.w) * r, hi);
+    o.x = (uint32_t)lo;
+    o.y = (uint32_t)hi;
+    return o;
+}
+
 // Codes of the 8 bf16 values in `v`, scaled by (pre, r), as 8 bytes.
 __device__ __forceinline__ uint2 encode8(const uint4& v, float pre, float r)
 {

@@ -102,10 +102,15 @@ __global__ __launch_bounds__(256) void quant_block_kernel(
             TileQ tq = wq;
             if constexpr (!WEIGHT)
                 tq = tile_params(dpp_row_max(mag8(v[p])));
+            uint2 codes;
+            if (__builtin_amdgcn_ballot_w64(tq.pre != 1.0f) != 0)
+                codes = encode8(v[p], tq.pre, tq.r);
+            else
+                codes = encode8_r(v[p], tq.r);
             if (r < rows) {
                 if (!WEIGHT && qd == 0)
                     s[cb * rows + r] = tq.s;
-                *reinterpret_cast<uint2*>(q + r * cols + col0) = encode8(v[p], tq.pre, tq.r);
+                *reinterpret_cast<uint2*>(q + r * cols + col0) = codes;
             }
         }
     }
@@ -160,10 +165,15 @@ __global__ __launch_bounds__(256) void quant_block_kernel(
                 const uint32_t w = (i < 2) ? v[p].x : (i < 4) ? v[p].y : (i < 6) ? v[p].z : v[p].w;
                 f[p] = (i & 1) ? bf16_hi(w) : bf16_lo(w);
             }
-            int lo = cvt2_lo((f[0] * pre) * r, (f[1] * pre) * r, 0);
-            lo = cvt2_hi((f[2] * pre) * r, (f[3] * pre) * r, lo);
-            int hi = cvt2_lo((f[4] * pre) * r, (f[5] * pre) * r, 0);
-            hi = cvt2_hi((f[6] * pre) * r, (f[7] * pre) * r, hi);
+            if (__builtin_amdgcn_ballot_w64(pre != 1.0f) != 0) {     // a tiny tile in the wave
+#pragma unroll
+                for (int p = 0; p < 8; ++p)
+                    f[p] = f[p] * pre;
+            }
+            int lo = cvt2_lo(f[0] * r, f[1] * r, 0);
+            lo = cvt2_hi(f[2] * r, f[3] * r, lo);
+            int hi = cvt2_lo(f[4] * r, f[5] * r, 0);
+            hi = cvt2_hi(f[6] * r, f[7] * r, hi);
             const int c = 8 * qd + i;
             *reinterpret_cast<uint2*>(tbuf + c * 128 + 8 * (g ^ qd)) = make_uint2((uint32_t)lo, (uint32_t)hi);
         }

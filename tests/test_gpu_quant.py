@@ -111,6 +111,38 @@ def test_quant_act_special_tiles(pf):
     _check_act(pf, x, row=True, col=True, tag="special")
 
 
+def test_quant_act_tiny_tiles_mixed_in_waves(pf):
+    """Tiles whose amax is below 2^-64 (the 2^64 rescale) beside ordinary
+    tiles within one wave, in both directions: every 7th row, one whole
+    128-column band, one 128 x 128 block, every third column of another band,
+    and zero rows.  Row-wise and column-wise codes and scales are bit-exact."""
+    rows, cols = 1024, 1024
+    x = random_bf16((rows, cols), seed=77, stream="act/tiny-mixed").float()
+    x[::7] *= 2.0 ** -80
+    x[:, 256:384] *= 2.0 ** -90
+    x[512:640, 640:768] *= 2.0 ** -100
+    x[:, 768:896:3] *= 2.0 ** -90
+    x[300:310] = 0.0
+    _check_act(pf, x.to(torch.bfloat16), row=True, col=True, tag="tiny-mixed")
+
+
+def test_quant_weight_tiny_and_zero_blocks(pf):
+    """Weight blocks with amax below 2^-64 and all-zero blocks beside
+    ordinary ones: codes, transposed codes and block scales bit-exact."""
+    n, k = 512, 768
+    w = random_bf16((n, k), std=0.02, seed=91, stream="w/tiny-blocks").float()
+    w[128:256, 256:384] *= 2.0 ** -90
+    w[0:128, 640:768] = 0.0
+    w[384:512, 0:128] *= 2.0 ** -110
+    w = w.to(torch.bfloat16)
+    out = pf.quant_weight(dev(w), transpose=True)
+    q, qt, s = oracle.quant_weight(synth.bits(w))
+    assert (s < 2.0 ** -64).sum() == 3
+    assert np.array_equal(host(out["q"]), q)
+    assert np.array_equal(host(out["qt"]), qt)
+    assert np.array_equal(host(out["s"]).view(np.uint32), s.view(np.uint32))
+
+
 def test_quant_act_exhaustive_amax_x_pairs(pf):
     """Every non-negative finite bf16 amax (32,640 values) against every bf16
     magnitude x <= amax (about 5.3e8 pairs, alternating signs): one tile per
