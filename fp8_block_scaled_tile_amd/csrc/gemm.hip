@@ -37,6 +37,7 @@ namespace puro {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -62,12 +63,12 @@ enum { OUT_BF16 = 0, OUT_FP32 = 1, OUT_FP32_ACC = 2, OUT_PARTIAL = 3 };
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
 // FWD / DGRAD read their B slice in a permuted row order (see frag_off_b)
-// and store it with a swizzle built from row bits 1, 4 and 5 instead:
-// position = c ^ (2 * ((r >> 4) & 3) + ((r >> 1) & 1)).  Within a 16-lane
+// and store it with a swizzle built from row bits 1, 3 and 4 instead:
+// position = c ^ (2 * ((r >> 3) & 3) + ((r >> 1) & 1)).  Within a 16-lane
 // fragment phase the rows of equal parity then carry 8 distinct masks, so
 // the reads stay conflict-free; any per-row XOR keeps the staging writes
 // conflict-free.
-__device__ __forceinline__ int swz_b(int row) { return (((row >> 4) & 3) << 1) | ((row >> 1) & 1); }
+__device__ __forceinline__ int swz_b(int row) { return (((row >> 3) & 3) << 1) | ((row >> 1) & 1); }
 template <int MODE>
 __device__ __forceinline__ int swz_stage_b(int row) { return MODE == 2 ? swz(row) : swz_b(row); }
 
@@ -91,15 +92,18 @@ __device__ __forceinline__ FragOff frag_off(int lane)
 }
 
 // B-side fragments of FWD / DGRAD: fragment row i of MFMA tile tn is B row
-// 16*(i>>2) + 4*tn + (i&3) of the wave's 64, so the lanes with
-// (lane >> 4) == g end up holding output columns 16*g .. 16*g+15 (4 per
-// tile, tiles side by side): 32 contiguous bytes of bf16 per row for the
-// epilogue.  The row's swizzle mask does not depend on tn, so tile tn is the
-// tn = 0 offsets plus 4*tn rows.
+// 8*(i>>2) + (i&3) + 4*(tn&1) + 32*(tn>>1) of the wave's 64, so the lanes
+// with (lane >> 4) == g hold output columns 8*g .. 8*g+7 (tiles 0, 1) and
+// 32+8*g .. 32+8*g+7 (tiles 2, 3).  One 16-byte bf16 store per lane then
+// covers 64 contiguous bytes of a row across the 4 lane groups.  The row's
+// swizzle mask does not depend on tn (it uses row bits 1, 3, 4), so tile tn
+// is the tn = 0 offsets plus b_tile_rows(tn) rows.
+__device__ __forceinline__ int b_tile_rows(int tn) { return 4 * (tn & 1) + 32 * (tn >> 1); }
+
 __device__ __forceinline__ FragOff frag_off_b(int lane)
 {
     const int i = lane & 15;
-    const int r = 16 * (i >> 2) + (i & 3);
+    const int r = 8 * (i >> 2) + (i & 3);
     const int c0 = 2 * (lane >> 4);
     return {r * BK + ((c0 ^ swz_b(r)) << 4), r * BK + (((c0 + 1) ^ swz_b(r)) << 4)};
 }
@@ -322,7 +326,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
 #pragma unroll
             for (int tn = 0; tn < TN; ++tn) {
                 __builtin_amdgcn_sched_barrier(0);
-                bf[tn] = load_frag(st.b, b_off + 4 * tn * BK, fob);
+                bf[tn] = load_frag(st.b, b_off + b_tile_rows(tn) * BK, fob);
             }
             __builtin_amdgcn_sched_barrier(0);
             const float sb_wave = st.sb[(wn * WN) / BK];
@@ -407,10 +411,11 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
                     }
                 }
         } else {
-            // lane: row m = m_lane + 16*sm; columns n_lane + 4*tn + r, i.e. 16
-            // consecutive columns (the B fragments' row order, frag_off_b)
+            // lane: row m = m_lane + 16*sm; columns n_lane + b_tile_rows(tn) + r,
+            // i.e. 8 consecutive columns from tiles 0, 1 and 8 more, 32 columns
+            // on, from tiles 2, 3 (the B fragments' row order, frag_off_b)
             const int m_lane = t.m0 + wm * WM + (lane & 15);
-            const int n_lane = t.n0 + wn * WN + 16 * (lane >> 4);
+            const int n_lane = t.n0 + wn * WN + 8 * (lane >> 4);
 #pragma unroll
             for (int sm = 0; sm < TM; ++sm) {
                 const int m = m_lane + 16 * sm;
@@ -424,13 +429,16 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
                         w[2 * tn] = pack_bf16(acc[sm][tn][0], acc[sm][tn][1]);
                         w[2 * tn + 1] = pack_bf16(acc[sm][tn][2], acc[sm][tn][3]);
                     }
-                    uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(C) + idx);
-                    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-                    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+                    // Non-temporal: the output is not read again by this
+                    // kernel, and streaming it keeps the cached A / B panels
+                    // that other work-groups re-read.
+                    v4u* dst = reinterpret_cast<v4u*>(static_cast<uint16_t*>(C) + idx);
+                    __builtin_nontemporal_store(v4u{w[0], w[1], w[2], w[3]}, dst);
+                    __builtin_nontemporal_store(v4u{w[4], w[5], w[6], w[7]}, dst + 4);
                 } else {
 #pragma unroll
                     for (int tn = 0; tn < TN; ++tn)
-                        store4(idx + 4 * tn, t.split, acc[sm][tn]);
+                        store4(idx + b_tile_rows(tn), t.split, acc[sm][tn]);
                 }
             }
         }
