@@ -365,6 +365,8 @@ def _operands_codes(rng, M, N, K, mode):
 @pytest.mark.parametrize("mode,M,N,K,out_dtype,accumulate", [
     (FWD, 70000, 1152, 512, torch.bfloat16, False),    # ragged M, half-inactive last column
     (DGRAD, 70000, 1152, 512, torch.float32, False),
+    (FWD, 70000, 1152, 128, torch.bfloat16, False),    # one K-block per unit: an epilogue every step
+    (DGRAD, 40000, 2048, 128, torch.bfloat16, False),
     (WGRAD, 8192, 8192, 256, torch.float32, False),    # 1024 units, 4 per work-group
     (WGRAD, 8192, 8192, 256, torch.float32, True),
     (WGRAD, 4000, 4224, 1024, torch.bfloat16, False),  # ragged M, N % 256 == 128
