@@ -50,7 +50,11 @@ constexpr int WN = 64;               // wave tile cols (N)
 constexpr int TM = WM / 16;          // 8 MFMA tiles along M
 constexpr int TN = WN / 16;          // 4 MFMA tiles along N
 constexpr int TILE_BYTES = BM * BK;  // 32 KB per operand slice
-constexpr int GROUP_M = 8;
+// Tiles per group along M in the unit order.  The 32 tiles that run together
+// on one XCD cover 4 M-tiles x 8 N-tiles; the 4 A panels stay in use for the
+// whole group and (at K = 2048, 512 KB each) fit in the XCD's L2 beside the
+// streamed B panels.  Measured 1-3% faster than 8 on the block GEMMs.
+constexpr int GROUP_M = 4;
 
 enum { MODE_FWD = 0, MODE_DGRAD = 1, MODE_WGRAD = 2 };
 enum { OUT_BF16 = 0, OUT_FP32 = 1, OUT_FP32_ACC = 2, OUT_PARTIAL = 3 };
