@@ -23,6 +23,11 @@ For context, the same 12 products are also timed as plain BF16 GEMMs of the
 vendor library (torch.matmul), after the FP8 timed region ("bf16_reference",
 with the FP8/BF16 step speedup).
 
+After the timed region every launch of one step is also run on its own, 50
+times, each right after a 512 MiB write that evicts the L2s and the MALL
+("kernels_cold": median, p10, p90 per launch), and a plain 1 GiB elementwise
+kernel gives the device's achievable HBM rate ("hbm_copy_reference").
+
 The CPU baseline times the plain CPU oracle (quantize + block-scaled GEMM in
 all three modes) on a bounded slice of the same workload: the first
 `--cpu-tokens` tokens of every linear layer, all host cores.
@@ -72,6 +77,10 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-bf16-reference", action="store_true",
                    help="skip the vendor BF16 GEMM comparison (context only)")
+    p.add_argument("--no-cold-stats", action="store_true",
+                   help="skip the per-launch cold-cache distribution (median / p10 / p90)")
+    p.add_argument("--cold-iters", type=int, default=50,
+                   help="cold-cache runs per launch of the step")
     p.add_argument("--ingest-pmc", nargs=4,
                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                    help="turn rocprofv3 --pmc counter CSVs (bench run, then the copy "
@@ -144,12 +153,13 @@ def check(pf, rc, what):
         raise RuntimeError(f"{what}: {pf.puro_fp8_status_string(rc)}")
 
 
-def run_step(pf, layers, stream, rec=None):
-    """Enqueue one step.  rec(name, work) returns (start_event, end_event) to
-    bracket a launch, or None to launch unbracketed."""
+def step_calls(pf, layers, stream):
+    """The launches of one step in order: (layer, class, work, fn), where work
+    is the launch's algorithmic bytes (quantizers) or FLOP (GEMMs)."""
     P = lambda t: t.data_ptr()
-    for L in layers:
-        calls = [
+
+    def layer_calls(L):     # a scope per layer: each lambda binds its own L
+        return [
             ("quant_act_dual", act_dual_bytes(L.T, L.din), lambda: pf.puro_fp8_quant_act(
                 P(L.x), L.T, L.din, P(L.qx), P(L.sx), P(L.qtx), P(L.stx), stream)),
             ("quant_weight_t", weight_t_bytes(L.dout, L.din), lambda: pf.puro_fp8_quant_weight(
@@ -166,13 +176,68 @@ def run_step(pf, layers, stream, rec=None):
                 pf.GEMM_WGRAD, L.dout, L.din, L.Tp, P(L.qtdy), P(L.stdy), P(L.qtx), P(L.stx),
                 P(L.dw), pf.OUT_FP32, 0, P(L.ws), L.ws.numel(), stream)),
         ]
-        for name, work, fn in calls:
-            ev = rec(name, work) if rec else None
-            if ev:
-                ev[0].record()
+
+    return [(L.spec.name, name, work, fn) for L in layers for name, work, fn in layer_calls(L)]
+
+
+def run_step(pf, layers, stream, rec=None):
+    """Enqueue one step.  rec(name, work) returns (start_event, end_event) to
+    bracket a launch, or None to launch unbracketed."""
+    for _, name, work, fn in step_calls(pf, layers, stream):
+        ev = rec(name, work) if rec else None
+        if ev:
+            ev[0].record()
+        check(pf, fn(), name)
+        if ev:
+            ev[1].record()
+
+
+def cold_kernel_stats(torch, pf, layers, stream, iters):
+    """Every launch of one step on its own, `iters` times, each right after a
+    512 MiB write that evicts the L2s and the MALL: median, p10 and p90 of the
+    event-timed duration per launch, and the rate at the median."""
+    import numpy as np
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    out = []
+    for layer, name, work, fn in step_calls(pf, layers, stream):
+        evs = []
+        for _ in range(iters):
+            flush.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
             check(pf, fn(), name)
-            if ev:
-                ev[1].record()
+            e1.record()
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        t = np.array([a.elapsed_time(b) for a, b in evs])
+        p10, p50, p90 = (float(v) for v in np.percentile(t, [10, 50, 90]))
+        e = {"layer": layer, "kernel": name, "median_ms": round(p50, 4), "p10_ms": round(p10, 4),
+             "p90_ms": round(p90, 4)}
+        if name.startswith("gemm"):
+            e["tflops"] = round(work / (p50 * 1e-3) / 1e12, 1)
+        else:
+            e["gbps"] = round(work / (p50 * 1e-3) / 1e9, 1)
+        out.append(e)
+    del flush
+    return out
+
+
+def hbm_copy_reference(torch):
+    """A plain elementwise kernel of known size on the same device: torch.neg
+    over 2^28 float32 (1 GiB read, 1 GiB written), best of 10."""
+    x = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+    y = torch.empty_like(x)
+    torch.neg(x, out=y)
+    best = 1e9
+    for _ in range(10):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.neg(x, out=y)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    del x, y
+    return {"kernel": "torch.neg over 2^28 float32 (1 GiB in, 1 GiB out)", "gbps": round(2 * (1 << 30) / (best * 1e-3) / 1e9, 1)}
 
 
 # ---- counters (rocprofv3 --pmc) ----------------------------------------------
@@ -372,7 +437,6 @@ def main():
         events.append((name, work, ev))
         return ev
 
-    pool = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -425,10 +489,14 @@ def main():
                 "fp8_step_speedup": round(bms / ms_per_step, 3),
                 "fp8_gemm_speedup": round(bms / gemm_ms, 3) if gemm_ms else None}
 
+    cold = None
+    copy_ref = None
+    if not args.no_cold_stats:
+        cold = cold_kernel_stats(torch, pf, layers, stream, args.cold_iters)
+        copy_ref = hbm_copy_reference(torch)
+
     cpu = None
     if host_tensors is not None:
-        for L in layers:     # free nothing on the device; the oracle runs on the host
-            pass
         cpu = cpu_baseline(specs, host_tensors, args.cpu_tokens)
 
     spec0 = specs[0]
@@ -457,6 +525,8 @@ def main():
         "kernels": kernels,
         "cpu_baseline": cpu,
         "bf16_reference": bf16,
+        "kernels_cold": cold,
+        "hbm_copy_reference": copy_ref,
         "input_generation_s": round(gen_s, 1),
     }
     print(json.dumps(line), flush=True)
