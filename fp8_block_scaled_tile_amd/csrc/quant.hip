@@ -10,7 +10,9 @@
 // One 256-thread workgroup owns a 128x128 block of the input.  Thread t
 // covers columns 8*(t%16) .. +7 and rows 8*(t/16) .. +7 of the block, so each
 // input row of the block lives in one 16-lane DPP row: the 1x128 amax is a
-// four-step DPP maximum with no LDS traffic.  Every lane issues its eight
+// four-step DPP maximum with no LDS traffic, and each of the 8 rows' scale
+// divisions is done by one lane of the DPP row and broadcast (row_newbcast)
+// to the other 15.  Every lane issues its eight
 // 16-byte loads up front; row-wise codes are stored straight from registers
 // (16 lanes write one 128-byte line); the transposed copy goes through an
 // XOR-swizzled 16 KB LDS tile and leaves as 16-byte stores.  The input is
@@ -96,22 +98,47 @@ __global__ __launch_bounds__(256) void quant_block_kernel(
 
     // ---- codes in input orientation (1x128 tiles, or the weight block) --
     if constexpr (ROW || WEIGHT) {
+        // Row tiles: every lane of a DPP row gets the 8 row maxima; lane qd
+        // computes the parameters of row qd & 7 only, lanes 0..7 store their
+        // row's scale, and r is broadcast from lane p of the DPP row.
+        int am[8];
+        float rr[8];
+        if constexpr (!WEIGHT) {
+#pragma unroll
+            for (int p = 0; p < 8; ++p)
+                am[p] = dpp_row_max(mag8(v[p]));
+            int mine = am[0];
+#pragma unroll
+            for (int p = 1; p < 8; ++p)
+                mine = ((qd & 7) == p) ? am[p] : mine;
+            const TileQ tm = tile_params(mine);
+            if (qd < 8 && row0 + qd < rows)
+                s[cb * rows + row0 + qd] = tm.s;
+            const int ri = __float_as_int(tm.r);
+            rr[0] = __int_as_float(__builtin_amdgcn_update_dpp(0, ri, 0x150, 0xF, 0xF, false));   // row_newbcast:0
+            rr[1] = __int_as_float(__builtin_amdgcn_update_dpp(0, ri, 0x151, 0xF, 0xF, false));
+            rr[2] = __int_as_float(__builtin_amdgcn_update_dpp(0, ri, 0x152, 0xF, 0xF, false));
+            rr[3] = __int_as_float(__builtin_amdgcn_update_dpp(0, ri, 0x153, 0xF, 0xF, false));
+            rr[4] = __int_as_float(__builtin_amdgcn_update_dpp(0, ri, 0x154, 0xF, 0xF, false));
+            rr[5] = __int_as_float(__builtin_amdgcn_update_dpp(0, ri, 0x155, 0xF, 0xF, false));
+            rr[6] = __int_as_float(__builtin_amdgcn_update_dpp(0, ri, 0x156, 0xF, 0xF, false));
+            rr[7] = __int_as_float(__builtin_amdgcn_update_dpp(0, ri, 0x157, 0xF, 0xF, false));
+        }
 #pragma unroll
         for (int p = 0; p < 8; ++p) {
             const int64_t r = row0 + p;
             TileQ tq = wq;
-            if constexpr (!WEIGHT)
-                tq = tile_params(dpp_row_max(mag8(v[p])));
+            if constexpr (!WEIGHT) {
+                tq.r = rr[p];
+                tq.pre = (am[p] != 0 && am[p] < 0x1F80) ? 0x1p64f : 1.0f;   // amax < 2^-64
+            }
             uint2 codes;
             if (__builtin_amdgcn_ballot_w64(tq.pre != 1.0f) != 0)
                 codes = encode8(v[p], tq.pre, tq.r);
             else
                 codes = encode8_r(v[p], tq.r);
-            if (r < rows) {
-                if (!WEIGHT && qd == 0)
-                    s[cb * rows + r] = tq.s;
+            if (r < rows)
                 *reinterpret_cast<uint2*>(q + r * cols + col0) = codes;
-            }
         }
     }
 
