@@ -13,8 +13,9 @@ Two layers:
   outputs with torch, call the entry points on the current stream, and raise
   ``PuroError`` with the library's status string on failure.
 
-Importing this package does not touch the GPU.  If the shared library is
-missing the import fails loudly; there is no fallback path.
+Importing this package does not touch the GPU or load the library.  The
+first call into the library loads it; if the shared library has not been
+built, that call raises ImportError.  There is no fallback path.
 """
 from __future__ import annotations
 
