@@ -91,8 +91,15 @@ def parse_args():
 
 
 def sha(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of a kernel source's code: comments and blank lines are dropped,
+    so editing a comment does not invalidate counters taken on the same code."""
+    import re
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = [re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines()]
+    code = "\n".join(ln for ln in lines if ln.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 # ---- per-launch algorithmic work -------------------------------------------

@@ -17,16 +17,24 @@
 //    product P_kb of a 16x16 tile comes out of a single instruction and is
 //    folded into the FP32 accumulator with one FMA per element:
 //        acc = fma(P_kb, sA*sB, acc).
-//  * The MFMA is issued with the B-side fragment as its first operand, so
-//    each lane's 4 accumulator rows are 4 consecutive n of one m: the A-side
-//    scale sA(kb, m) is one value per lane per tile, and in FWD / DGRAD sB is
+//  * FWD / DGRAD issue the MFMA with the B-side fragment as its first
+//    operand, so each lane's 4 accumulator rows are 4 consecutive n of one
+//    m: the A-side scale sA(kb, m) is one value per lane per tile, and sB is
 //    constant over the wave's 64 columns (they sit inside one 128-wide
-//    weight block).  WGRAD's sB varies per column: one extra multiply.
-//  * LDS rows are 128 bytes with the 16-byte chunk index XOR-swizzled by
-//    (row & 7); fragment reads (16 rows x 32 bytes per instruction group)
-//    and the staging writes are then bank-conflict free.
-//  * Workgroup ids are remapped so the tiles that run concurrently on one
-//    XCD form a compact 8(M) x 4(N) group sharing that XCD's L2.
+//    weight block).  WGRAD's sB varies per column; it issues the A-side
+//    fragment first and pays one extra multiply per element.
+//  * LDS rows are 128 bytes with the 16-byte chunk index XOR-swizzled per
+//    row (swz for A and WGRAD's B, swz_b for FWD / DGRAD's B); fragment
+//    reads (16 rows x 32 bytes per instruction group) and the staging
+//    writes are then bank-conflict free.
+//  * Persistent launch: one workgroup per CU walks its (split, tile) units;
+//    the next unit's first K-block is staged during the last one, and a
+//    finished unit's epilogue runs under the next block's MFMAs.  Unit ids
+//    are remapped so the 32 tiles that run together on one XCD form a
+//    compact 4(M) x 8(N) group sharing that XCD's L2.
+//  * bf16 output leaves as non-temporal stores of 64 contiguous bytes per
+//    row and instruction, so the streamed output does not evict the A / B
+//    panels that the other workgroups re-read.
 //  * Small-output problems split K across workgroups; the FP32 partials go
 //    to the caller's workspace and a second kernel sums them in a fixed
 //    order (deterministic).
