@@ -51,6 +51,7 @@ METRIC = "FP8 block-scaled GEMM TFLOP/s (fwd+dgrad+wgrad) and % of MI355X FP8 pe
 FP8_PEAK_TFLOPS = 5000.0          # MI355X dense FP8 MFMA, published
 HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_block_stack.json")
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_block_stack.json")
 GEMM_SOURCE = os.path.join(ROOT, "fp8_block_scaled_tile_amd", "csrc", "gemm.hip")
 QUANT_SOURCE = os.path.join(ROOT, "fp8_block_scaled_tile_amd", "csrc", "quant.hip")
 
@@ -85,6 +86,9 @@ def parse_args():
                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                    help="turn rocprofv3 --pmc counter CSVs (bench run, then the copy "
                         "calibration run) into the traffic file and exit")
+    p.add_argument("--ingest-mfma", metavar="MFMA_CSV",
+                   help="turn a rocprofv3 --pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_F8 GRBM_GUI_ACTIVE "
+                        "CSV of a bench run into the matrix-core file and exit")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain 1 GiB device copy (counter calibration) and exit")
     return p.parse_args()
@@ -299,11 +303,42 @@ def ingest_pmc(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     print(f"wrote {TRAFFIC_FILE}: {len(kernels)} kernels")
 
 
-def traffic_for(symbol_prefix):
-    """HBM bytes per dispatch for a kernel, or None if the counters are absent
-    or were taken on a different version of the kernel source."""
+def ingest_mfma(csv_path):
+    """Write the matrix-core file from one rocprofv3 pass with the derived
+    MfmaUtil (busy cycles of the MFMA units over GPU-active cycles x SIMDs)
+    and SQ_INSTS_VALU_MFMA_MOPS_F8 (FP8 multiply-add operations / 512): per
+    kernel, the duration-weighted MfmaUtil and the FP8 FLOP per dispatch."""
+    import csv
+    per = {}
+    with open(csv_path) as f:
+        for row in csv.DictReader(f):
+            d = per.setdefault(row["Dispatch_Id"], {"name": row["Kernel_Name"],
+                                                    "ns": int(row["End_Timestamp"]) - int(row["Start_Timestamp"])})
+            d[row["Counter_Name"]] = float(row["Counter_Value"])
+    kernels = {}
+    for d in per.values():
+        if "MfmaUtil" not in d:
+            continue
+        k = kernels.setdefault(d["name"], {"dispatches": 0, "ns": 0, "util_ns": 0.0, "f8_flop": 0.0})
+        k["dispatches"] += 1
+        k["ns"] += d["ns"]
+        k["util_ns"] += d["MfmaUtil"] * d["ns"]
+        k["f8_flop"] += d.get("SQ_INSTS_VALU_MFMA_MOPS_F8", 0.0) * 512.0
+    out = {name: {"dispatches": k["dispatches"],
+                  "mfma_util_pct": k["util_ns"] / k["ns"] if k["ns"] else 0.0,
+                  "f8_flop_per_dispatch": k["f8_flop"] / k["dispatches"]}
+           for name, k in kernels.items()}
+    doc = {"gemm_source_sha": sha(GEMM_SOURCE), "quant_source_sha": sha(QUANT_SOURCE), "kernels": out}
+    with open(MFMA_FILE, "w") as f:
+        json.dump(doc, f, indent=1, sort_keys=True)
+    print(f"wrote {MFMA_FILE}: {len(out)} kernels")
+
+
+def _profile_entry(path, symbol_prefix):
+    """The entry of a counter file for a kernel, or None if the file is absent
+    or its counters were taken on a different version of the kernel code."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             doc = json.load(f)
     except (OSError, ValueError):
         return None
@@ -313,8 +348,21 @@ def traffic_for(symbol_prefix):
         return None
     for name, v in doc.get("kernels", {}).items():
         if name.startswith(symbol_prefix):
-            return v["hbm_bytes_per_dispatch"]
+            return v
     return None
+
+
+def mfma_busy_for(symbol_prefix):
+    """Duration-weighted MfmaUtil (%) of a kernel from the counter file, or None."""
+    v = _profile_entry(MFMA_FILE, symbol_prefix)
+    return round(v["mfma_util_pct"], 2) if v else None
+
+
+def traffic_for(symbol_prefix):
+    """HBM bytes per dispatch for a kernel, or None if the counters are absent
+    or were taken on a different version of the kernel code."""
+    v = _profile_entry(TRAFFIC_FILE, symbol_prefix)
+    return v["hbm_bytes_per_dispatch"] if v else None
 
 
 # ---- BF16 comparator ------------------------------------------------------------
@@ -406,6 +454,9 @@ def main():
     if args.ingest_pmc:
         ingest_pmc(*args.ingest_pmc)
         return 0
+    if args.ingest_mfma:
+        ingest_mfma(args.ingest_mfma)
+        return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: the FP8 linear-layer path is measured on a single "
               f"MI355X (--gpus {args.gpus} is not supported; data-parallel sharding only "
@@ -482,7 +533,8 @@ def main():
     traffic = traffic_for(dk["symbol"])
     roofline = {"bound": "mfma", "achieved": dk["tflops"], "peak": FP8_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(dk["tflops"] / FP8_PEAK_TFLOPS, 4),
-                "traffic": traffic, "kernel": dk["symbol"], "launch_class": dom,
+                "traffic": traffic, "mfma_busy_pct": mfma_busy_for(dk["symbol"]),
+                "kernel": dk["symbol"], "launch_class": dom,
                 "algorithmic_gflop_per_launch": dk["avg_gflop"], "avg_ms": dk["avg_ms"]}
     gemm_ms = sum(v["ms_per_step"] for k, v in kernels.items() if k.startswith("gemm"))
     quant_ms = sum(v["ms_per_step"] for k, v in kernels.items() if k.startswith("quant"))
