@@ -44,3 +44,28 @@ def test_step_calls_bind_each_layer():
     assert seen == expect
     works = [c[2] for c in calls]
     assert works[2] == 2.0 * 256 * 384 * 128 and works[8] == 2.0 * 512 * 128 * 256
+
+
+def test_ingest_mfma_weights_by_duration_and_gates_on_code(tmp_path, monkeypatch):
+    """The matrix-core file: MfmaUtil averaged with each dispatch's duration as
+    weight, MOPS x 512 as FLOP, and the entry withheld once the kernel code
+    differs from the code the counters were taken on."""
+    name = "void puro::gemm_bs_kernel<0, 0>(unsigned char const*, int)"
+    head = "Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value,Start_Timestamp,End_Timestamp\n"
+    rows = [(1, "MfmaUtil", 40.0, 0, 100), (1, "SQ_INSTS_VALU_MFMA_MOPS_F8", 1e6, 0, 100),
+            (2, "MfmaUtil", 60.0, 1000, 1300), (2, "SQ_INSTS_VALU_MFMA_MOPS_F8", 1e6, 1000, 1300),
+            (3, "GRBM_GUI_ACTIVE", 5.0, 2000, 2010)]
+    csv_path = tmp_path / "c.csv"
+    csv_path.write_text(head + "".join(f'{d},"{name}",{c},{v},{a},{b}\n' for d, c, v, a, b in rows))
+    monkeypatch.setattr(bench, "MFMA_FILE", str(tmp_path / "m.json"))
+    bench.ingest_mfma(str(csv_path))
+    assert bench.mfma_busy_for("void puro::gemm_bs_kernel<0, 0>") == 55.0
+    entry = bench._profile_entry(bench.MFMA_FILE, "void puro::gemm_bs_kernel<0, 0>")
+    assert entry["dispatches"] == 2 and entry["f8_flop_per_dispatch"] == 512e6
+    # a comment edit keeps the entry, a code edit drops it
+    src = tmp_path / "gemm.hip"
+    src.write_text(open(bench.GEMM_SOURCE).read() + "\n// a comment\n")
+    monkeypatch.setattr(bench, "GEMM_SOURCE", str(src))
+    assert bench.mfma_busy_for("void puro::gemm_bs_kernel<0, 0>") == 55.0
+    src.write_text(open(str(src)).read() + "int changed_code;\n")
+    assert bench.mfma_busy_for("void puro::gemm_bs_kernel<0, 0>") is None
