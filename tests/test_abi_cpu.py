@@ -126,3 +126,22 @@ def test_probe_validation(lib):
     assert lib.puro_fp8_probe_encode(0, -1, P16, None) == SHAPE
     assert lib.puro_fp8_probe_encode(0, 10, None, None) == NULLP
     assert lib.puro_fp8_probe_encode(0, 0, None, None) == OK
+
+
+def test_plain_host_consumer_compiles_and_links(tmp_path):
+    """The C header is usable from a plain C++ host program: the ABI consumer
+    compiles against include/puro_fp8.h and links against the library (it is
+    run by the GPU tests)."""
+    import subprocess
+    from fp8_block_scaled_tile_amd import build as hip_build
+    import oracle
+    oracle.build(force=False)
+    src = os.path.join(ROOT, "tests", "c_abi", "abi_consumer.cpp")
+    out = str(tmp_path / "abi_consumer")
+    subprocess.run([hip_build.hipcc(), "--offload-arch=gfx950", "-O0", "-std=c++17",
+                    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                    "-I", os.path.join(ROOT, "include"), "-I", os.path.join(ROOT, "oracle"), src,
+                    "-o", out, "-L", os.path.join(ROOT, "fp8_block_scaled_tile_amd"), "-lpuro_fp8",
+                    "-L", os.path.join(ROOT, "oracle"), "-lpuro_oracle"],
+                   check=True, capture_output=True, text=True)
+    assert os.path.exists(out)
