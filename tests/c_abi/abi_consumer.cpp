@@ -4,7 +4,8 @@
 //
 // One small linear layer, X [T x K] and W [N x K] in bf16 with a ragged token
 // count: quant_act (row + transposed column codes), quant_weight (+ W^T),
-// FWD Y = X . W^T with FP32 output and WGRAD dW = dY^T . X with FP32 output.
+// FWD Y = X . W^T with FP32 output, WGRAD dW = dY^T . X with FP32 output and
+// DGRAD dX = dY . W with bf16 output, the last on a stream of its own.
 // Codes and scales must equal the CPU oracle's bit for bit; the GEMM outputs
 // must be within relative Frobenius error 1e-3 of the oracle's.  The oracle
 // (oracle/puro_oracle.h) is test infrastructure and is linked here, by a
@@ -80,6 +81,17 @@ std::vector<T> to_host(const T* d, size_t n)
     return h;
 }
 
+// bf16 value nearest to f (ties to even), as a float; f is finite
+float round_bf16(float f)
+{
+    uint32_t u;
+    std::memcpy(&u, &f, 4);
+    u = (u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u;
+    float r;
+    std::memcpy(&r, &u, 4);
+    return r;
+}
+
 double rel_fro(const std::vector<float>& got, const std::vector<float>& ref)
 {
     double num = 0.0, den = 0.0;
@@ -113,8 +125,9 @@ int main()
     float *sw = dev_alloc<float>((N / 128) * (K / 128));
     float *sdy = dev_alloc<float>((N / 128) * T), *stdy = dev_alloc<float>((Tp / 128) * N);
     float *y = dev_alloc<float>(T * N), *gw = dev_alloc<float>(N * K);
+    uint16_t* gx = dev_alloc<uint16_t>(T * K);
     if (!dx || !dw || !ddy || !qx || !qtx || !qw || !qtw || !qdy || !qtdy || !sx || !stx || !sw ||
-        !sdy || !stdy || !y || !gw) {
+        !sdy || !stdy || !y || !gw || !gx) {
         std::printf("FAIL hipMalloc\n");
         return 1;
     }
@@ -144,11 +157,19 @@ int main()
         return 1;
     if (!ok_hip(hipDeviceSynchronize(), "synchronize"))
         return 1;
+    // DGRAD on a stream of its own (its inputs are complete after the sync)
+    hipStream_t stream = nullptr;
+    if (!ok_hip(hipStreamCreate(&stream), "stream create") ||
+        !ok_puro(puro_fp8_gemm_blockscaled(PURO_GEMM_DGRAD, T, K, N, qdy, sdy, qtw, sw, gx, PURO_OUT_BF16,
+                                           0, nullptr, 0, stream), "gemm dgrad") ||
+        !ok_hip(hipStreamSynchronize(stream), "stream synchronize") ||
+        !ok_hip(hipStreamDestroy(stream), "stream destroy"))
+        return 1;
 
     // oracle
     std::vector<uint8_t> oqx(T * K), oqtx(K * Tp), oqw(N * K), oqtw(K * N), oqdy(T * N), oqtdy(N * Tp);
     std::vector<float> osx((K / 128) * T), ostx((Tp / 128) * K), osw((N / 128) * (K / 128));
-    std::vector<float> osdy((N / 128) * T), ostdy((Tp / 128) * N), oy(T * N), ogw(N * K);
+    std::vector<float> osdy((N / 128) * T), ostdy((Tp / 128) * N), oy(T * N), ogw(N * K), ogx(T * K);
     if (orc_quant_rowwise(x.data(), T, K, oqx.data(), osx.data()) ||
         orc_quant_colwise(x.data(), T, K, oqtx.data(), ostx.data()) ||
         orc_quant_weight(w.data(), N, K, oqw.data(), oqtw.data(), osw.data()) ||
@@ -157,7 +178,9 @@ int main()
         orc_gemm_blockscaled(0, T, N, K, oqx.data(), osx.data(), oqw.data(), osw.data(), oy.data(),
                              nullptr, 0, T) ||
         orc_gemm_blockscaled(2, N, K, Tp, oqtdy.data(), ostdy.data(), oqtx.data(), ostx.data(),
-                             ogw.data(), nullptr, 0, N)) {
+                             ogw.data(), nullptr, 0, N) ||
+        orc_gemm_blockscaled(1, T, K, N, oqdy.data(), osdy.data(), oqtw.data(), osw.data(),
+                             ogx.data(), nullptr, 0, T)) {
         std::printf("FAIL oracle\n");
         return 1;
     }
@@ -192,16 +215,28 @@ int main()
     }
     const double e_fwd = rel_fro(to_host(y, T * N), oy);
     const double e_wgrad = rel_fro(to_host(gw, N * K), ogw);
-    std::printf("rel_fro fwd %.3e wgrad %.3e\n", e_fwd, e_wgrad);
-    if (!(e_fwd <= 1e-3) || !(e_wgrad <= 1e-3)) {
+    std::vector<float> gx32(T * K);
+    {
+        const std::vector<uint16_t> g = to_host(gx, T * K);
+        for (size_t i = 0; i < gx32.size() && i < g.size(); ++i) {
+            const uint32_t b = (uint32_t)g[i] << 16;
+            std::memcpy(&gx32[i], &b, 4);
+        }
+    }
+    for (float& v : ogx)
+        v = round_bf16(v);            // the bf16 output is the RNE of the FP32 result
+    const double e_dgrad = rel_fro(gx32, ogx);
+    std::printf("rel_fro fwd %.3e wgrad %.3e dgrad(bf16) %.3e\n", e_fwd, e_wgrad, e_dgrad);
+    if (!(e_fwd <= 1e-3) || !(e_wgrad <= 1e-3) || !(e_dgrad <= 1e-3)) {
         std::printf("FAIL GEMM error above 1e-3\n");
         return 1;
     }
     for (void* p : {(void*)dx, (void*)dw, (void*)ddy, (void*)qx, (void*)qtx, (void*)qw, (void*)qtw,
                     (void*)qdy, (void*)qtdy, (void*)sx, (void*)stx, (void*)sw, (void*)sdy,
-                    (void*)stdy, (void*)y, (void*)gw, ws})
+                    (void*)stdy, (void*)y, (void*)gw, (void*)gx, ws})
         if (p)
             (void)hipFree(p);
-    std::printf("abi_consumer ok: 11 code/scale buffers bit-exact, FWD and WGRAD within 1e-3\n");
+    std::printf("abi_consumer ok: 11 code/scale buffers bit-exact, FWD and WGRAD (FP32) within 1e-3, "
+                "DGRAD (bf16, own stream) within 1e-3 of the oracle rounded to bf16\n");
     return 0;
 }

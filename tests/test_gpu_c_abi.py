@@ -1,8 +1,9 @@
 """The C ABI from a plain host program (tests/c_abi/abi_consumer.cpp): HIP
 runtime allocations, no Python or PyTorch in the process.  It quantizes a
-small ragged linear layer's X, W and dY, runs FWD and WGRAD with FP32 output,
-and checks codes and scales bit-exact and the GEMMs within relative Frobenius
-1e-3 against the CPU oracle."""
+small ragged linear layer's X, W and dY, runs FWD and WGRAD with FP32 output
+and DGRAD with bf16 output on a stream of its own, and checks codes and
+scales bit-exact and the GEMMs within relative Frobenius 1e-3 against the CPU
+oracle (the bf16 output against the oracle's result rounded to bf16)."""
 from __future__ import annotations
 
 import os
