@@ -22,22 +22,25 @@
 
 namespace puro {
 
-#ifndef PURO_QUANT_GROUP_ROWS
-#define PURO_QUANT_GROUP_ROWS 8
-#endif
 // Block order: the grid is 1-D and walks the 128x128 blocks in groups of
-// kGroupRows block rows, column block by column block inside a group, so
+// `group_rows` block rows, column block by column block inside a group, so
 // the work-groups in flight at any moment read a few contiguous row bands
 // and write contiguous runs of the transposed copy (a plain row-major or
 // column-major walk concentrates the reads or the transposed writes on a
-// few HBM channels when rows are 8 KB or more apart).
-constexpr int kGroupRows = PURO_QUANT_GROUP_ROWS;
+// few HBM channels when rows are 8 KB or more apart).  The group height is
+// chosen per shape by the launch code (measured on MI355X).
+static int quant_group_rows(bool weight, int64_t cols)
+{
+    if (weight)
+        return 4;
+    return cols <= 2048 ? 16 : 8;
+}
 
 template <bool ROW, bool COL, bool WEIGHT, bool WT>
 __global__ __launch_bounds__(256) void quant_block_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_t,
     uint8_t* __restrict__ q, float* __restrict__ s, uint8_t* __restrict__ qt,
-    float* __restrict__ st)
+    float* __restrict__ st, int group_rows)
 {
     constexpr bool TRANS = COL || WT;
     __shared__ int colmax[COL ? 16 : 1][COL ? 128 : 1];
@@ -51,18 +54,12 @@ __global__ __launch_bounds__(256) void quant_block_kernel(
     const int g = t >> 4;        // row group of 8 rows
     const int64_t nrb = (WEIGHT ? rows : ld_t) / 128;   // block rows
     const int64_t ncb = cols / 128;                      // block columns
-    int64_t rb, cb;
-    if (kGroupRows <= 0) {            // column blocks fastest
-        rb = blockIdx.x / ncb;
-        cb = blockIdx.x - rb * ncb;
-    } else {
-        const int64_t per_group = (int64_t)kGroupRows * ncb;
-        const int64_t group = blockIdx.x / per_group;
-        const int64_t j = blockIdx.x - group * per_group;
-        const int64_t gr = min((int64_t)kGroupRows, nrb - group * kGroupRows);
-        cb = j / gr;
-        rb = group * kGroupRows + (j - cb * gr);
-    }
+    const int64_t per_group = (int64_t)group_rows * ncb;
+    const int64_t group = blockIdx.x / per_group;
+    const int64_t j = blockIdx.x - group * per_group;
+    const int64_t gr = min((int64_t)group_rows, nrb - group * group_rows);
+    const int64_t cb = j / gr;
+    const int64_t rb = group * group_rows + (j - cb * gr);
     const int64_t row0 = rb * 128 + 8 * g;
     const int64_t col0 = cb * 128 + 8 * qd;
 
@@ -248,12 +245,13 @@ hipError_t launch_quant_act(const void* x, int64_t rows, int64_t cols, uint8_t* 
     const dim3 grid((unsigned)((rows_pad / 128) * (cols / 128)));
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     const bool row = q != nullptr, col = qt != nullptr;
+    const int gr = quant_group_rows(false, cols);
     if (row && col)
-        quant_block_kernel<true, true, false, false><<<grid, 256, 0, stream>>>(xb, rows, cols, rows_pad, q, s, qt, st);
+        quant_block_kernel<true, true, false, false><<<grid, 256, 0, stream>>>(xb, rows, cols, rows_pad, q, s, qt, st, gr);
     else if (row)
-        quant_block_kernel<true, false, false, false><<<grid, 256, 0, stream>>>(xb, rows, cols, rows_pad, q, s, qt, st);
+        quant_block_kernel<true, false, false, false><<<grid, 256, 0, stream>>>(xb, rows, cols, rows_pad, q, s, qt, st, gr);
     else
-        quant_block_kernel<false, true, false, false><<<grid, 256, 0, stream>>>(xb, rows, cols, rows_pad, q, s, qt, st);
+        quant_block_kernel<false, true, false, false><<<grid, 256, 0, stream>>>(xb, rows, cols, rows_pad, q, s, qt, st, gr);
     return hipGetLastError();
 }
 
@@ -262,10 +260,11 @@ hipError_t launch_quant_weight(const void* w, int64_t n, int64_t k, uint8_t* q, 
 {
     const dim3 grid((unsigned)((n / 128) * (k / 128)));
     const uint16_t* wb = static_cast<const uint16_t*>(w);
+    const int gr = quant_group_rows(true, k);
     if (qt)
-        quant_block_kernel<false, false, true, true><<<grid, 256, 0, stream>>>(wb, n, k, n, q, s, qt, nullptr);
+        quant_block_kernel<false, false, true, true><<<grid, 256, 0, stream>>>(wb, n, k, n, q, s, qt, nullptr, gr);
     else
-        quant_block_kernel<false, false, true, false><<<grid, 256, 0, stream>>>(wb, n, k, n, q, s, nullptr, nullptr);
+        quant_block_kernel<false, false, true, false><<<grid, 256, 0, stream>>>(wb, n, k, n, q, s, nullptr, nullptr, gr);
     return hipGetLastError();
 }
 
