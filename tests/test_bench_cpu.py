@@ -69,3 +69,31 @@ def test_ingest_mfma_weights_by_duration_and_gates_on_code(tmp_path, monkeypatch
     assert bench.mfma_busy_for("void puro::gemm_bs_kernel<0, 0>") == 55.0
     src.write_text(open(str(src)).read() + "int changed_code;\n")
     assert bench.mfma_busy_for("void puro::gemm_bs_kernel<0, 0>") is None
+
+
+def test_ingest_pmc_scales_by_the_copy_calibration(tmp_path, monkeypatch):
+    """The traffic file: per kernel, FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch, averaged over dispatches) scaled by what the same counters read
+    for the 1 GiB copy (bytes expected / bytes counted)."""
+    head = "Kernel_Name,Counter_Value\n"
+    k = "void puro::gemm_bs_kernel<0, 0>(int)"
+    neg = "void at::native::neg_kernel(float)"
+
+    def csv(name, rows):
+        path = tmp_path / name
+        path.write_text(head + "".join(f'"{n}",{v}\n' for n, v in rows))
+        return str(path)
+
+    fetch = csv("f.csv", [(k, 1000.0), (k, 3000.0)])
+    write = csv("w.csv", [(k, 500.0), (k, 500.0)])
+    copy_f = csv("cf.csv", [(neg, 524288.0)])          # half of 1 GiB counted -> factor 2
+    copy_w = csv("cw.csv", [(neg, 1048576.0)])         # all of it -> factor 1
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "t.json"))
+    bench.ingest_pmc(fetch, write, copy_f, copy_w)
+    import json
+    doc = json.load(open(bench.TRAFFIC_FILE))
+    assert doc["copy_factor_fetch"] == 2.0 and doc["copy_factor_write"] == 1.0
+    e = doc["kernels"][k]
+    assert e["dispatches"] == 2
+    assert e["hbm_bytes_per_dispatch"] == 2000.0 * 1024 * 2.0 + 500.0 * 1024 * 1.0
+    assert bench.traffic_for("void puro::gemm_bs_kernel<0, 0>") == e["hbm_bytes_per_dispatch"]
