@@ -19,9 +19,10 @@ launch inside the timed region, on the stream the kernels run on; the
 dominant kernel's achieved rate is reported against the MI355X dense FP8
 MFMA peak (5.0 PFLOP/s), the quantizers' against HBM (8 TB/s).
 
-For context, the same 12 products are also timed as plain BF16 GEMMs of the
-vendor library (torch.matmul), after the FP8 timed region ("bf16_reference",
-with the FP8/BF16 step speedup).
+For context, the same 12 products are also timed as plain BF16 GEMMs, after
+the FP8 timed region: with the vendor library (torch.matmul,
+"bf16_reference") and with this library's own tiling on the bf16 matrix
+cores ("bf16_tiled"), each with the FP8/BF16 step and GEMM speedups.
 
 After the timed region every launch of one step is also run on its own, 50
 times, each right after a 512 MiB write that evicts the L2s and the MALL
@@ -77,7 +78,7 @@ def parse_args():
                    help="token slice for the CPU-oracle baseline (0 = skip)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-bf16-reference", action="store_true",
-                   help="skip the vendor BF16 GEMM comparison (context only)")
+                   help="skip the BF16 GEMM comparisons, vendor and own tiling (context only)")
     p.add_argument("--no-cold-stats", action="store_true",
                    help="skip the per-launch cold-cache distribution (median / p10 / p90)")
     p.add_argument("--cold-iters", type=int, default=50,
@@ -399,6 +400,46 @@ def bf16_reference(torch, layers, steps):
     return ms, flops / (ms * 1e-3) / 1e12
 
 
+def bf16_tiled(torch, pf, layers, steps, stream):
+    """The same 12 products through this library's BF16 comparator GEMM
+    (puro_bf16_gemm_nt: the FP8 path's own tiling on the bf16 matrix cores,
+    no block scales), bf16 outputs, with the transposed operands materialized
+    beforehand (outside the timing).  Kernel-for-kernel context for the FP8
+    speedup, not part of the measured step."""
+    P = lambda t: t.data_ptr()
+    calls = []
+    keep = []
+    for L in layers:
+        wt, dyt, xt = L.w.t().contiguous(), L.dy.t().contiguous(), L.x.t().contiguous()
+        y, dx = torch.empty_like(L.y), torch.empty_like(L.dx)
+        dw = torch.empty((L.dout, L.din), dtype=torch.bfloat16, device="cuda:0")
+        shapes = [(L.T, L.dout, L.din, L.x, L.w, y),      # Y  = X . W^T
+                  (L.T, L.din, L.dout, L.dy, wt, dx),     # dX = dY . W   (B = W^T)
+                  (L.dout, L.din, L.T, dyt, xt, dw)]      # dW = dY^T . X (A = dY^T, B = X^T)
+        need = max(pf.puro_bf16_gemm_nt_workspace_bytes(M, N, K) for M, N, K, *_ in shapes)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda:0")
+        keep += [wt, dyt, xt, y, dx, dw, ws]
+        for M, N, K, a, b, c in shapes:
+            calls.append((M, N, K, P(a), P(b), P(c), P(ws), ws.numel()))
+
+    def step():
+        for M, N, K, a, b, c, w, wb in calls:
+            check(pf, pf.puro_bf16_gemm_nt(M, N, K, a, b, c, w, wb, stream), "bf16 comparator")
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = sum(2.0 * M * N * K for M, N, K, *_ in calls)
+    del keep
+    return ms, flops / (ms * 1e-3) / 1e12
+
+
 # ---- CPU baseline --------------------------------------------------------------
 
 def cpu_baseline(specs, host_tensors, tokens):
@@ -540,6 +581,7 @@ def main():
     quant_ms = sum(v["ms_per_step"] for k, v in kernels.items() if k.startswith("quant"))
 
     bf16 = None
+    bf16_own = None
     if not args.no_bf16_reference:
         bms, btf = bf16_reference(torch, layers, args.steps)
         bf16 = {"value": round(btf, 1), "unit": "TFLOP/s", "ms_per_step": round(bms, 4),
@@ -547,6 +589,13 @@ def main():
                         "bf16 outputs, transposed operands pre-materialized; context, not timed above",
                 "fp8_step_speedup": round(bms / ms_per_step, 3),
                 "fp8_gemm_speedup": round(bms / gemm_ms, 3) if gemm_ms else None}
+        tms, ttf = bf16_tiled(torch, pf, layers, args.steps, stream)
+        bf16_own = {"value": round(ttf, 1), "unit": "TFLOP/s", "ms_per_step": round(tms, 4),
+                    "kind": "this library's BF16 comparator GEMM (the FP8 path's tiling on bf16 "
+                            "matrix cores, no block scales), same 12 products, bf16 outputs, "
+                            "transposed operands pre-materialized; context, not timed above",
+                    "fp8_step_speedup": round(tms / ms_per_step, 3),
+                    "fp8_gemm_speedup": round(tms / gemm_ms, 3) if gemm_ms else None}
 
     cold = None
     copy_ref = None
@@ -584,6 +633,7 @@ def main():
         "kernels": kernels,
         "cpu_baseline": cpu,
         "bf16_reference": bf16,
+        "bf16_tiled": bf16_own,
         "kernels_cold": cold,
         "hbm_copy_reference": copy_ref,
         "input_generation_s": round(gen_s, 1),

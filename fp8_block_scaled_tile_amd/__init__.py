@@ -29,6 +29,7 @@ __all__ = [
     "puro_fp8_quant_act", "puro_fp8_quant_weight", "puro_fp8_gemm_blockscaled",
     "puro_fp8_gemm_workspace_bytes", "puro_fp8_status_string", "puro_fp8_abi_version",
     "puro_fp8_probe_encode", "quant_act", "quant_weight", "gemm_blockscaled",
+    "puro_bf16_gemm_nt", "puro_bf16_gemm_nt_workspace_bytes", "gemm_bf16_nt",
     "library_path",
 ]
 
@@ -77,6 +78,14 @@ def puro_fp8_abi_version() -> int:
 
 def puro_fp8_probe_encode(first_bits, n, out, stream) -> int:
     return _lib.get().puro_fp8_probe_encode(first_bits, n, out, stream)
+
+
+def puro_bf16_gemm_nt(M, N, K, a, b, c, workspace, workspace_bytes, stream) -> int:
+    return _lib.get().puro_bf16_gemm_nt(M, N, K, a, b, c, workspace, workspace_bytes, stream)
+
+
+def puro_bf16_gemm_nt_workspace_bytes(M, N, K) -> int:
+    return int(_lib.get().puro_bf16_gemm_nt_workspace_bytes(M, N, K))
 
 
 # ---- torch-facing wrappers --------------------------------------------------
@@ -188,4 +197,30 @@ def gemm_blockscaled(mode: int, a, sa, b, sb, out_dtype=None, out=None, accumula
     _check(puro_fp8_gemm_blockscaled(mode, M, N, K, _ptr(a), _ptr(sa), _ptr(b), _ptr(sb),
                                      _ptr(out), c_dtype, 1 if accumulate else 0, ws_ptr, ws_bytes,
                                      _stream(stream)))
+    return out
+
+
+def gemm_bf16_nt(a, b, out=None, workspace=None, stream=None):
+    """The BF16 comparator: bf16 C [M, N] = a [M, K] . b [N, K]^T with FP32
+    accumulation, on this library's own tiling (measurement only; not part of
+    the FP8 path).  Both operands K-contiguous bf16 CUDA tensors."""
+    torch = _torch()
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[1]:
+        raise ValueError("gemm_bf16_nt expects a [M, K] and b [N, K]")
+    M, K = a.shape
+    N = b.shape[0]
+    _need(a, torch.bfloat16, (M, K), "a")
+    _need(b, torch.bfloat16, (N, K), "b")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    else:
+        _need(out, torch.bfloat16, (M, N), "out")
+    need = puro_bf16_gemm_nt_workspace_bytes(M, N, K)
+    ws_ptr, ws_bytes = None, 0
+    if need:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=a.device)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check(puro_bf16_gemm_nt(M, N, K, _ptr(a), _ptr(b), _ptr(out), ws_ptr, ws_bytes,
+                             _stream(stream)))
     return out

@@ -14,7 +14,7 @@ _handle = None
 EXPORTS = (
     "puro_fp8_quant_act", "puro_fp8_quant_weight", "puro_fp8_gemm_blockscaled",
     "puro_fp8_gemm_workspace_bytes", "puro_fp8_status_string", "puro_fp8_abi_version",
-    "puro_fp8_probe_encode",
+    "puro_fp8_probe_encode", "puro_bf16_gemm_nt", "puro_bf16_gemm_nt_workspace_bytes",
 )
 
 
@@ -49,5 +49,9 @@ def get():
         lib.puro_fp8_abi_version.argtypes = []
         lib.puro_fp8_probe_encode.restype = I
         lib.puro_fp8_probe_encode.argtypes = [ctypes.c_uint32, I64, P, P]
+        lib.puro_bf16_gemm_nt.restype = I
+        lib.puro_bf16_gemm_nt.argtypes = [I64, I64, I64, P, P, P, P, ctypes.c_size_t, P]
+        lib.puro_bf16_gemm_nt_workspace_bytes.restype = ctypes.c_size_t
+        lib.puro_bf16_gemm_nt_workspace_bytes.argtypes = [I64, I64, I64]
         _handle = lib
         return lib

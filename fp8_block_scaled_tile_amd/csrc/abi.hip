@@ -78,6 +78,18 @@ bool gemm_shape_ok(int64_t M, int64_t N, int64_t K)
     return tiles * 8 <= kMaxDim;
 }
 
+// BF16 comparator: K counts bf16 elements (2 bytes); the kernel's K-block is
+// 128 bytes, i.e. 64 elements.
+bool bf16_shape_ok(int64_t M, int64_t N, int64_t K)
+{
+    if (M < 0 || N <= 0 || K <= 0 || N % 128 != 0 || K % 64 != 0)
+        return false;
+    if (M > kMaxDim || N > kMaxDim || 2 * K > kMaxGemmK)
+        return false;
+    const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+    return tiles * 8 <= kMaxDim;
+}
+
 }  // namespace
 
 extern "C" {
@@ -144,6 +156,37 @@ puro_status_t puro_fp8_gemm_blockscaled(puro_gemm_mode_t mode, int64_t M, int64_
         return from_hip(puro::launch_gemm((int)mode, M, N, K, a, sa, b, sb, c,
                                           c_dtype == PURO_OUT_FP32, accumulate ? 1 : 0, workspace,
                                           static_cast<hipStream_t>(stream)));
+    });
+}
+
+size_t puro_bf16_gemm_nt_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    if (!bf16_shape_ok(M, N, K) || M == 0)
+        return 0;
+    return puro::gemm_bf16_workspace_bytes(M, N, K);
+}
+
+puro_status_t puro_bf16_gemm_nt(int64_t M, int64_t N, int64_t K, const void* a, const void* b,
+                                void* c, void* workspace, size_t workspace_bytes, void* stream)
+{
+    return guarded([&]() -> puro_status_t {
+        if (!bf16_shape_ok(M, N, K))
+            return PURO_ERR_BAD_SHAPE;
+        if (M == 0)
+            return PURO_OK;
+        if (!a || !b || !c)
+            return PURO_ERR_NULL_POINTER;
+        if (!aligned16(a) || !aligned16(b) || !aligned16(c))
+            return PURO_ERR_MISALIGNED;
+        const size_t need = puro::gemm_bf16_workspace_bytes(M, N, K);
+        if (need > 0) {
+            if (!workspace || workspace_bytes < need)
+                return PURO_ERR_WORKSPACE;
+            if (!aligned16(workspace))
+                return PURO_ERR_MISALIGNED;
+        }
+        return from_hip(puro::launch_gemm_bf16_nt(M, N, K, a, b, c, workspace,
+                                                  static_cast<hipStream_t>(stream)));
     });
 }
 

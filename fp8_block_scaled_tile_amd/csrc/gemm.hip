@@ -46,6 +46,7 @@ namespace puro {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -64,7 +65,10 @@ constexpr int TILE_BYTES = BM * BK;  // 32 KB per operand slice
 // streamed B panels.  Measured 1-3% faster than 8 on the block GEMMs.
 constexpr int GROUP_M = 4;
 
-enum { MODE_FWD = 0, MODE_DGRAD = 1, MODE_WGRAD = 2 };
+// MODE_BF16 is the BF16 comparator: C = A . B^T on bf16 operands with the
+// same tiling, staging and schedule, no block scales.  K is passed in bytes
+// (2 per element), so a 128-byte K-block holds 64 bf16 values.
+enum { MODE_FWD = 0, MODE_DGRAD = 1, MODE_WGRAD = 2, MODE_BF16 = 3 };
 enum { OUT_BF16 = 0, OUT_FP32 = 1, OUT_FP32_ACC = 2, OUT_PARTIAL = 3 };
 
 // LDS rows are 128 bytes (one K-block of one row).  The 16-byte chunk c of
@@ -133,6 +137,22 @@ __device__ __forceinline__ v8i load_frag(const uint8_t* base, int off, FragOff f
     return f;
 }
 
+// BF16 operand fragment (v_mfma_f32_16x16x32_bf16): lane l holds 8 values of
+// row (l & 15), i.e. one 16-byte chunk.  A 128-byte K-block is two MFMA
+// K-steps: chunk (l >> 4) in the first and 4 + (l >> 4) in the second, with
+// the same lane mapping for A and B.  `lo` / `hi` are the two chunk offsets.
+__device__ __forceinline__ FragOff frag_off_bf16(int r, int lane, int mask)
+{
+    const int c0 = lane >> 4;
+    return {r * BK + ((c0 ^ mask) << 4), r * BK + (((c0 + 4) ^ mask) << 4)};
+}
+
+__device__ __forceinline__ v8bf load_chunk_bf16(const uint8_t* base, int off)
+{
+    const uint4 v = *reinterpret_cast<const uint4*>(&base[off]);
+    return __builtin_bit_cast(v8bf, v);
+}
+
 // One K-block (128 deep) staged in LDS: A and B code slices and their scales.
 struct Stage {
     uint8_t a[TILE_BYTES];
@@ -182,6 +202,8 @@ __device__ __forceinline__ void issue_stage(Stage& st, const uint8_t* At, const 
         __builtin_amdgcn_global_load_lds(ab + ao, (lds_void*)(st.a + (32 * wave + 8 * i) * BK), 16, 0, 0);
         __builtin_amdgcn_global_load_lds(bb + bo, (lds_void*)(st.b + (32 * wave + 8 * i) * BK), 16, 0, 0);
     }
+    if constexpr (MODE == MODE_BF16)
+        return;                                  // no block scales
     if (wave == 0) {
         const float* sab = uniform_ptr(SA + (size_t)kb * M);
 #pragma unroll
@@ -293,7 +315,54 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
     // block's first fragments individually (while an LDS-DMA copy is in
     // flight it makes every LDS-read wait a full lgkmcnt(0)).
     auto compute = [&](const Stage& st, auto&& after_row0) __attribute__((always_inline)) {
-        if constexpr (MODE == MODE_WGRAD) {
+        if constexpr (MODE == MODE_BF16) {
+            // B-first like FWD (the same store-friendly B row order); the
+            // MFMAs accumulate into acc directly.  Within a row the four tiles
+            // take K-step 0, then K-step 1, so dependent accumulations are
+            // four MFMAs apart.
+            const int ra = lane & 15;
+            const int rb = 8 * ((lane & 15) >> 2) + (lane & 3);
+            const FragOff fa = frag_off_bf16(ra, lane, swz(ra));
+            const FragOff fb = frag_off_bf16(rb, lane, swz_b(rb));
+            v8bf bf[TN][2];
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) {
+                __builtin_amdgcn_sched_barrier(0);
+                bf[tn][0] = load_chunk_bf16(st.b, b_off + b_tile_rows(tn) * BK + fb.lo);
+                bf[tn][1] = load_chunk_bf16(st.b, b_off + b_tile_rows(tn) * BK + fb.hi);
+            }
+            v8bf af0 = load_chunk_bf16(st.a, a_off + fa.lo);
+            v8bf af1 = load_chunk_bf16(st.a, a_off + fa.hi);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int sm = 0; sm < TM; ++sm) {
+                __builtin_amdgcn_sched_barrier(0);
+                v8bf an0, an1;
+                if (sm + 1 < TM) {
+                    an0 = load_chunk_bf16(st.a, a_off + 16 * (sm + 1) * BK + fa.lo);
+                    an1 = load_chunk_bf16(st.a, a_off + 16 * (sm + 1) * BK + fa.hi);
+                }
+#pragma unroll
+                for (int tn = 0; tn < TN; ++tn) {
+                    acc[sm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[tn][0], af0, acc[sm][tn], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+#pragma unroll
+                for (int tn = 0; tn < TN; ++tn) {
+                    acc[sm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[tn][1], af1, acc[sm][tn], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if (sm + 1 < TM) {
+                    af0 = an0;
+                    af1 = an1;
+                }
+                if (sm == 0) {
+                    after_row0();
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        } else if constexpr (MODE == MODE_WGRAD) {
             v8i bf[TN];
 #pragma unroll
             for (int tn = 0; tn < TN; ++tn)
@@ -403,7 +472,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
         }
     };
     auto epilogue = [&](const Unit& t) __attribute__((always_inline)) {
-        if constexpr (MODE != MODE_WGRAD)
+        if constexpr (MODE == MODE_FWD || MODE == MODE_DGRAD)
             fold_row(TM - 1, sc_carry);               // the unit's last row
         if ((t.n0 + wn * WN) >= N)
             return;
@@ -655,6 +724,22 @@ static hipError_t launch_mode(int out, const uint8_t* a, const float* sa, const 
     else
         gemm_bs_kernel<MODE, OUT_FP32_ACC><<<grid, NTHREADS, 0, stream>>>(a, sa, b, sb, c, M, N, K, tiles_m, tiles_n, 1, KB);
     return hipGetLastError();
+}
+
+size_t gemm_bf16_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    const int s = choose_splits(M, N, 2 * K);
+    return s > 1 ? (size_t)s * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
+hipError_t launch_gemm_bf16_nt(int64_t M, int64_t N, int64_t K, const void* a, const void* b,
+                               void* c, void* ws, hipStream_t stream)
+{
+    const int64_t kbytes = 2 * K;
+    const int splits = choose_splits(M, N, kbytes);
+    return launch_mode<MODE_BF16>(OUT_BF16, static_cast<const uint8_t*>(a), nullptr,
+                                  static_cast<const uint8_t*>(b), nullptr, c, ws, (int)M, (int)N,
+                                  (int)kbytes, splits, stream);
 }
 
 hipError_t launch_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* a,

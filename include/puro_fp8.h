@@ -171,6 +171,30 @@ int puro_fp8_abi_version(void);
 puro_status_t puro_fp8_probe_encode(uint32_t first_bits, int64_t n, uint8_t* out,
                                     void* stream);
 
+/*
+ * BF16 comparator (measurement only, not part of the FP8 path).
+ *
+ * The BF16 linear-layer GEMM the FP8 path replaces, on this library's own
+ * tiling, staging and schedule (bf16 matrix cores, no block scales), so the
+ * FP8 / BF16 speedup can be measured kernel for kernel:
+ *
+ *   c  bf16 [M][N]  = a . b^T, FP32 accumulation, rounded to nearest even
+ *   a  bf16 [M][K]  K-contiguous
+ *   b  bf16 [N][K]  K-contiguous (for DGRAD / WGRAD pass the transposed
+ *                   operands, as the FP8 path's transposed code copies do)
+ *
+ * Requires M >= 0, N > 0 and a multiple of 128, K > 0 and a multiple of 64,
+ * K <= 2^23; pointers 16-byte aligned.  Few output tiles with a long K split
+ * the contraction: the FP32 partials need a workspace of
+ * puro_bf16_gemm_nt_workspace_bytes(M, N, K) bytes (0 when not split).
+ * Errors and streams as for puro_fp8_gemm_blockscaled.
+ * Defined by: the BF16 matmul the FP8 path replaces (arXiv report section
+ * 2.1; blog section "FP8").
+ */
+size_t puro_bf16_gemm_nt_workspace_bytes(int64_t M, int64_t N, int64_t K);
+puro_status_t puro_bf16_gemm_nt(int64_t M, int64_t N, int64_t K, const void* a, const void* b,
+                                void* c, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -145,3 +145,21 @@ def test_plain_host_consumer_compiles_and_links(tmp_path):
                     "-L", os.path.join(ROOT, "oracle"), "-lpuro_oracle"],
                    check=True, capture_output=True, text=True)
     assert os.path.exists(out)
+
+
+def test_bf16_comparator_validation(lib):
+    f = lib.puro_bf16_gemm_nt
+    q = lib.puro_bf16_gemm_nt_workspace_bytes
+    assert f(256, 256, 100, P16, P16, P16, None, 0, None) == SHAPE     # K % 64
+    assert f(256, 200, 128, P16, P16, P16, None, 0, None) == SHAPE     # N % 128
+    assert f(-1, 256, 128, P16, P16, P16, None, 0, None) == SHAPE
+    assert f(256, 256, (1 << 23) + 64, P16, P16, P16, None, 0, None) == SHAPE   # 2K > 2^24 bytes
+    assert f(256, 256, 128, None, P16, P16, None, 0, None) == NULLP
+    assert f(256, 256, 128, P16, P16, None, None, 0, None) == NULLP
+    assert f(256, 256, 128, P16, P_ODD, P16, None, 0, None) == ALIGN
+    assert f(0, 256, 128, P16, P16, P16, None, 0, None) == OK          # empty: no-op
+    need = q(256, 256, 8192)                                            # one tile, long K: split
+    assert need > 0 and need % (256 * 256 * 4) == 0
+    assert f(256, 256, 8192, P16, P16, P16, None, 0, None) == WS
+    assert f(256, 256, 8192, P16, P16, P16, P16, need - 16, None) == WS
+    assert q(32768, 6144, 2048) == 0 and q(256, 100, 128) == 0
