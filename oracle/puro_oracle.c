@@ -498,18 +498,17 @@ int orc_matmul_ref(int64_t M, int64_t N, int64_t K,
 /* FP32 -> bf16 with round-to-nearest-even: keep the top 16 bits of the value
  * rounded at bit 16, halfway cases to the even result. */
 
-uint16_t orc_f32_to_bf16(float v)
+uint16_t orc_f64_to_bf16(double d)
 {
-    if (isnan(v))
+    if (isnan(d))
         return 0x7FC0;
-    double d = (double)v;                  /* exact */
-    if (d == 0.0 || isinf(d)) {
-        uint32_t u;
-        memcpy(&u, &v, sizeof u);
-        return (uint16_t)(u >> 16);
-    }
+    const uint16_t sign = signbit(d) ? 0x8000 : 0x0000;
+    if (d == 0.0)
+        return sign;
+    if (isinf(d))
+        return sign | 0x7F80;
     int e2;
-    const double f = frexp(fabs(d), &e2); /* |d| = f * 2^e2, f in [0.5,1) */
+    frexp(fabs(d), &e2);                  /* |d| = f * 2^e2, f in [0.5,1) */
     /* bf16 keeps 8 significant bits; below 2^-126 the spacing is fixed at
      * 2^-133 (subnormals). */
     int lsb_exp = e2 - 8;
@@ -517,12 +516,15 @@ uint16_t orc_f32_to_bf16(float v)
         lsb_exp = -133;
     const double units = rint(ldexp(fabs(d), -lsb_exp));   /* half to even */
     const double mag = ldexp(units, lsb_exp);
-    (void)f;
-    float out = (float)(d < 0 ? -mag : mag);              /* exact in fp32 */
+    const float out = (float)mag;         /* exact, or +inf past the largest bf16 */
     uint32_t u;
     memcpy(&u, &out, sizeof u);
-    if (isinf(out)) u = (u & 0x80000000u) | 0x7F800000u;
-    return (uint16_t)(u >> 16);
+    return sign | (uint16_t)(u >> 16);
+}
+
+uint16_t orc_f32_to_bf16(float v)
+{
+    return orc_f64_to_bf16((double)v);    /* exact widening */
 }
 
 typedef struct {
@@ -541,4 +543,178 @@ void orc_f32_to_bf16_array(const float* v, int64_t n, uint16_t* out)
 {
     cvt_ctx c = {v, out};
     parallel_for(n, cvt_range, &c);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Neighbour ops that produce the path's operands (quantize-on-produce).
+ *
+ * Each op is evaluated in double straight from its definition and rounded
+ * once to bf16.  The alternative result: with M the op's magnitude scale at
+ * that element, a device that evaluates the op in FP32 returns some value in
+ * [v - tol*M, v + tol*M]; rounding is monotonic, so its bf16 result is the
+ * rounding of one of the two ends.  y_alt is whichever end rounds differently
+ * from y (y itself when both round to y).  When the two ends and y are three
+ * distinct values the interval is wider than one bf16 step and the element is
+ * counted as a failure (the function returns the count). */
+
+static int64_t round_pair(double v, double band, uint16_t* y, uint16_t* y_alt)
+{
+    const uint16_t c = orc_f64_to_bf16(v);
+    *y = c;
+    *y_alt = c;
+    if (!(band > 0.0))
+        return 0;                         /* exact: one result (keeps the sign of a zero) */
+    const uint16_t lo = orc_f64_to_bf16(v - band);
+    const uint16_t hi = orc_f64_to_bf16(v + band);
+    if (lo != c && hi != c)
+        return 1;
+    *y_alt = (lo != c) ? lo : hi;
+    return 0;
+}
+
+static double bf16_to_f64(uint16_t h) { return (double)bf16_to_f32(h); }
+
+/* logistic function 1 / (1 + e^-g) */
+static double sigmoid64(double g) { return 1.0 / (1.0 + exp(-g)); }
+
+/* SwiGLU at one element, in double: h = silu(g) * u with silu(g) = g *
+ * sigmoid(g); for the upstream gradient dh,
+ *   d gate = dh * u * silu'(g),  silu'(g) = sigmoid(g) * (1 + g * (1 - sigmoid(g)))
+ *   d up   = dh * silu(g)
+ * m_gate = |dh * u * sigmoid(g)| * (1 + |g|) is the magnitude M of d gate: the
+ * sum inside silu' can cancel, and an error in sigmoid(g) enters it
+ * multiplied by g.  For h and d up, M is the magnitude of the result. */
+static void swiglu_point(double g, double u, double dh, double* h, double* dgate, double* dup,
+                         double* m_gate)
+{
+    const double sg = sigmoid64(g);
+    const double silu = g * sg;
+    *h = silu * u;
+    *dgate = dh * u * (sg * (1.0 + g * (1.0 - sg)));
+    *dup = dh * silu;
+    *m_gate = fabs(dh * u * sg) * (1.0 + fabs(g));
+}
+
+void orc_swiglu_point(double g, double u, double dh, double* out4)
+{
+    swiglu_point(g, u, dh, &out4[0], &out4[1], &out4[2], &out4[3]);
+}
+
+int64_t orc_bf16_band(double v, double band, uint16_t* out2)
+{
+    return round_pair(v, band, &out2[0], &out2[1]);
+}
+
+typedef struct {
+    const uint16_t *a, *b, *gamma;
+    int64_t rows, f, cols;
+    double tol, eps;
+    uint16_t *y, *y_alt;
+    double* rstd;
+    int64_t* fails_per_row;               /* summed after the threads join */
+} nb_ctx;
+
+/* SwiGLU forward: gate = gu[r][c], up = gu[r][f + c] -> h[r][c]. */
+static void swiglu_fwd_rows(void* p, int64_t r0, int64_t r1)
+{
+    nb_ctx* x = (nb_ctx*)p;
+    const int64_t f = x->f;
+    for (int64_t r = r0; r < r1; ++r) {
+        int64_t fails = 0;
+        for (int64_t c = 0; c < f; ++c) {
+            const double g = bf16_to_f64(x->a[r * 2 * f + c]);
+            const double u = bf16_to_f64(x->a[r * 2 * f + f + c]);
+            double h, dg, du, mg;
+            swiglu_point(g, u, 0.0, &h, &dg, &du, &mg);
+            fails += round_pair(h, x->tol * fabs(h), &x->y[r * f + c], &x->y_alt[r * f + c]);
+        }
+        x->fails_per_row[r] = fails;
+    }
+}
+
+/* SwiGLU backward: dh[r][c], gate, up -> d gate at dgu[r][c], d up at
+ * dgu[r][f + c]. */
+static void swiglu_bwd_rows(void* p, int64_t r0, int64_t r1)
+{
+    nb_ctx* x = (nb_ctx*)p;
+    const int64_t f = x->f;
+    for (int64_t r = r0; r < r1; ++r) {
+        int64_t fails = 0;
+        for (int64_t c = 0; c < f; ++c) {
+            const double dh = bf16_to_f64(x->b[r * f + c]);
+            const double g = bf16_to_f64(x->a[r * 2 * f + c]);
+            const double u = bf16_to_f64(x->a[r * 2 * f + f + c]);
+            double h, dg, du, mg;
+            swiglu_point(g, u, dh, &h, &dg, &du, &mg);
+            fails += round_pair(dg, x->tol * mg, &x->y[r * 2 * f + c], &x->y_alt[r * 2 * f + c]);
+            fails += round_pair(du, x->tol * fabs(du), &x->y[r * 2 * f + f + c],
+                                &x->y_alt[r * 2 * f + f + c]);
+        }
+        x->fails_per_row[r] = fails;
+    }
+}
+
+/* RMSNorm forward: y[r][c] = x[r][c] * rstd[r] * gamma[c] with
+ * rstd[r] = 1 / sqrt(mean over c of x[r][c]^2 + eps).  M = |y|. */
+static void rmsnorm_fwd_rows(void* p, int64_t r0, int64_t r1)
+{
+    nb_ctx* x = (nb_ctx*)p;
+    const int64_t n = x->cols;
+    for (int64_t r = r0; r < r1; ++r) {
+        double ss = 0.0;
+        for (int64_t c = 0; c < n; ++c) {
+            const double v = bf16_to_f64(x->a[r * n + c]);
+            ss += v * v;
+        }
+        const double rs = 1.0 / sqrt(ss / (double)n + x->eps);
+        if (x->rstd)
+            x->rstd[r] = rs;
+        int64_t fails = 0;
+        for (int64_t c = 0; c < n; ++c) {
+            const double y = bf16_to_f64(x->a[r * n + c]) * rs * bf16_to_f64(x->gamma[c]);
+            fails += round_pair(y, x->tol * fabs(y), &x->y[r * n + c], &x->y_alt[r * n + c]);
+        }
+        x->fails_per_row[r] = fails;
+    }
+}
+
+static int64_t run_rows(nb_ctx* c, range_fn fn)
+{
+    c->fails_per_row = (int64_t*)calloc((size_t)(c->rows > 0 ? c->rows : 1), sizeof(int64_t));
+    if (!c->fails_per_row)
+        return -1;
+    parallel_for(c->rows, fn, c);
+    int64_t total = 0;
+    for (int64_t r = 0; r < c->rows; ++r)
+        total += c->fails_per_row[r];
+    free(c->fails_per_row);
+    return total;
+}
+
+int64_t orc_swiglu_fwd(const uint16_t* gu, int64_t rows, int64_t f, double tol,
+                       uint16_t* y, uint16_t* y_alt)
+{
+    if (rows < 0 || f <= 0 || !gu || !y || !y_alt || !(tol >= 0.0))
+        return -1;
+    nb_ctx c = {.a = gu, .rows = rows, .f = f, .tol = tol, .y = y, .y_alt = y_alt};
+    return run_rows(&c, swiglu_fwd_rows);
+}
+
+int64_t orc_swiglu_bwd(const uint16_t* dh, const uint16_t* gu, int64_t rows, int64_t f,
+                       double tol, uint16_t* y, uint16_t* y_alt)
+{
+    if (rows < 0 || f <= 0 || !dh || !gu || !y || !y_alt || !(tol >= 0.0))
+        return -1;
+    nb_ctx c = {.a = gu, .b = dh, .rows = rows, .f = f, .tol = tol, .y = y, .y_alt = y_alt};
+    return run_rows(&c, swiglu_bwd_rows);
+}
+
+int64_t orc_rmsnorm_fwd(const uint16_t* x, const uint16_t* gamma, int64_t rows, int64_t cols,
+                        double eps, double tol, uint16_t* y, uint16_t* y_alt, double* rstd)
+{
+    if (rows < 0 || cols <= 0 || !x || !gamma || !y || !y_alt || !(tol >= 0.0) || !(eps >= 0.0))
+        return -1;
+    nb_ctx c = {.a = x, .gamma = gamma, .rows = rows, .cols = cols, .tol = tol, .eps = eps,
+                .y = y, .y_alt = y_alt, .rstd = rstd};
+    return run_rows(&c, rmsnorm_fwd_rows);
 }

@@ -102,7 +102,43 @@ int orc_matmul_ref(int64_t M, int64_t N, int64_t K,
 
 /* FP32 -> bf16, round to nearest even (the epilogue's output rounding). */
 uint16_t orc_f32_to_bf16(float v);
+/* Any double -> bf16, rounded once to nearest even (subnormals kept, +-inf
+ * past the largest finite bf16, NaN -> 0x7FC0). */
+uint16_t orc_f64_to_bf16(double v);
 void     orc_f32_to_bf16_array(const float* v, int64_t n, uint16_t* out);
+
+/* ---- neighbour ops that produce the path's operands ----------------------
+ * (quantize-on-produce).  The pages keep the ops around the FP8 GEMMs in
+ * BF16 ("Puro-2B" arXiv report, section 2.1; training.farm blog, FP8
+ * section): each produces a bf16 tensor, which the path quantizes exactly as
+ * orc_quant_rowwise / orc_quant_colwise do.  The pages do not define the ops;
+ * these are the standard RMSNorm and SwiGLU of a pre-norm Transformer block,
+ * with gate and up concatenated as gu[rows][2f] (gate first), the layout the
+ * fused up+gate projection produces.
+ *
+ * Each op is evaluated in double and rounded once to bf16 (y).  y_alt is the
+ * other correct bf16 result for a device that evaluates the op in FP32 with
+ * an error of at most tol * M (M: the op's magnitude at that element, stated
+ * per op in the source), else y_alt == y.  The return value is the number of
+ * elements where that band spans more than one bf16 step (0 expected), or
+ * -1 on a bad argument.
+ *   swiglu_fwd: gu [rows][2f] -> y [rows][f],  h = silu(gate) * up
+ *   swiglu_bwd: dh [rows][f], gu [rows][2f] -> y [rows][2f] = (d gate | d up)
+ *   rmsnorm_fwd: x [rows][cols], gamma [cols] -> y [rows][cols],
+ *                y = x * rstd * gamma, rstd[r] = 1/sqrt(mean(x^2) + eps)
+ *                (rstd, optional, receives rstd in double) */
+int64_t orc_swiglu_fwd(const uint16_t* gu, int64_t rows, int64_t f, double tol,
+                       uint16_t* y, uint16_t* y_alt);
+int64_t orc_swiglu_bwd(const uint16_t* dh, const uint16_t* gu, int64_t rows, int64_t f,
+                       double tol, uint16_t* y, uint16_t* y_alt);
+int64_t orc_rmsnorm_fwd(const uint16_t* x, const uint16_t* gamma, int64_t rows, int64_t cols,
+                        double eps, double tol, uint16_t* y, uint16_t* y_alt, double* rstd);
+/* The SwiGLU arithmetic above at one point, unrounded: out4 = {h, d gate,
+ * d up, M of d gate} for gate g, up u and upstream gradient dh. */
+void    orc_swiglu_point(double g, double u, double dh, double* out4);
+/* The rounding above for one value: out2 = {y, y_alt} of v with band
+ * half-width `band`; returns 1 when the band spans more than one step. */
+int64_t orc_bf16_band(double v, double band, uint16_t* out2);
 
 /* Worker threads used by the array functions (default: all online cores). */
 void orc_set_threads(int n);
