@@ -74,6 +74,8 @@ def _load():
         lib.orc_scaled_value.argtypes = [ctypes.c_float, ctypes.c_float]
         lib.orc_quant_elem.restype = ctypes.c_uint8
         lib.orc_quant_elem.argtypes = [ctypes.c_float, ctypes.c_float]
+        lib.orc_quant_elems.restype = None
+        lib.orc_quant_elems.argtypes = [P, P, I64, P]
         for name in ("orc_quant_rowwise", "orc_quant_colwise"):
             getattr(lib, name).restype = ctypes.c_int
             getattr(lib, name).argtypes = [P, I64, I64, P, P]
@@ -93,15 +95,16 @@ def _load():
         lib.orc_f32_to_bf16_array.argtypes = [P, I64, P]
         lib.orc_f64_to_bf16.restype = ctypes.c_uint16
         lib.orc_f64_to_bf16.argtypes = [ctypes.c_double]
-        lib.orc_swiglu_fwd.restype = I64
-        lib.orc_swiglu_fwd.argtypes = [P, I64, I64, ctypes.c_double, P, P]
-        lib.orc_swiglu_bwd.restype = I64
-        lib.orc_swiglu_bwd.argtypes = [P, P, I64, I64, ctypes.c_double, P, P]
-        lib.orc_rmsnorm_fwd.restype = I64
-        lib.orc_rmsnorm_fwd.argtypes = [P, P, I64, I64, ctypes.c_double, ctypes.c_double, P, P, P]
+        lib.orc_swiglu_fwd.restype = ctypes.c_int
+        lib.orc_swiglu_fwd.argtypes = [P, I64, I64, ctypes.c_double, P, P, P]
+        lib.orc_swiglu_bwd.restype = ctypes.c_int
+        lib.orc_swiglu_bwd.argtypes = [P, P, I64, I64, ctypes.c_double, P, P, P]
+        lib.orc_rmsnorm_fwd.restype = ctypes.c_int
+        lib.orc_rmsnorm_fwd.argtypes = [P, P, I64, I64, ctypes.c_double, ctypes.c_double, P, P, P,
+                                        P]
         lib.orc_swiglu_point.restype = None
         lib.orc_swiglu_point.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_double, P]
-        lib.orc_bf16_band.restype = I64
+        lib.orc_bf16_band.restype = None
         lib.orc_bf16_band.argtypes = [ctypes.c_double, ctypes.c_double, P]
         lib.orc_set_threads.restype = None
         lib.orc_set_threads.argtypes = [ctypes.c_int]
@@ -164,6 +167,15 @@ def scaled_value(x: float, amax: float) -> float:
 
 def quant_elem(x: float, amax: float) -> int:
     return int(_load().orc_quant_elem(float(x), float(amax)))
+
+
+def quant_elems(x: np.ndarray, amax: np.ndarray) -> np.ndarray:
+    """Elementwise quant_elem over float32 arrays of one shape."""
+    x = _c(np.asarray(x, np.float32), np.float32)
+    amax = _c(np.broadcast_to(np.asarray(amax, np.float32), x.shape), np.float32)
+    out = np.empty(x.shape, np.uint8)
+    _load().orc_quant_elems(_ptr(x), _ptr(amax), x.size, _ptr(out))
+    return out
 
 
 # ---- quantizers ------------------------------------------------------------
@@ -291,27 +303,19 @@ def f64_to_bf16(v: float) -> int:
 
 
 def bf16_band(v: float, band: float):
-    """(y, y_alt, wide) for one value: y its bf16 rounding, y_alt the other
-    rounding reachable within +-band (y if none), wide when the band spans
-    more than one bf16 step."""
-    out = np.empty(2, np.uint16)
-    wide = _load().orc_bf16_band(float(v), float(band), _ptr(out))
-    return int(out[0]), int(out[1]), bool(wide)
+    """(y, lo, hi) for one value: y its bf16 rounding, lo and hi the roundings
+    of v - band and v + band."""
+    out = np.empty(3, np.uint16)
+    _load().orc_bf16_band(float(v), float(band), _ptr(out))
+    return int(out[0]), int(out[1]), int(out[2])
 
 
 # ---- neighbour ops (quantize-on-produce) -------------------------------------
-# The op runs in double and is rounded once to bf16 (y); y_alt holds the other
-# bf16 result that a device evaluating the op in FP32 within tol * M may
-# return (y_alt == y where only one result is correct).  What the path then
-# quantizes is the bf16 tensor, exactly as quant_rowwise / quant_colwise do.
-
-def _band_check(fails: int, what: str):
-    if fails < 0:
-        raise ValueError(f"oracle {what}: bad arguments")
-    if fails > 0:
-        raise ValueError(f"oracle {what}: {fails} elements with a tolerance band wider "
-                         "than one bf16 step")
-
+# The op runs in double and is rounded once to bf16 (y); a device evaluating
+# it in FP32 within tol * M may return any bf16 value between lo and hi (both
+# included; lo == hi == y where only one result is correct).  What the path
+# then quantizes is the bf16 tensor, exactly as quant_rowwise / quant_colwise
+# do.
 
 def swiglu_point(g: float, u: float, dh: float = 0.0):
     """Unrounded (h, d_gate, d_up, M_gate) at one point, in double."""
@@ -320,47 +324,48 @@ def swiglu_point(g: float, u: float, dh: float = 0.0):
     return tuple(float(v) for v in out)
 
 
+def _three(shape):
+    return tuple(np.empty(shape, np.uint16) for _ in range(3))
+
+
 def swiglu_fwd(gu_bits: np.ndarray, tol: float):
-    """gu: uint16 [rows, 2f] (gate | up) -> (y, y_alt) uint16 [rows, f]."""
+    """gu: uint16 [rows, 2f] (gate | up) -> (y, lo, hi) uint16 [rows, f]."""
     gu = _c(gu_bits, np.uint16)
     rows, f2 = gu.shape
     f = f2 // 2
-    y = np.empty((rows, f), np.uint16)
-    y_alt = np.empty((rows, f), np.uint16)
-    _band_check(_load().orc_swiglu_fwd(_ptr(gu), rows, f, float(tol), _ptr(y), _ptr(y_alt)),
-                "swiglu_fwd")
-    return y, y_alt
+    y, lo, hi = _three((rows, f))
+    _check(_load().orc_swiglu_fwd(_ptr(gu), rows, f, float(tol), _ptr(y), _ptr(lo), _ptr(hi)),
+           "swiglu_fwd")
+    return y, lo, hi
 
 
 def swiglu_bwd(dh_bits: np.ndarray, gu_bits: np.ndarray, tol: float):
-    """dh: uint16 [rows, f], gu: uint16 [rows, 2f] -> (y, y_alt) uint16
+    """dh: uint16 [rows, f], gu: uint16 [rows, 2f] -> (y, lo, hi) uint16
     [rows, 2f] holding (d gate | d up)."""
     dh = _c(dh_bits, np.uint16)
     gu = _c(gu_bits, np.uint16)
     rows, f = dh.shape
     if gu.shape != (rows, 2 * f):
         raise ValueError("gu must be [rows, 2f]")
-    y = np.empty((rows, 2 * f), np.uint16)
-    y_alt = np.empty((rows, 2 * f), np.uint16)
-    _band_check(_load().orc_swiglu_bwd(_ptr(dh), _ptr(gu), rows, f, float(tol), _ptr(y),
-                                       _ptr(y_alt)), "swiglu_bwd")
-    return y, y_alt
+    y, lo, hi = _three((rows, 2 * f))
+    _check(_load().orc_swiglu_bwd(_ptr(dh), _ptr(gu), rows, f, float(tol), _ptr(y), _ptr(lo),
+                                  _ptr(hi)), "swiglu_bwd")
+    return y, lo, hi
 
 
 def rmsnorm_fwd(x_bits: np.ndarray, gamma_bits: np.ndarray, eps: float, tol: float):
-    """x: uint16 [rows, cols], gamma: uint16 [cols] -> (y, y_alt, rstd) with
+    """x: uint16 [rows, cols], gamma: uint16 [cols] -> (y, lo, hi, rstd) with
     rstd float64 [rows]."""
     x = _c(x_bits, np.uint16)
     gamma = _c(gamma_bits, np.uint16)
     rows, cols = x.shape
     if gamma.shape != (cols,):
         raise ValueError("gamma must be [cols]")
-    y = np.empty((rows, cols), np.uint16)
-    y_alt = np.empty((rows, cols), np.uint16)
+    y, lo, hi = _three((rows, cols))
     rstd = np.empty(rows, np.float64)
-    _band_check(_load().orc_rmsnorm_fwd(_ptr(x), _ptr(gamma), rows, cols, float(eps), float(tol),
-                                        _ptr(y), _ptr(y_alt), _ptr(rstd)), "rmsnorm_fwd")
-    return y, y_alt, rstd
+    _check(_load().orc_rmsnorm_fwd(_ptr(x), _ptr(gamma), rows, cols, float(eps), float(tol),
+                                   _ptr(y), _ptr(lo), _ptr(hi), _ptr(rstd)), "rmsnorm_fwd")
+    return y, lo, hi, rstd
 
 
 def set_threads(n: int) -> None:

@@ -103,6 +103,12 @@ uint8_t orc_quant_elem(float x, float amax)
     return orc_e4m3_encode(orc_scaled_value(x, amax));
 }
 
+void orc_quant_elems(const float* x, const float* amax, int64_t n, uint8_t* out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = orc_quant_elem(x[i], amax[i]);
+}
+
 /* ------------------------------------------------------------------------ */
 /* A tiny parallel-for over [0, n). */
 
@@ -549,27 +555,22 @@ void orc_f32_to_bf16_array(const float* v, int64_t n, uint16_t* out)
 /* Neighbour ops that produce the path's operands (quantize-on-produce).
  *
  * Each op is evaluated in double straight from its definition and rounded
- * once to bf16.  The alternative result: with M the op's magnitude scale at
- * that element, a device that evaluates the op in FP32 returns some value in
- * [v - tol*M, v + tol*M]; rounding is monotonic, so its bf16 result is the
- * rounding of one of the two ends.  y_alt is whichever end rounds differently
- * from y (y itself when both round to y).  When the two ends and y are three
- * distinct values the interval is wider than one bf16 step and the element is
- * counted as a failure (the function returns the count). */
+ * once to bf16 (y).  The band: with M the op's magnitude scale at that
+ * element, a device that evaluates the op in FP32 returns some value in
+ * [v - tol*M, v + tol*M]; rounding is monotonic, so its bf16 result lies
+ * between the roundings of the two ends (lo, hi), both included.  lo == hi
+ * (== y) marks an element with one correct result. */
 
-static int64_t round_pair(double v, double band, uint16_t* y, uint16_t* y_alt)
+static void round_band(double v, double band, uint16_t* y, uint16_t* lo, uint16_t* hi)
 {
-    const uint16_t c = orc_f64_to_bf16(v);
-    *y = c;
-    *y_alt = c;
-    if (!(band > 0.0))
-        return 0;                         /* exact: one result (keeps the sign of a zero) */
-    const uint16_t lo = orc_f64_to_bf16(v - band);
-    const uint16_t hi = orc_f64_to_bf16(v + band);
-    if (lo != c && hi != c)
-        return 1;
-    *y_alt = (lo != c) ? lo : hi;
-    return 0;
+    *y = orc_f64_to_bf16(v);
+    if (!(band > 0.0)) {
+        *lo = *y;                         /* exact: one result (keeps the sign of a zero) */
+        *hi = *y;
+        return;
+    }
+    *lo = orc_f64_to_bf16(v - band);
+    *hi = orc_f64_to_bf16(v + band);
 }
 
 static double bf16_to_f64(uint16_t h) { return (double)bf16_to_f32(h); }
@@ -600,18 +601,17 @@ void orc_swiglu_point(double g, double u, double dh, double* out4)
     swiglu_point(g, u, dh, &out4[0], &out4[1], &out4[2], &out4[3]);
 }
 
-int64_t orc_bf16_band(double v, double band, uint16_t* out2)
+void orc_bf16_band(double v, double band, uint16_t* out3)
 {
-    return round_pair(v, band, &out2[0], &out2[1]);
+    round_band(v, band, &out3[0], &out3[1], &out3[2]);
 }
 
 typedef struct {
     const uint16_t *a, *b, *gamma;
     int64_t rows, f, cols;
     double tol, eps;
-    uint16_t *y, *y_alt;
+    uint16_t *y, *lo, *hi;
     double* rstd;
-    int64_t* fails_per_row;               /* summed after the threads join */
 } nb_ctx;
 
 /* SwiGLU forward: gate = gu[r][c], up = gu[r][f + c] -> h[r][c]. */
@@ -620,15 +620,14 @@ static void swiglu_fwd_rows(void* p, int64_t r0, int64_t r1)
     nb_ctx* x = (nb_ctx*)p;
     const int64_t f = x->f;
     for (int64_t r = r0; r < r1; ++r) {
-        int64_t fails = 0;
         for (int64_t c = 0; c < f; ++c) {
             const double g = bf16_to_f64(x->a[r * 2 * f + c]);
             const double u = bf16_to_f64(x->a[r * 2 * f + f + c]);
             double h, dg, du, mg;
             swiglu_point(g, u, 0.0, &h, &dg, &du, &mg);
-            fails += round_pair(h, x->tol * fabs(h), &x->y[r * f + c], &x->y_alt[r * f + c]);
+            const int64_t i = r * f + c;
+            round_band(h, x->tol * fabs(h), &x->y[i], &x->lo[i], &x->hi[i]);
         }
-        x->fails_per_row[r] = fails;
     }
 }
 
@@ -639,18 +638,16 @@ static void swiglu_bwd_rows(void* p, int64_t r0, int64_t r1)
     nb_ctx* x = (nb_ctx*)p;
     const int64_t f = x->f;
     for (int64_t r = r0; r < r1; ++r) {
-        int64_t fails = 0;
         for (int64_t c = 0; c < f; ++c) {
             const double dh = bf16_to_f64(x->b[r * f + c]);
             const double g = bf16_to_f64(x->a[r * 2 * f + c]);
             const double u = bf16_to_f64(x->a[r * 2 * f + f + c]);
             double h, dg, du, mg;
             swiglu_point(g, u, dh, &h, &dg, &du, &mg);
-            fails += round_pair(dg, x->tol * mg, &x->y[r * 2 * f + c], &x->y_alt[r * 2 * f + c]);
-            fails += round_pair(du, x->tol * fabs(du), &x->y[r * 2 * f + f + c],
-                                &x->y_alt[r * 2 * f + f + c]);
+            const int64_t ig = r * 2 * f + c, iu = r * 2 * f + f + c;
+            round_band(dg, x->tol * mg, &x->y[ig], &x->lo[ig], &x->hi[ig]);
+            round_band(du, x->tol * fabs(du), &x->y[iu], &x->lo[iu], &x->hi[iu]);
         }
-        x->fails_per_row[r] = fails;
     }
 }
 
@@ -669,52 +666,41 @@ static void rmsnorm_fwd_rows(void* p, int64_t r0, int64_t r1)
         const double rs = 1.0 / sqrt(ss / (double)n + x->eps);
         if (x->rstd)
             x->rstd[r] = rs;
-        int64_t fails = 0;
         for (int64_t c = 0; c < n; ++c) {
             const double y = bf16_to_f64(x->a[r * n + c]) * rs * bf16_to_f64(x->gamma[c]);
-            fails += round_pair(y, x->tol * fabs(y), &x->y[r * n + c], &x->y_alt[r * n + c]);
+            round_band(y, x->tol * fabs(y), &x->y[r * n + c], &x->lo[r * n + c], &x->hi[r * n + c]);
         }
-        x->fails_per_row[r] = fails;
     }
 }
 
-static int64_t run_rows(nb_ctx* c, range_fn fn)
+int orc_swiglu_fwd(const uint16_t* gu, int64_t rows, int64_t f, double tol, uint16_t* y,
+                   uint16_t* lo, uint16_t* hi)
 {
-    c->fails_per_row = (int64_t*)calloc((size_t)(c->rows > 0 ? c->rows : 1), sizeof(int64_t));
-    if (!c->fails_per_row)
+    if (rows < 0 || f <= 0 || !gu || !y || !lo || !hi || !(tol >= 0.0))
         return -1;
-    parallel_for(c->rows, fn, c);
-    int64_t total = 0;
-    for (int64_t r = 0; r < c->rows; ++r)
-        total += c->fails_per_row[r];
-    free(c->fails_per_row);
-    return total;
+    nb_ctx c = {.a = gu, .rows = rows, .f = f, .tol = tol, .y = y, .lo = lo, .hi = hi};
+    parallel_for(rows, swiglu_fwd_rows, &c);
+    return 0;
 }
 
-int64_t orc_swiglu_fwd(const uint16_t* gu, int64_t rows, int64_t f, double tol,
-                       uint16_t* y, uint16_t* y_alt)
+int orc_swiglu_bwd(const uint16_t* dh, const uint16_t* gu, int64_t rows, int64_t f, double tol,
+                   uint16_t* y, uint16_t* lo, uint16_t* hi)
 {
-    if (rows < 0 || f <= 0 || !gu || !y || !y_alt || !(tol >= 0.0))
+    if (rows < 0 || f <= 0 || !dh || !gu || !y || !lo || !hi || !(tol >= 0.0))
         return -1;
-    nb_ctx c = {.a = gu, .rows = rows, .f = f, .tol = tol, .y = y, .y_alt = y_alt};
-    return run_rows(&c, swiglu_fwd_rows);
+    nb_ctx c = {.a = gu, .b = dh, .rows = rows, .f = f, .tol = tol, .y = y, .lo = lo, .hi = hi};
+    parallel_for(rows, swiglu_bwd_rows, &c);
+    return 0;
 }
 
-int64_t orc_swiglu_bwd(const uint16_t* dh, const uint16_t* gu, int64_t rows, int64_t f,
-                       double tol, uint16_t* y, uint16_t* y_alt)
+int orc_rmsnorm_fwd(const uint16_t* x, const uint16_t* gamma, int64_t rows, int64_t cols,
+                    double eps, double tol, uint16_t* y, uint16_t* lo, uint16_t* hi, double* rstd)
 {
-    if (rows < 0 || f <= 0 || !dh || !gu || !y || !y_alt || !(tol >= 0.0))
-        return -1;
-    nb_ctx c = {.a = gu, .b = dh, .rows = rows, .f = f, .tol = tol, .y = y, .y_alt = y_alt};
-    return run_rows(&c, swiglu_bwd_rows);
-}
-
-int64_t orc_rmsnorm_fwd(const uint16_t* x, const uint16_t* gamma, int64_t rows, int64_t cols,
-                        double eps, double tol, uint16_t* y, uint16_t* y_alt, double* rstd)
-{
-    if (rows < 0 || cols <= 0 || !x || !gamma || !y || !y_alt || !(tol >= 0.0) || !(eps >= 0.0))
+    if (rows < 0 || cols <= 0 || !x || !gamma || !y || !lo || !hi || !(tol >= 0.0) ||
+        !(eps >= 0.0))
         return -1;
     nb_ctx c = {.a = x, .gamma = gamma, .rows = rows, .cols = cols, .tol = tol, .eps = eps,
-                .y = y, .y_alt = y_alt, .rstd = rstd};
-    return run_rows(&c, rmsnorm_fwd_rows);
+                .y = y, .lo = lo, .hi = hi, .rstd = rstd};
+    parallel_for(rows, rmsnorm_fwd_rows, &c);
+    return 0;
 }

@@ -51,6 +51,8 @@ void    orc_e4m3_encode_range(uint32_t first_bits, int64_t n, uint8_t* out);
 float   orc_tile_scale(float amax);
 float   orc_scaled_value(float x, float amax);
 uint8_t orc_quant_elem(float x, float amax);  /* E(scaled value) */
+/* out[i] = orc_quant_elem(x[i], amax[i]) for i < n */
+void    orc_quant_elems(const float* x, const float* amax, int64_t n, uint8_t* out);
 
 /* ---- quantizers (bf16 inputs as raw uint16 bit patterns) ----------------
  * row-wise, 1x128 tiles along cols:   q[rows][cols], s[cols/128][rows]
@@ -116,29 +118,30 @@ void     orc_f32_to_bf16_array(const float* v, int64_t n, uint16_t* out);
  * with gate and up concatenated as gu[rows][2f] (gate first), the layout the
  * fused up+gate projection produces.
  *
- * Each op is evaluated in double and rounded once to bf16 (y).  y_alt is the
- * other correct bf16 result for a device that evaluates the op in FP32 with
- * an error of at most tol * M (M: the op's magnitude at that element, stated
- * per op in the source), else y_alt == y.  The return value is the number of
- * elements where that band spans more than one bf16 step (0 expected), or
+ * Each op is evaluated in double and rounded once to bf16 (y).  A device
+ * that evaluates the op in FP32 with an error of at most tol * M (M: the op's
+ * magnitude at that element, stated per op in the source) returns a bf16
+ * value between lo and hi, both included: the roundings of the two ends of
+ * that band.  lo == hi (== y) where only one result is correct.  Return 0, or
  * -1 on a bad argument.
- *   swiglu_fwd: gu [rows][2f] -> y [rows][f],  h = silu(gate) * up
- *   swiglu_bwd: dh [rows][f], gu [rows][2f] -> y [rows][2f] = (d gate | d up)
- *   rmsnorm_fwd: x [rows][cols], gamma [cols] -> y [rows][cols],
+ *   swiglu_fwd: gu [rows][2f] -> [rows][f],  h = silu(gate) * up
+ *   swiglu_bwd: dh [rows][f], gu [rows][2f] -> [rows][2f] = (d gate | d up)
+ *   rmsnorm_fwd: x [rows][cols], gamma [cols] -> [rows][cols],
  *                y = x * rstd * gamma, rstd[r] = 1/sqrt(mean(x^2) + eps)
  *                (rstd, optional, receives rstd in double) */
-int64_t orc_swiglu_fwd(const uint16_t* gu, int64_t rows, int64_t f, double tol,
-                       uint16_t* y, uint16_t* y_alt);
-int64_t orc_swiglu_bwd(const uint16_t* dh, const uint16_t* gu, int64_t rows, int64_t f,
-                       double tol, uint16_t* y, uint16_t* y_alt);
-int64_t orc_rmsnorm_fwd(const uint16_t* x, const uint16_t* gamma, int64_t rows, int64_t cols,
-                        double eps, double tol, uint16_t* y, uint16_t* y_alt, double* rstd);
+int orc_swiglu_fwd(const uint16_t* gu, int64_t rows, int64_t f, double tol, uint16_t* y,
+                   uint16_t* lo, uint16_t* hi);
+int orc_swiglu_bwd(const uint16_t* dh, const uint16_t* gu, int64_t rows, int64_t f, double tol,
+                   uint16_t* y, uint16_t* lo, uint16_t* hi);
+int orc_rmsnorm_fwd(const uint16_t* x, const uint16_t* gamma, int64_t rows, int64_t cols,
+                    double eps, double tol, uint16_t* y, uint16_t* lo, uint16_t* hi,
+                    double* rstd);
 /* The SwiGLU arithmetic above at one point, unrounded: out4 = {h, d gate,
  * d up, M of d gate} for gate g, up u and upstream gradient dh. */
-void    orc_swiglu_point(double g, double u, double dh, double* out4);
-/* The rounding above for one value: out2 = {y, y_alt} of v with band
- * half-width `band`; returns 1 when the band spans more than one step. */
-int64_t orc_bf16_band(double v, double band, uint16_t* out2);
+void orc_swiglu_point(double g, double u, double dh, double* out4);
+/* The rounding above for one value: out3 = {y, lo, hi} of v with band
+ * half-width `band`. */
+void orc_bf16_band(double v, double band, uint16_t* out3);
 
 /* Worker threads used by the array functions (default: all online cores). */
 void orc_set_threads(int n);

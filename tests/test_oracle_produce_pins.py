@@ -80,18 +80,17 @@ def test_f64_to_bf16_range_ends(orc):
     assert orc.f64_to_bf16(-0.0) == 0x8000
 
 
-def test_band_alternatives(orc):
-    """The alternative result is the rounding reachable within the band."""
+def test_band_ends(orc):
+    """(y, lo, hi): the rounding of v and of the two ends of the band."""
     mid = 1.0 + 2.0**-8                                          # between 0x3F80 and 0x3F81
-    assert orc.bf16_band(mid, 1e-10) == (0x3F80, 0x3F81, False)
-    assert orc.bf16_band(mid + 2e-10, 1e-10) == (0x3F81, 0x3F81, False)
-    assert orc.bf16_band(mid + 2e-10, 3e-10) == (0x3F81, 0x3F80, False)
-    assert orc.bf16_band(1.0, 1e-6) == (0x3F80, 0x3F80, False)
-    assert orc.bf16_band(-mid, 1e-10) == (0xBF80, 0xBF81, False)
-    y, alt, wide = orc.bf16_band(0.0, 1e-3)                      # -1e-3 .. 1e-3: three results
-    assert wide
-    y, alt, wide = orc.bf16_band(1e-45, 1e-44)                   # straddles zero: +0 or -0
-    assert (y, alt, wide) == (0x0000, 0x8000, False)
+    assert orc.bf16_band(mid, 1e-10) == (0x3F80, 0x3F80, 0x3F81)
+    assert orc.bf16_band(mid + 2e-10, 1e-10) == (0x3F81, 0x3F81, 0x3F81)
+    assert orc.bf16_band(mid + 2e-10, 3e-10) == (0x3F81, 0x3F80, 0x3F81)
+    assert orc.bf16_band(1.0, 1e-6) == (0x3F80, 0x3F80, 0x3F80)
+    assert orc.bf16_band(-mid, 1e-10) == (0xBF80, 0xBF81, 0xBF80)  # lo is the more negative
+    assert orc.bf16_band(1.0, 2.0**-6) == (0x3F80, 0x3F7C, 0x3F82)  # several steps wide
+    assert orc.bf16_band(1e-45, 1e-44) == (0x0000, 0x8000, 0x0000)  # straddles zero
+    assert orc.bf16_band(-0.0, 0.0) == (0x8000, 0x8000, 0x8000)    # exact: keeps the sign
 
 
 # ---- SwiGLU ------------------------------------------------------------------
@@ -99,16 +98,16 @@ def test_band_alternatives(orc):
 def test_swiglu_fwd_golden(orc):
     rows = _golden("swiglu")
     gu = np.array([[g, u] for g, u, _ in rows], np.uint16)       # f = 1: gate | up
-    y, y_alt = orc.swiglu_fwd(gu, tol=2.0**-18)
+    y, lo, hi = orc.swiglu_fwd(gu, tol=2.0**-18)
     assert [int(v) for v in y[:, 0]] == [want for _, _, want in rows]
-    assert np.array_equal(y, y_alt)                              # none lies near a tie
+    assert np.array_equal(lo, y) and np.array_equal(hi, y)       # none lies near a tie
 
 
 def test_swiglu_gate_up_layout(orc):
     """With f = 2 the gate of column c is gu[:, c] and its up is gu[:, 2 + c]."""
     gu = np.array([[0x3F80, 0x4000, 0x3F80, 0x3F80],             # gates (1, 2), ups (1, 1)
                    [0x3F80, 0x3F80, 0x4000, 0x3F80]], np.uint16)  # gates (1, 1), ups (2, 1)
-    y, _ = orc.swiglu_fwd(gu, tol=0.0)
+    y, _, _ = orc.swiglu_fwd(gu, tol=0.0)
     assert y.tolist() == [[0x3F3B, 0x3FE1], [0x3FBB, 0x3F3B]]
 
 
@@ -147,9 +146,10 @@ def test_swiglu_bwd_layout_and_rounding(orc):
     f, rows = 3, 5
     gu = _to_bf16_torch(rng.standard_normal((rows, 2 * f)) * 2.0)
     dh = _to_bf16_torch(rng.standard_normal((rows, f)))
-    y, y_alt = orc.swiglu_bwd(dh, gu, tol=0.0)
-    assert np.array_equal(y, y_alt)
-    wid = lambda b: float(np.array([b], np.uint16).astype(np.uint32).__lshift__(16).view(np.float32)[0])
+    y, lo, hi = orc.swiglu_bwd(dh, gu, tol=0.0)
+    assert np.array_equal(y, lo) and np.array_equal(y, hi)
+    def wid(b):
+        return float(orc.bf16_bits_to_f32(np.array([b], np.uint16))[0])
     for r in range(rows):
         for c in range(f):
             _, dg, du, _ = orc.swiglu_point(wid(gu[r, c]), wid(gu[r, f + c]), wid(dh[r, c]))
@@ -161,7 +161,7 @@ def test_swiglu_bwd_layout_and_rounding(orc):
 
 def test_rmsnorm_golden(orc):
     (x0, x1, g0, g1, y0, y1), = _golden("rmsnorm")
-    y, y_alt, rstd = orc.rmsnorm_fwd(np.array([[x0, x1]], np.uint16),
+    y, _, _, rstd = orc.rmsnorm_fwd(np.array([[x0, x1]], np.uint16),
                                      np.array([g0, g1], np.uint16), eps=0.0, tol=2.0**-18)
     assert y.tolist() == [[y0, y1]]
     assert abs(rstd[0] - math.sqrt(2.0) / 5.0) < 1e-16
@@ -174,10 +174,10 @@ def test_rmsnorm_constant_magnitude_rows(orc):
     gamma = _to_bf16_torch(rng.standard_normal(cols))
     signs = np.where(rng.standard_normal((4, cols)) < 0, -1.0, 1.0)
     x = _to_bf16_torch(signs * np.array([[0.375], [3.0], [2.0**-20], [96.0]]))
-    y, y_alt, rstd = orc.rmsnorm_fwd(x, gamma, eps=0.0, tol=2.0**-18)
+    y, lo, hi, rstd = orc.rmsnorm_fwd(x, gamma, eps=0.0, tol=2.0**-18)
     want = _to_bf16_torch(signs * (gamma.astype(np.uint32) << 16).view(np.float32))
     assert np.array_equal(y, want)
-    assert np.array_equal(y, y_alt)
+    assert np.array_equal(y, lo) and np.array_equal(y, hi)
     assert np.allclose(rstd, 1.0 / np.array([0.375, 3.0, 2.0**-20, 96.0]), rtol=1e-15)
 
 
@@ -190,9 +190,9 @@ def test_rmsnorm_scaling_identities(orc):
     x8 = _to_bf16_torch(xf * 8.0)
     gamma = _to_bf16_torch(rng.standard_normal(cols))
     gamma2 = _to_bf16_torch((gamma.astype(np.uint32) << 16).view(np.float32) * 2.0)
-    y, _, rs = orc.rmsnorm_fwd(x, gamma, eps=0.0, tol=0.0)
-    y8, _, rs8 = orc.rmsnorm_fwd(x8, gamma, eps=0.0, tol=0.0)
-    y2, _, _ = orc.rmsnorm_fwd(x, gamma2, eps=0.0, tol=0.0)
+    y, _, _, rs = orc.rmsnorm_fwd(x, gamma, eps=0.0, tol=0.0)
+    y8, _, _, rs8 = orc.rmsnorm_fwd(x8, gamma, eps=0.0, tol=0.0)
+    y2, _, _, _ = orc.rmsnorm_fwd(x, gamma2, eps=0.0, tol=0.0)
     assert np.array_equal(y, y8)
     assert np.array_equal(rs, rs8 * 8.0)
     nz = (y & 0x7FFF) != 0
@@ -204,6 +204,6 @@ def test_rmsnorm_eps(orc):
     x = np.zeros((1, 128), np.uint16)
     x[0, 1] = 0x8000                                             # -0
     gamma = np.full(128, 0x3F80, np.uint16)
-    y, _, rstd = orc.rmsnorm_fwd(x, gamma, eps=2.0**-20, tol=2.0**-18)
+    y, _, _, rstd = orc.rmsnorm_fwd(x, gamma, eps=2.0**-20, tol=2.0**-18)
     assert rstd[0] == 1024.0
     assert y[0, 0] == 0x0000 and y[0, 1] == 0x8000
