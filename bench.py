@@ -24,6 +24,12 @@ the FP8 timed region: with the vendor library (torch.matmul,
 "bf16_reference") and with this library's own tiling on the bf16 matrix
 cores ("bf16_tiled"), each with the FP8/BF16 step and GEMM speedups.
 
+Quantize-on-produce ("produce"): the BF16 neighbour ops of one block at the
+same token count (RMSNorm x2 before QKV and up/gate, SwiGLU forward before
+down, SwiGLU backward after down's DGRAD), each writing FP8 operands straight
+from the op, timed against the unfused pair (the op writing bf16, then
+quant_act on it).  Not part of the step above, whose inputs are bf16 tensors.
+
 After the timed region every launch of one step is also run on its own, 50
 times, each right after a 512 MiB write that evicts the L2s and the MALL
 ("kernels_cold": median, p10, p90 per launch), and a plain 1 GiB elementwise
@@ -53,8 +59,10 @@ FP8_PEAK_TFLOPS = 5000.0          # MI355X dense FP8 MFMA, published
 HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_block_stack.json")
 MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_block_stack.json")
-GEMM_SOURCE = os.path.join(ROOT, "fp8_block_scaled_tile_amd", "csrc", "gemm.hip")
-QUANT_SOURCE = os.path.join(ROOT, "fp8_block_scaled_tile_amd", "csrc", "quant.hip")
+_CSRC = os.path.join(ROOT, "fp8_block_scaled_tile_amd", "csrc")
+# the sources each profiled kernel is compiled from (its file and the headers it includes)
+GEMM_SOURCES = [os.path.join(_CSRC, n) for n in ("gemm.hip", "device_common.hpp")]
+QUANT_SOURCES = [os.path.join(_CSRC, n) for n in ("quant.hip", "quant_block.hpp", "device_common.hpp")]
 
 # kernel symbol of each launch class (for matching rocprofv3 summaries)
 KERNEL_SYMBOLS = {
@@ -83,6 +91,10 @@ def parse_args():
                    help="skip the per-launch cold-cache distribution (median / p10 / p90)")
     p.add_argument("--cold-iters", type=int, default=50,
                    help="cold-cache runs per launch of the step")
+    p.add_argument("--no-produce", action="store_true",
+                   help="skip the quantize-on-produce comparison (fused vs op + quant_act)")
+    p.add_argument("--produce-iters", type=int, default=20,
+                   help="timed calls per variant in the quantize-on-produce comparison")
     p.add_argument("--ingest-pmc", nargs=4,
                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                    help="turn rocprofv3 --pmc counter CSVs (bench run, then the copy "
@@ -95,12 +107,15 @@ def parse_args():
     return p.parse_args()
 
 
-def sha(path: str) -> str:
-    """Hash of a kernel source's code: comments and blank lines are dropped,
-    so editing a comment does not invalidate counters taken on the same code."""
+def sha(paths) -> str:
+    """Hash of a kernel's source code (its files in order): comments and blank
+    lines are dropped, so editing a comment does not invalidate counters taken
+    on the same code."""
     import re
-    with open(path) as f:
-        text = f.read()
+    text = ""
+    for path in paths:
+        with open(path) as f:
+            text += f.read() + "\n"
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     lines = [re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines()]
     code = "\n".join(ln for ln in lines if ln.strip())
@@ -158,6 +173,10 @@ class Linear:
 
     def flops(self):
         return sum(2.0 * M * N * K for _, _, M, N, K in self.gemms)
+
+
+def spec0_tokens(specs):
+    return specs[0].tokens
 
 
 def check(pf, rc, what):
@@ -234,6 +253,108 @@ def cold_kernel_stats(torch, pf, layers, stream, iters):
     return out
 
 
+def _median_ms(torch, fn, iters):
+    """Median event-timed duration of fn() over `iters` back-to-back calls
+    (after two untimed ones)."""
+    import numpy as np
+    for _ in range(2):
+        fn()
+    evs = []
+    for _ in range(iters):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in evs]))
+
+
+def produce_bench(torch, pf, tokens, hidden, ffn, stream, iters, seed):
+    """Fused (op -> FP8 codes, 1x128 + 128x1^T) against unfused (op -> bf16,
+    then quant_act) for the neighbour ops of one block.  Algorithmic bytes:
+    inputs read once, outputs written once (codes 1 B + 1 B, scales 8 B per
+    128 elements; bf16 2 B)."""
+    import synth
+    dual = 2.0 + 8.0 / 128.0                       # q + qt + s + st per element
+    ops = []
+
+    def bufs(rows, cols):
+        rp = (rows + 127) // 128 * 128
+        u8, f32 = torch.uint8, torch.float32
+        return {"q": torch.empty((rows, cols), dtype=u8, device="cuda"),
+                "s": torch.empty((cols // 128, rows), dtype=f32, device="cuda"),
+                "qt": torch.empty((cols, rp), dtype=u8, device="cuda"),
+                "st": torch.empty((rp // 128, cols), dtype=f32, device="cuda"),
+                "y": torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda")}
+
+    def qa(b, rows, cols):
+        return lambda: check(pf, pf.puro_fp8_quant_act(b["y"].data_ptr(), rows, cols, b["q"].data_ptr(),
+                                                       b["s"].data_ptr(), b["qt"].data_ptr(),
+                                                       b["st"].data_ptr(), stream), "quant_act")
+
+    def measure(name, rows, cols, fused, op_only, quant, bytes_fused, bytes_unfused, count):
+        f_ms = _median_ms(torch, fused, iters)
+        o_ms = _median_ms(torch, op_only, iters)
+        q_ms = _median_ms(torch, quant, iters)
+        rate = bytes_fused / (f_ms * 1e-3) / 1e9
+        ops.append({"op": name, "out_shape": [rows, cols], "per_block": count,
+                    "fused_ms": round(f_ms, 4), "unfused_ms": round(o_ms + q_ms, 4),
+                    "unfused_op_ms": round(o_ms, 4), "unfused_quant_ms": round(q_ms, 4),
+                    "speedup": round((o_ms + q_ms) / f_ms, 3),
+                    "fused_mb": round(bytes_fused / 1e6, 1), "unfused_mb": round(bytes_unfused / 1e6, 1),
+                    "fused_gbps": round(rate, 1), "frac_hbm_peak": round(rate / HBM_PEAK_GBPS, 4)})
+
+    # SwiGLU forward: gu [T, 2F] -> h [T, F]
+    d = synth.swiglu_inputs(tokens, ffn, seed=seed)
+    gu, dh = d["gu"].to("cuda"), d["dh"].to("cuda")
+    del d
+    b = bufs(tokens, ffn)
+    P = lambda t: t.data_ptr()
+    measure("swiglu_fwd", tokens, ffn,
+            lambda: check(pf, pf.puro_fp8_swiglu_quant(P(gu), tokens, ffn, P(b["q"]), P(b["s"]), P(b["qt"]),
+                                                       P(b["st"]), None, stream), "swiglu_quant"),
+            lambda: check(pf, pf.puro_fp8_swiglu_quant(P(gu), tokens, ffn, None, None, None, None,
+                                                       P(b["y"]), stream), "swiglu"),
+            qa(b, tokens, ffn),
+            tokens * ffn * (4.0 + dual), tokens * ffn * (4.0 + 2.0 + 2.0 + dual), 1)
+    del b
+    # SwiGLU backward: dh [T, F], gu -> (d gate | d up) [T, 2F]
+    b = bufs(tokens, 2 * ffn)
+    measure("swiglu_bwd", tokens, 2 * ffn,
+            lambda: check(pf, pf.puro_fp8_swiglu_bwd_quant(P(dh), P(gu), tokens, ffn, P(b["q"]), P(b["s"]),
+                                                           P(b["qt"]), P(b["st"]), None, stream),
+                          "swiglu_bwd_quant"),
+            lambda: check(pf, pf.puro_fp8_swiglu_bwd_quant(P(dh), P(gu), tokens, ffn, None, None, None,
+                                                           None, P(b["y"]), stream), "swiglu_bwd"),
+            qa(b, tokens, 2 * ffn),
+            tokens * ffn * (6.0 + 2 * dual), tokens * ffn * (6.0 + 4.0 + 2 * (2.0 + dual)), 1)
+    del b, gu, dh
+    # RMSNorm: x [T, H], gamma [H] -> y [T, H] (twice per block)
+    d = synth.rmsnorm_inputs(tokens, hidden, seed=seed)
+    x, gamma = d["x"].to("cuda"), d["gamma"].to("cuda")
+    rstd = torch.empty(tokens, dtype=torch.float32, device="cuda")
+    b = bufs(tokens, hidden)
+    measure("rmsnorm", tokens, hidden,
+            lambda: check(pf, pf.puro_fp8_rmsnorm_quant(P(x), P(gamma), tokens, hidden, 1e-6, P(rstd),
+                                                        P(b["q"]), P(b["s"]), P(b["qt"]), P(b["st"]),
+                                                        None, stream), "rmsnorm_quant"),
+            lambda: check(pf, pf.puro_fp8_rmsnorm_quant(P(x), P(gamma), tokens, hidden, 1e-6, P(rstd),
+                                                        None, None, None, None, P(b["y"]), stream),
+                          "rmsnorm"),
+            qa(b, tokens, hidden),
+            tokens * hidden * (2.0 + dual) + 4.0 * tokens,
+            tokens * hidden * (2.0 + 2.0 + 2.0 + dual) + 4.0 * tokens, 2)
+    del b, x, gamma, rstd
+    fused = sum(o["fused_ms"] * o["per_block"] for o in ops)
+    unfused = sum(o["unfused_ms"] * o["per_block"] for o in ops)
+    return {"ops": ops, "fused_ms_per_block": round(fused, 4),
+            "unfused_ms_per_block": round(unfused, 4),
+            "saved_ms_per_block": round(unfused - fused, 4),
+            "kind": "neighbour ops of one block writing FP8 operands directly vs op (bf16 out) + "
+                    "quant_act; median of event-timed calls; not part of the step"}
+
+
 def hbm_copy_reference(torch):
     """A plain elementwise kernel of known size on the same device: torch.neg
     over 2^28 float32 (1 GiB read, 1 GiB written), best of 10."""
@@ -297,7 +418,7 @@ def ingest_pmc(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
                                        sum(w) / len(w) * 1024.0 * (fw or 1.0)),
         }
     doc = {"copy_factor_fetch": ff, "copy_factor_write": fw,
-           "gemm_source_sha": sha(GEMM_SOURCE), "quant_source_sha": sha(QUANT_SOURCE),
+           "gemm_source_sha": sha(GEMM_SOURCES), "quant_source_sha": sha(QUANT_SOURCES),
            "kernels": kernels}
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(doc, f, indent=1, sort_keys=True)
@@ -329,7 +450,7 @@ def ingest_mfma(csv_path):
                   "mfma_util_pct": k["util_ns"] / k["ns"] if k["ns"] else 0.0,
                   "f8_flop_per_dispatch": k["f8_flop"] / k["dispatches"]}
            for name, k in kernels.items()}
-    doc = {"gemm_source_sha": sha(GEMM_SOURCE), "quant_source_sha": sha(QUANT_SOURCE), "kernels": out}
+    doc = {"gemm_source_sha": sha(GEMM_SOURCES), "quant_source_sha": sha(QUANT_SOURCES), "kernels": out}
     with open(MFMA_FILE, "w") as f:
         json.dump(doc, f, indent=1, sort_keys=True)
     print(f"wrote {MFMA_FILE}: {len(out)} kernels")
@@ -343,7 +464,7 @@ def _profile_entry(path, symbol_prefix):
             doc = json.load(f)
     except (OSError, ValueError):
         return None
-    src = GEMM_SOURCE if "gemm" in symbol_prefix else QUANT_SOURCE
+    src = GEMM_SOURCES if "gemm" in symbol_prefix else QUANT_SOURCES
     key = "gemm_source_sha" if "gemm" in symbol_prefix else "quant_source_sha"
     if doc.get(key) != sha(src):
         return None
@@ -597,6 +718,11 @@ def main():
                     "fp8_step_speedup": round(tms / ms_per_step, 3),
                     "fp8_gemm_speedup": round(tms / gemm_ms, 3) if gemm_ms else None}
 
+    produce = None
+    if not args.no_produce:
+        produce = produce_bench(torch, pf, spec0_tokens(specs), 2048, 8192, stream, args.produce_iters,
+                                args.seed)
+
     cold = None
     copy_ref = None
     if not args.no_cold_stats:
@@ -634,6 +760,7 @@ def main():
         "cpu_baseline": cpu,
         "bf16_reference": bf16,
         "bf16_tiled": bf16_own,
+        "produce": produce,
         "kernels_cold": cold,
         "hbm_copy_reference": copy_ref,
         "input_generation_s": round(gen_s, 1),

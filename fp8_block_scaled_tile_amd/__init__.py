@@ -30,7 +30,8 @@ __all__ = [
     "puro_fp8_gemm_workspace_bytes", "puro_fp8_status_string", "puro_fp8_abi_version",
     "puro_fp8_probe_encode", "quant_act", "quant_weight", "gemm_blockscaled",
     "puro_bf16_gemm_nt", "puro_bf16_gemm_nt_workspace_bytes", "gemm_bf16_nt",
-    "library_path",
+    "puro_fp8_swiglu_quant", "puro_fp8_swiglu_bwd_quant", "puro_fp8_rmsnorm_quant",
+    "swiglu_quant", "swiglu_bwd_quant", "rmsnorm_quant", "library_path",
 ]
 
 GEMM_FWD, GEMM_DGRAD, GEMM_WGRAD = 0, 1, 2
@@ -86,6 +87,19 @@ def puro_bf16_gemm_nt(M, N, K, a, b, c, workspace, workspace_bytes, stream) -> i
 
 def puro_bf16_gemm_nt_workspace_bytes(M, N, K) -> int:
     return int(_lib.get().puro_bf16_gemm_nt_workspace_bytes(M, N, K))
+
+
+def puro_fp8_swiglu_quant(gu, rows, f, q, s, qt, st, y, stream) -> int:
+    return _lib.get().puro_fp8_swiglu_quant(gu, rows, f, q, s, qt, st, y, stream)
+
+
+def puro_fp8_swiglu_bwd_quant(dh, gu, rows, f, q, s, qt, st, y, stream) -> int:
+    return _lib.get().puro_fp8_swiglu_bwd_quant(dh, gu, rows, f, q, s, qt, st, y, stream)
+
+
+def puro_fp8_rmsnorm_quant(x, gamma, rows, cols, eps, rstd, q, s, qt, st, y, stream) -> int:
+    return _lib.get().puro_fp8_rmsnorm_quant(x, gamma, rows, cols, eps, rstd, q, s, qt, st, y,
+                                             stream)
 
 
 # ---- torch-facing wrappers --------------------------------------------------
@@ -145,6 +159,75 @@ def quant_act(x, row: bool = True, col: bool = False, stream=None):
         out["st"] = torch.empty((rp // 128, cols), dtype=torch.float32, device=dev)
     _check(puro_fp8_quant_act(_ptr(x), rows, cols, _ptr(out.get("q")), _ptr(out.get("s")),
                               _ptr(out.get("qt")), _ptr(out.get("st")), _stream(stream)))
+    return out
+
+
+def _produce_outputs(rows, cols, dev, row, col, bf16_out):
+    torch = _torch()
+    rp = (rows + 127) // 128 * 128
+    out = {}
+    if row:
+        out["q"] = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+        out["s"] = torch.empty((cols // 128, rows), dtype=torch.float32, device=dev)
+    if col:
+        out["qt"] = torch.empty((cols, rp), dtype=torch.uint8, device=dev)
+        out["st"] = torch.empty((rp // 128, cols), dtype=torch.float32, device=dev)
+    if bf16_out:
+        out["y"] = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
+    return out
+
+
+def _bf16_2d(t, name):
+    torch = _torch()
+    if t.dtype != torch.bfloat16 or t.dim() != 2:
+        raise TypeError(f"{name}: expected a 2-D bfloat16 tensor")
+    return t.contiguous()
+
+
+def swiglu_quant(gu, row: bool = True, col: bool = True, bf16_out: bool = False, stream=None):
+    """SwiGLU of gu = (gate | up) [rows, 2f] written as FP8 operands: ``q``/``s``
+    (1x128), ``qt``/``st`` (128x1, transposed) and optionally ``y`` (bf16 h),
+    layouts as in quant_act with cols = f."""
+    gu = _bf16_2d(gu, "gu")
+    rows, f2 = gu.shape
+    out = _produce_outputs(rows, f2 // 2, gu.device, row, col, bf16_out)
+    _check(puro_fp8_swiglu_quant(_ptr(gu), rows, f2 // 2, _ptr(out.get("q")), _ptr(out.get("s")),
+                                 _ptr(out.get("qt")), _ptr(out.get("st")), _ptr(out.get("y")),
+                                 _stream(stream)))
+    return out
+
+
+def swiglu_bwd_quant(dh, gu, row: bool = True, col: bool = True, bf16_out: bool = False,
+                     stream=None):
+    """SwiGLU backward: (d gate | d up) [rows, 2f] from dh [rows, f] and gu,
+    written as FP8 operands (and optionally bf16 ``y``)."""
+    dh = _bf16_2d(dh, "dh")
+    gu = _bf16_2d(gu, "gu")
+    rows, f = dh.shape
+    if tuple(gu.shape) != (rows, 2 * f):
+        raise ValueError("gu must be [rows, 2f] for dh [rows, f]")
+    out = _produce_outputs(rows, 2 * f, dh.device, row, col, bf16_out)
+    _check(puro_fp8_swiglu_bwd_quant(_ptr(dh), _ptr(gu), rows, f, _ptr(out.get("q")),
+                                     _ptr(out.get("s")), _ptr(out.get("qt")), _ptr(out.get("st")),
+                                     _ptr(out.get("y")), _stream(stream)))
+    return out
+
+
+def rmsnorm_quant(x, gamma, eps: float = 1e-6, row: bool = True, col: bool = True,
+                  bf16_out: bool = False, stream=None):
+    """RMSNorm of x [rows, cols] with gain gamma [cols] written as FP8 operands
+    (and optionally bf16 ``y``); ``rstd`` f32 [rows] is always returned."""
+    torch = _torch()
+    x = _bf16_2d(x, "x")
+    rows, cols = x.shape
+    if gamma.dtype != torch.bfloat16 or tuple(gamma.shape) != (cols,):
+        raise TypeError("gamma: expected a bfloat16 tensor of shape [cols]")
+    gamma = gamma.contiguous()
+    out = _produce_outputs(rows, cols, x.device, row, col, bf16_out)
+    out["rstd"] = torch.empty(rows, dtype=torch.float32, device=x.device)
+    _check(puro_fp8_rmsnorm_quant(_ptr(x), _ptr(gamma), rows, cols, float(eps), _ptr(out["rstd"]),
+                                  _ptr(out.get("q")), _ptr(out.get("s")), _ptr(out.get("qt")),
+                                  _ptr(out.get("st")), _ptr(out.get("y")), _stream(stream)))
     return out
 
 

@@ -15,6 +15,7 @@ EXPORTS = (
     "puro_fp8_quant_act", "puro_fp8_quant_weight", "puro_fp8_gemm_blockscaled",
     "puro_fp8_gemm_workspace_bytes", "puro_fp8_status_string", "puro_fp8_abi_version",
     "puro_fp8_probe_encode", "puro_bf16_gemm_nt", "puro_bf16_gemm_nt_workspace_bytes",
+    "puro_fp8_swiglu_quant", "puro_fp8_swiglu_bwd_quant", "puro_fp8_rmsnorm_quant",
 )
 
 
@@ -53,5 +54,12 @@ def get():
         lib.puro_bf16_gemm_nt.argtypes = [I64, I64, I64, P, P, P, P, ctypes.c_size_t, P]
         lib.puro_bf16_gemm_nt_workspace_bytes.restype = ctypes.c_size_t
         lib.puro_bf16_gemm_nt_workspace_bytes.argtypes = [I64, I64, I64]
+        lib.puro_fp8_swiglu_quant.restype = I
+        lib.puro_fp8_swiglu_quant.argtypes = [P, I64, I64, P, P, P, P, P, P]
+        lib.puro_fp8_swiglu_bwd_quant.restype = I
+        lib.puro_fp8_swiglu_bwd_quant.argtypes = [P, P, I64, I64, P, P, P, P, P, P]
+        lib.puro_fp8_rmsnorm_quant.restype = I
+        lib.puro_fp8_rmsnorm_quant.argtypes = [P, P, I64, I64, ctypes.c_float, P, P, P, P, P, P,
+                                               P]
         _handle = lib
         return lib

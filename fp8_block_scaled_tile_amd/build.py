@@ -22,7 +22,7 @@ LIB_NAME = "libpuro_fp8.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["abi.hip", "quant.hip", "gemm.hip"]
+SOURCES = ["abi.hip", "quant.hip", "produce.hip", "gemm.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",

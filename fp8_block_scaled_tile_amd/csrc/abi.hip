@@ -67,6 +67,30 @@ puro_status_t check_weight(const void* w, int64_t n, int64_t k, const uint8_t* q
     return PURO_OK;
 }
 
+// Quantize-on-produce outputs: rows x out_cols, the layouts of check_act.
+// `in_ok` is false when a required input pointer is NULL.
+puro_status_t check_produce(bool in_ok, bool in_aligned, int64_t rows, int64_t out_cols,
+                            const uint8_t* q, const float* s, const uint8_t* qt, const float* st,
+                            const void* y)
+{
+    if (rows < 0 || out_cols <= 0 || out_cols % 128 != 0 || out_cols > kMaxDim)
+        return PURO_ERR_BAD_SHAPE;
+    if (rows > kMaxDim * 128 || ((rows + 127) / 128) * (out_cols / 128) > kMaxDim)
+        return PURO_ERR_BAD_SHAPE;
+    if (rows == 0)
+        return PURO_OK;
+    if (!in_ok)
+        return PURO_ERR_NULL_POINTER;
+    if ((q == nullptr) != (s == nullptr) || (qt == nullptr) != (st == nullptr))
+        return PURO_ERR_NULL_POINTER;
+    if (!q && !qt && !y)
+        return PURO_ERR_NULL_POINTER;
+    if (!in_aligned || (q && !aligned16(q)) || (s && !aligned16(s)) || (qt && !aligned16(qt)) ||
+        (st && !aligned16(st)) || (y && !aligned16(y)))
+        return PURO_ERR_MISALIGNED;
+    return PURO_OK;
+}
+
 bool gemm_shape_ok(int64_t M, int64_t N, int64_t K)
 {
     if (M < 0 || N <= 0 || K <= 0 || N % 128 != 0 || K % 128 != 0)
@@ -115,6 +139,57 @@ puro_status_t puro_fp8_quant_weight(const void* w, int64_t n, int64_t k, uint8_t
             return rc;
         return from_hip(puro::launch_quant_weight(w, n, k, q, qt, s,
                                                   static_cast<hipStream_t>(stream)));
+    });
+}
+
+puro_status_t puro_fp8_swiglu_quant(const void* gu, int64_t rows, int64_t f, uint8_t* q,
+                                    float* s, uint8_t* qt, float* st, void* y, void* stream)
+{
+    return guarded([&]() -> puro_status_t {
+        if (f > kMaxDim / 2)
+            return PURO_ERR_BAD_SHAPE;
+        const puro_status_t rc = check_produce(gu != nullptr, aligned16(gu), rows, f, q, s, qt, st, y);
+        if (rc != PURO_OK || rows == 0)
+            return rc;
+        return from_hip(puro::launch_swiglu_quant(gu, rows, f, q, s, qt, st, y,
+                                                  static_cast<hipStream_t>(stream)));
+    });
+}
+
+puro_status_t puro_fp8_swiglu_bwd_quant(const void* dh, const void* gu, int64_t rows, int64_t f,
+                                        uint8_t* q, float* s, uint8_t* qt, float* st, void* y,
+                                        void* stream)
+{
+    return guarded([&]() -> puro_status_t {
+        if (f <= 0 || f % 128 != 0 || f > kMaxDim / 2)
+            return PURO_ERR_BAD_SHAPE;
+        const puro_status_t rc = check_produce(dh && gu, aligned16(dh) && aligned16(gu), rows,
+                                               2 * f, q, s, qt, st, y);
+        if (rc != PURO_OK || rows == 0)
+            return rc;
+        return from_hip(puro::launch_swiglu_bwd_quant(dh, gu, rows, f, q, s, qt, st, y,
+                                                      static_cast<hipStream_t>(stream)));
+    });
+}
+
+puro_status_t puro_fp8_rmsnorm_quant(const void* x, const void* gamma, int64_t rows, int64_t cols,
+                                     float eps, float* rstd, uint8_t* q, float* s, uint8_t* qt,
+                                     float* st, void* y, void* stream)
+{
+    return guarded([&]() -> puro_status_t {
+        const puro_status_t rc = check_produce(x && gamma && rstd,
+                                               aligned16(x) && aligned16(gamma) && aligned16(rstd),
+                                               rows, cols, q, s, qt, st, y);
+        if (rc != PURO_OK)
+            return rc;
+        if ((rows + 3) / 4 > kMaxDim)        // the statistics pass runs 4 rows per work-group
+            return PURO_ERR_BAD_SHAPE;
+        if (!(eps >= 0.0f) || eps > std::numeric_limits<float>::max())
+            return PURO_ERR_BAD_VALUE;
+        if (rows == 0)
+            return PURO_OK;
+        return from_hip(puro::launch_rmsnorm_quant(x, gamma, rows, cols, eps, rstd, q, s, qt, st,
+                                                   y, static_cast<hipStream_t>(stream)));
     });
 }
 
@@ -216,6 +291,7 @@ const char* puro_fp8_status_string(puro_status_t status)
     case PURO_ERR_UNIMPLEMENTED: return "PURO_ERR_UNIMPLEMENTED: not supported by this build";
     case PURO_ERR_HIP:           return "PURO_ERR_HIP: the HIP runtime rejected a launch";
     case PURO_ERR_INTERNAL:      return "PURO_ERR_INTERNAL: unexpected internal failure";
+    case PURO_ERR_BAD_VALUE:     return "PURO_ERR_BAD_VALUE: a scalar argument is out of range";
     }
     return "unknown puro_status_t";
 }

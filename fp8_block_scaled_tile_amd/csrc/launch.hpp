@@ -12,6 +12,14 @@ hipError_t launch_quant_act(const void* x, int64_t rows, int64_t cols, uint8_t* 
                             uint8_t* qt, float* st, hipStream_t stream);
 hipError_t launch_quant_weight(const void* w, int64_t n, int64_t k, uint8_t* q, uint8_t* qt,
                                float* s, hipStream_t stream);
+hipError_t launch_swiglu_quant(const void* gu, int64_t rows, int64_t f, uint8_t* q, float* s,
+                               uint8_t* qt, float* st, void* h, hipStream_t stream);
+hipError_t launch_swiglu_bwd_quant(const void* dh, const void* gu, int64_t rows, int64_t f,
+                                   uint8_t* q, float* s, uint8_t* qt, float* st, void* dgu,
+                                   hipStream_t stream);
+hipError_t launch_rmsnorm_quant(const void* x, const void* gamma, int64_t rows, int64_t cols,
+                                float eps, float* rstd, uint8_t* q, float* s, uint8_t* qt,
+                                float* st, void* y, hipStream_t stream);
 hipError_t launch_probe_encode(uint32_t first, int64_t n, uint8_t* out, hipStream_t stream);
 
 size_t gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K);

@@ -1,0 +1,310 @@
+// produce.hip -- quantize-on-produce for gfx950: the BF16 neighbour ops of
+// the FP8 GEMMs compute their bf16 output in registers and quantize it there,
+// so the operand never makes a bf16 round trip through HBM.
+//
+// The pages put only the main linear-layer GEMMs on FP8 and keep the other
+// ops in BF16 (arXiv report "Puro-2B" section 2.1; training.farm blog section
+// "FP8").  Each kernel here therefore rounds the op's FP32 result to bf16
+// (nearest even) first and quantizes that bf16 value, so its codes and scales
+// are those of quant_act applied to the op's bf16 output:
+//   - SwiGLU forward: h = silu(gate) * up, gate | up concatenated as the
+//     fused up+gate projection writes them (gu [rows][2f], gate first); h is
+//     the down projection's input X.
+//   - SwiGLU backward: d gate = dh * up * silu'(gate), d up = dh * silu(gate),
+//     written as dgu [rows][2f] (d gate first): the up+gate projection's
+//     output gradient dY.
+//   - RMSNorm forward: y = x * rstd * gamma, rstd = 1/sqrt(mean(x^2) + eps):
+//     the input X of the projection after the norm.
+// Each can also write the bf16 result itself (what the unfused op writes).
+//
+// Work decomposition, block walk and code layout are those of the plain
+// activation quantizer (quant_block.hpp): one 256-thread work-group per
+// 128x128 output block.  SwiGLU backward takes one 128x128 block of h
+// columns and quantizes the two output blocks it yields (d gate and d up), so
+// dh, gate and up are read once.
+#include "launch.hpp"
+#include "quant_block.hpp"
+
+namespace puro {
+
+// sigmoid(g) = 1 / (1 + e^-g) in FP32.  e^-g = 2^(-g * log2 e) on the
+// hardware base-2 exponential, then the hardware reciprocal, each within
+// 1 ulp.  Rounding -g * log2 e carries a relative error of up to |g| * 2^-24
+// into the exponent, which shows in e^-g but is damped by e^-g / (1 + e^-g)
+// in the result: sigmoid's relative error stays below (2|g| (1 - sigmoid) + 3)
+// units of 2^-24.  For g < -87 the exponential overflows and the result is
+// 0 (silu's exact value there is below 10^-36).
+__device__ __forceinline__ float sigmoid_f32(float g)
+{
+    const float e = __builtin_amdgcn_exp2f(g * -1.44269504088896341f);
+    return __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+__device__ __forceinline__ uint4 load16(const uint16_t* p)
+{
+    return *reinterpret_cast<const uint4*>(p);
+}
+
+__device__ __forceinline__ void store16(uint16_t* p, const uint4& v)
+{
+    *reinterpret_cast<uint4*>(p) = v;
+}
+
+// Eight bf16 words of an op applied lane-wise to one, two or three inputs of
+// eight bf16 values each; `fn(a, b, c)` returns the FP32 result.
+template <typename Fn>
+__device__ __forceinline__ uint4 map8(const uint4& a, const uint4& b, const uint4& c, Fn fn)
+{
+    const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
+    const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
+    const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        o[i] = pack_bf16(fn(bf16_lo(aw[i]), bf16_lo(bw[i]), bf16_lo(cw[i])),
+                         fn(bf16_hi(aw[i]), bf16_hi(bw[i]), bf16_hi(cw[i])));
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// h = silu(g) * u = (g * sigmoid(g)) * u.
+struct SwigluH {
+    __device__ float operator()(float g, float u, float) const
+    {
+        return (g * sigmoid_f32(g)) * u;
+    }
+};
+
+// d gate = ((dh * u) * sigmoid(g)) * (1 + g * (1 - sigmoid(g))).
+struct SwigluDGate {
+    __device__ float operator()(float g, float u, float dh) const
+    {
+        const float sg = sigmoid_f32(g);
+        return ((dh * u) * sg) * __builtin_fmaf(g, 1.0f - sg, 1.0f);
+    }
+};
+
+// d up = dh * (g * sigmoid(g)).
+struct SwigluDUp {
+    __device__ float operator()(float g, float, float dh) const
+    {
+        return dh * (g * sigmoid_f32(g));
+    }
+};
+
+constexpr uint4 kZero4 = {0u, 0u, 0u, 0u};
+
+// ---- SwiGLU forward ---------------------------------------------------------
+
+template <bool ROW, bool COL, bool STORE_Y>
+__global__ __launch_bounds__(256) void swiglu_quant_kernel(
+    const uint16_t* __restrict__ gu, int64_t rows, int64_t f, int64_t ld_t,
+    uint8_t* __restrict__ q, float* __restrict__ s, uint8_t* __restrict__ qt,
+    float* __restrict__ st, uint16_t* __restrict__ h, int group_rows)
+{
+    __shared__ QuantLds<ROW, COL, false, false> lds;
+    const int t = threadIdx.x;
+    const BlockRC b = block_of(blockIdx.x, ld_t / 128, f / 128, group_rows);
+    const int64_t row0 = b.rb * 128 + 8 * (t >> 4);
+    const int64_t col0 = b.cb * 128 + 8 * (t & 15);
+
+    uint4 gv[8], uv[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const int64_t r = row0 + p;
+        gv[p] = r < rows ? load16(gu + r * 2 * f + col0) : kZero4;
+        uv[p] = r < rows ? load16(gu + r * 2 * f + f + col0) : kZero4;
+    }
+    uint4 v[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        // rows past the end hold zeros (silu(0) * 0 = +0), as the body requires
+        v[p] = row0 + p < rows ? map8(gv[p], uv[p], kZero4, SwigluH{}) : kZero4;
+        if (STORE_Y && row0 + p < rows)
+            store16(h + (row0 + p) * f + col0, v[p]);
+    }
+    if constexpr (ROW || COL)
+        quant_block_body<ROW, COL, false, false>(v, rows, f, ld_t, b.rb, b.cb, q, s, qt, st, lds);
+}
+
+// ---- SwiGLU backward --------------------------------------------------------
+
+template <bool ROW, bool COL, bool STORE_Y>
+__global__ __launch_bounds__(256) void swiglu_bwd_quant_kernel(
+    const uint16_t* __restrict__ dh, const uint16_t* __restrict__ gu, int64_t rows, int64_t f,
+    int64_t ld_t, uint8_t* __restrict__ q, float* __restrict__ s, uint8_t* __restrict__ qt,
+    float* __restrict__ st, uint16_t* __restrict__ dgu, int group_rows)
+{
+    __shared__ QuantLds<ROW, COL, false, false> lds;
+    const int t = threadIdx.x;
+    const BlockRC b = block_of(blockIdx.x, ld_t / 128, f / 128, group_rows);
+    const int64_t row0 = b.rb * 128 + 8 * (t >> 4);
+    const int64_t col0 = b.cb * 128 + 8 * (t & 15);
+
+    uint4 dg[8], du[8];
+    {
+        uint4 dv[8], gv[8], uv[8];
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const int64_t r = row0 + p;
+            dv[p] = r < rows ? load16(dh + r * f + col0) : kZero4;
+            gv[p] = r < rows ? load16(gu + r * 2 * f + col0) : kZero4;
+            uv[p] = r < rows ? load16(gu + r * 2 * f + f + col0) : kZero4;
+        }
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const bool in = row0 + p < rows;
+            dg[p] = in ? map8(gv[p], uv[p], dv[p], SwigluDGate{}) : kZero4;
+            du[p] = in ? map8(gv[p], uv[p], dv[p], SwigluDUp{}) : kZero4;
+            if (STORE_Y && in) {
+                store16(dgu + (row0 + p) * 2 * f + col0, dg[p]);
+                store16(dgu + (row0 + p) * 2 * f + f + col0, du[p]);
+            }
+        }
+    }
+    if constexpr (ROW || COL) {
+        quant_block_body<ROW, COL, false, false>(dg, rows, 2 * f, ld_t, b.rb, b.cb, q, s, qt, st,
+                                                 lds);
+        __syncthreads();   // the second block reuses the LDS
+        quant_block_body<ROW, COL, false, false>(du, rows, 2 * f, ld_t, b.rb, b.cb + f / 128, q, s,
+                                                 qt, st, lds);
+    }
+}
+
+// ---- RMSNorm forward --------------------------------------------------------
+
+// rstd[r] = 1 / sqrt(mean over c of x[r][c]^2 + eps), one wave per row.  Each
+// lane keeps eight partial sums (one per element of its 16-byte loads) that
+// are added pairwise and then across the wave, so no sum runs over more than
+// cols/512 sequential terms.  The square root and division are IEEE
+// correctly rounded (the library is built without fast-math).
+__global__ __launch_bounds__(256) void rmsnorm_rstd_kernel(const uint16_t* __restrict__ x,
+                                                           int64_t rows, int64_t cols, float eps,
+                                                           float* __restrict__ rstd)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= rows)
+        return;
+    float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t c = 8 * lane; c < cols; c += 512) {
+        const uint4 v = load16(x + r * cols + c);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float lo = bf16_lo(w[i]), hi = bf16_hi(w[i]);
+            acc[2 * i] = __builtin_fmaf(lo, lo, acc[2 * i]);
+            acc[2 * i + 1] = __builtin_fmaf(hi, hi, acc[2 * i + 1]);
+        }
+    }
+    float sum = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        sum += __shfl_xor(sum, off, 64);
+    if (lane == 0)
+        rstd[r] = 1.0f / sqrtf(sum / (float)cols + eps);
+}
+
+template <bool ROW, bool COL, bool STORE_Y>
+__global__ __launch_bounds__(256) void rmsnorm_quant_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma,
+    const float* __restrict__ rstd, int64_t rows, int64_t cols, int64_t ld_t,
+    uint8_t* __restrict__ q, float* __restrict__ s, uint8_t* __restrict__ qt,
+    float* __restrict__ st, uint16_t* __restrict__ y, int group_rows)
+{
+    __shared__ QuantLds<ROW, COL, false, false> lds;
+    const int t = threadIdx.x;
+    const BlockRC b = block_of(blockIdx.x, ld_t / 128, cols / 128, group_rows);
+    const int64_t row0 = b.rb * 128 + 8 * (t >> 4);
+    const int64_t col0 = b.cb * 128 + 8 * (t & 15);
+
+    uint4 xv[8];
+    float rs[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const int64_t r = row0 + p;
+        xv[p] = r < rows ? load16(x + r * cols + col0) : kZero4;
+        rs[p] = r < rows ? rstd[r] : 0.0f;
+    }
+    const uint4 gv = load16(gamma + col0);
+    uint4 v[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const float rp = rs[p];
+        v[p] = row0 + p < rows
+                   ? map8(xv[p], gv, kZero4, [rp](float xe, float ge, float) { return (xe * rp) * ge; })
+                   : kZero4;
+        if (STORE_Y && row0 + p < rows)
+            store16(y + (row0 + p) * cols + col0, v[p]);
+    }
+    if constexpr (ROW || COL)
+        quant_block_body<ROW, COL, false, false>(v, rows, cols, ld_t, b.rb, b.cb, q, s, qt, st,
+                                                 lds);
+}
+
+// ---- launchers --------------------------------------------------------------
+
+namespace {
+
+// Instantiates KERNEL<ROW, COL, STORE_Y> for the requested outputs.
+#define PURO_DISPATCH_OUTPUTS(KERNEL, GRID, ARGS)                                              \
+    do {                                                                                       \
+        const bool r_ = q != nullptr, c_ = qt != nullptr, y_ = yout != nullptr;                \
+        if (r_ && c_ && y_)        KERNEL<true, true, true><<<GRID, 256, 0, stream>>> ARGS;    \
+        else if (r_ && c_)         KERNEL<true, true, false><<<GRID, 256, 0, stream>>> ARGS;   \
+        else if (r_ && y_)         KERNEL<true, false, true><<<GRID, 256, 0, stream>>> ARGS;   \
+        else if (r_)               KERNEL<true, false, false><<<GRID, 256, 0, stream>>> ARGS;  \
+        else if (c_ && y_)         KERNEL<false, true, true><<<GRID, 256, 0, stream>>> ARGS;   \
+        else if (c_)               KERNEL<false, true, false><<<GRID, 256, 0, stream>>> ARGS;  \
+        else                       KERNEL<false, false, true><<<GRID, 256, 0, stream>>> ARGS;  \
+    } while (0)
+
+}  // namespace
+
+hipError_t launch_swiglu_quant(const void* gu, int64_t rows, int64_t f, uint8_t* q, float* s,
+                               uint8_t* qt, float* st, void* yout, hipStream_t stream)
+{
+    const int64_t rows_pad = (rows + 127) / 128 * 128;
+    const dim3 grid((unsigned)((rows_pad / 128) * (f / 128)));
+    const uint16_t* g = static_cast<const uint16_t*>(gu);
+    uint16_t* h = static_cast<uint16_t*>(yout);
+    const int gr = quant_group_rows(false, f);
+    PURO_DISPATCH_OUTPUTS(swiglu_quant_kernel, grid, (g, rows, f, rows_pad, q, s, qt, st, h, gr));
+    return hipGetLastError();
+}
+
+hipError_t launch_swiglu_bwd_quant(const void* dh, const void* gu, int64_t rows, int64_t f,
+                                   uint8_t* q, float* s, uint8_t* qt, float* st, void* yout,
+                                   hipStream_t stream)
+{
+    const int64_t rows_pad = (rows + 127) / 128 * 128;
+    const dim3 grid((unsigned)((rows_pad / 128) * (f / 128)));
+    const uint16_t* d = static_cast<const uint16_t*>(dh);
+    const uint16_t* g = static_cast<const uint16_t*>(gu);
+    uint16_t* dgu = static_cast<uint16_t*>(yout);
+    const int gr = quant_group_rows(false, 2 * f);
+    PURO_DISPATCH_OUTPUTS(swiglu_bwd_quant_kernel, grid,
+                          (d, g, rows, f, rows_pad, q, s, qt, st, dgu, gr));
+    return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_quant(const void* x, const void* gamma, int64_t rows, int64_t cols,
+                                float eps, float* rstd, uint8_t* q, float* s, uint8_t* qt,
+                                float* st, void* yout, hipStream_t stream)
+{
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    const uint16_t* gb = static_cast<const uint16_t*>(gamma);
+    uint16_t* y = static_cast<uint16_t*>(yout);
+    rmsnorm_rstd_kernel<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, stream>>>(xb, rows, cols, eps,
+                                                                             rstd);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    const int64_t rows_pad = (rows + 127) / 128 * 128;
+    const dim3 grid((unsigned)((rows_pad / 128) * (cols / 128)));
+    const int gr = quant_group_rows(false, cols);
+    PURO_DISPATCH_OUTPUTS(rmsnorm_quant_kernel, grid,
+                          (xb, gb, rstd, rows, cols, rows_pad, q, s, qt, st, y, gr));
+    return hipGetLastError();
+}
+
+}  // namespace puro

@@ -59,7 +59,8 @@ typedef enum {
     PURO_ERR_WORKSPACE = 5,     /* workspace smaller than required            */
     PURO_ERR_UNIMPLEMENTED = 6, /* valid request this build does not serve    */
     PURO_ERR_HIP = 7,           /* the HIP runtime rejected a launch          */
-    PURO_ERR_INTERNAL = 8       /* unexpected failure inside the library      */
+    PURO_ERR_INTERNAL = 8,      /* unexpected failure inside the library      */
+    PURO_ERR_BAD_VALUE = 9      /* a scalar argument out of range (e.g. eps)  */
 } puro_status_t;
 
 typedef enum {
@@ -170,6 +171,67 @@ int puro_fp8_abi_version(void);
  */
 puro_status_t puro_fp8_probe_encode(uint32_t first_bits, int64_t n, uint8_t* out,
                                     void* stream);
+
+/*
+ * Quantize-on-produce: the BF16 ops next to the FP8 GEMMs, each writing its
+ * result straight as FP8 operands (and, optionally, as bf16).
+ *
+ * The pages run only the main linear-layer GEMMs in FP8 and keep the other
+ * ops in BF16 (arXiv report section 2.1; blog section "FP8").  These entry
+ * points compute such an op in FP32, round the result to bf16 (nearest even)
+ * and quantize that bf16 tensor in the same kernel, so the outputs equal
+ * what the op followed by puro_fp8_quant_act on its [rows][out_cols] bf16
+ * result gives, without the bf16 round trip through HBM.  Output layouts and
+ * the ragged-row rule are those of puro_fp8_quant_act:
+ *   q  u8  [rows][out_cols]       s  f32 [out_cols/128][rows]
+ *   qt u8  [out_cols][rows_pad]   st f32 [rows_pad/128][out_cols]
+ *   y  bf16 [rows][out_cols]      the op's bf16 result (NULL = not written)
+ * Each of the pairs (q, s) and (qt, st) may be NULL, and y may be NULL, but
+ * not all three.  Requires rows >= 0 and the column counts below to be > 0
+ * multiples of 128.
+ *
+ * FP32 evaluation.  The result may differ from the exactly rounded bf16 of
+ * the op where the exact value lies within the FP32 evaluation error of a
+ * bf16 rounding boundary; it is then the other neighbour.  That error stays
+ * below 2^-18 of the op's magnitude (|result|; for d gate,
+ * |dh * up * sigmoid(gate)| * (1 + |gate|)) for |gate| <= 28 and, for
+ * RMSNorm, rows up to 2^16 columns.
+ */
+
+/*
+ * SwiGLU forward.  gu bf16 [rows][2f] holds gate (columns 0 .. f-1) and up
+ * (columns f .. 2f-1), as the fused up+gate projection writes them; the
+ * output (out_cols = f) is h = silu(gate) * up, silu(g) = g / (1 + e^-g):
+ * the input X of the down projection.
+ */
+puro_status_t puro_fp8_swiglu_quant(const void* gu, int64_t rows, int64_t f,
+                                    uint8_t* q, float* s, uint8_t* qt, float* st,
+                                    void* y, void* stream);
+
+/*
+ * SwiGLU backward.  dh bf16 [rows][f] is the gradient of h, gu as above; the
+ * output (out_cols = 2f) is (d gate | d up) with
+ *   d gate = dh * up * sigmoid(gate) * (1 + gate * (1 - sigmoid(gate)))
+ *   d up   = dh * silu(gate)
+ * the output gradient dY of the up+gate projection.
+ */
+puro_status_t puro_fp8_swiglu_bwd_quant(const void* dh, const void* gu, int64_t rows,
+                                        int64_t f, uint8_t* q, float* s, uint8_t* qt,
+                                        float* st, void* y, void* stream);
+
+/*
+ * RMSNorm forward.  x bf16 [rows][cols], gamma bf16 [cols]; the output
+ * (out_cols = cols) is y = x * rstd * gamma with
+ * rstd[r] = 1 / sqrt(mean over c of x[r][c]^2 + eps), the input X of the
+ * projection after the norm.  rstd f32 [rows] is written too (the norm's
+ * backward needs it) and is required.  eps must be finite and >= 0
+ * (PURO_ERR_BAD_VALUE otherwise).  Two kernels: the row statistics, then
+ * the fused normalize-and-quantize pass.
+ */
+puro_status_t puro_fp8_rmsnorm_quant(const void* x, const void* gamma, int64_t rows,
+                                     int64_t cols, float eps, float* rstd, uint8_t* q,
+                                     float* s, uint8_t* qt, float* st, void* y,
+                                     void* stream);
 
 /*
  * BF16 comparator (measurement only, not part of the FP8 path).

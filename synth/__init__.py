@@ -28,7 +28,8 @@ import numpy as np
 import torch
 
 __all__ = ["normal", "student_t3", "with_outliers", "bits", "from_bits",
-           "LinearSpec", "WORKLOADS", "workload", "linear_inputs"]
+           "LinearSpec", "WORKLOADS", "workload", "linear_inputs", "swiglu_inputs",
+           "rmsnorm_inputs"]
 
 
 def _gen(seed: int, stream: str) -> torch.Generator:
@@ -169,3 +170,33 @@ def linear_inputs(spec: LinearSpec, seed: int = 0, need=("x", "w", "dy")) -> dic
     if "dy" in need:
         out["dy"] = normal((spec.tokens, spec.d_out), spec.dy_std, seed, base + "/dy").to(torch.bfloat16)
     return out
+
+
+# ---- inputs of the BF16 neighbour ops (quantize-on-produce) ------------------
+# Readings: the up+gate projection's bf16 output (gate | up) is drawn as
+# N(0, 1) with 1% of its columns x4 (|gate| stays below ~20); the gradient of
+# the SwiGLU output as N(0, 1e-3) like the other output gradients; the
+# residual stream entering RMSNorm as N(0, 1) with 1% of channels x20 like the
+# linear inputs; the learned RMSNorm gain as 1 + N(0, 0.1).
+
+def swiglu_inputs(rows: int, f: int, seed: int = 0, need=("gu", "dh")) -> dict:
+    """bf16 CPU tensors gu [rows, 2f] (gate | up) and dh [rows, f]."""
+    out = {}
+    base = f"swiglu/{rows}x{f}"
+    if "gu" in need:
+        gu = normal((rows, 2 * f), 1.0, seed, base + "/gu")
+        with_outliers(gu, _pct_channels(2 * f), 4.0, seed, base + "/gu")
+        out["gu"] = gu.to(torch.bfloat16)
+        del gu
+    if "dh" in need:
+        out["dh"] = normal((rows, f), 1e-3, seed, base + "/dh").to(torch.bfloat16)
+    return out
+
+
+def rmsnorm_inputs(rows: int, cols: int, seed: int = 0) -> dict:
+    """bf16 CPU tensors x [rows, cols] and gamma [cols]."""
+    base = f"rmsnorm/{rows}x{cols}"
+    x = normal((rows, cols), 1.0, seed, base + "/x")
+    with_outliers(x, _pct_channels(cols), 20.0, seed, base + "/x")
+    gamma = 1.0 + normal((cols,), 0.1, seed, base + "/gamma")
+    return {"x": x.to(torch.bfloat16), "gamma": gamma.to(torch.bfloat16)}

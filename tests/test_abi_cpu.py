@@ -13,7 +13,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "puro_fp8.h")
 
-OK, NULLP, SHAPE, ALIGN, ENUM, WS = 0, 1, 2, 3, 4, 5
+OK, NULLP, SHAPE, ALIGN, ENUM, WS, VALUE = 0, 1, 2, 3, 4, 5, 9
 
 # fake device addresses: never dereferenced, since validation fails first
 P16 = 0x7F0000000000          # 16-byte aligned
@@ -23,7 +23,7 @@ P_ODD = 0x7F0000000008        # 8-byte aligned only
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(puro_fp8_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(puro_(?:fp8|bf16)_\w+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -39,7 +39,8 @@ def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("puro_fp8_quant_act", "puro_fp8_quant_weight", "puro_fp8_gemm_blockscaled",
               "puro_fp8_gemm_workspace_bytes", "puro_fp8_status_string",
-              "puro_fp8_abi_version", "puro_fp8_probe_encode"):
+              "puro_fp8_abi_version", "puro_fp8_probe_encode", "puro_fp8_swiglu_quant",
+              "puro_fp8_swiglu_bwd_quant", "puro_fp8_rmsnorm_quant", "puro_bf16_gemm_nt"):
         assert n in names
 
 
@@ -51,7 +52,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_abi_version_and_status_strings(lib):
     assert lib.puro_fp8_abi_version() == 1
-    for code in range(9):
+    for code in range(10):
         s = lib.puro_fp8_status_string(code)
         assert s.startswith("PURO_")
     assert "unknown" in lib.puro_fp8_status_string(77)
@@ -163,3 +164,47 @@ def test_bf16_comparator_validation(lib):
     assert f(256, 256, 8192, P16, P16, P16, None, 0, None) == WS
     assert f(256, 256, 8192, P16, P16, P16, P16, need - 16, None) == WS
     assert q(32768, 6144, 2048) == 0 and q(256, 100, 128) == 0
+
+
+def test_swiglu_quant_validation(lib):
+    f = lib.puro_fp8_swiglu_quant
+    assert f(P16, 16, 100, P16, P16, None, None, None, None) == SHAPE     # f % 128
+    assert f(P16, 16, 0, P16, P16, None, None, None, None) == SHAPE
+    assert f(P16, -1, 128, P16, P16, None, None, None, None) == SHAPE
+    assert f(None, 16, 128, P16, P16, None, None, None, None) == NULLP
+    assert f(P16, 16, 128, None, None, None, None, None, None) == NULLP   # no output at all
+    assert f(P16, 16, 128, P16, None, None, None, None, None) == NULLP    # half a pair
+    assert f(P16, 16, 128, None, None, None, P16, None, None) == NULLP
+    assert f(P_ODD, 16, 128, P16, P16, None, None, None, None) == ALIGN
+    assert f(P16, 16, 128, None, None, None, None, P_ODD, None) == ALIGN  # bf16 output
+    assert f(P16, 0, 128, P16, P16, P16, P16, P16, None) == OK            # empty: no-op
+
+
+def test_swiglu_bwd_quant_validation(lib):
+    f = lib.puro_fp8_swiglu_bwd_quant
+    assert f(P16, P16, 16, 64, P16, P16, None, None, None, None) == SHAPE
+    assert f(P16, P16, 16, -128, P16, P16, None, None, None, None) == SHAPE
+    assert f(None, P16, 16, 128, P16, P16, None, None, None, None) == NULLP
+    assert f(P16, None, 16, 128, P16, P16, None, None, None, None) == NULLP
+    assert f(P16, P16, 16, 128, None, None, None, None, None, None) == NULLP
+    assert f(P16, P_ODD, 16, 128, P16, P16, None, None, None, None) == ALIGN
+    assert f(P16, P16, 16, 128, None, None, P16, P_ODD, None, None) == ALIGN
+    assert f(P16, P16, 0, 128, P16, P16, None, None, None, None) == OK
+
+
+def test_rmsnorm_quant_validation(lib):
+    f = lib.puro_fp8_rmsnorm_quant
+    ok = (P16, P16, 16, 256, 1e-6, P16, P16, P16, P16, P16, None, None)
+    call = lambda i, v: f(*(ok[:i] + (v,) + ok[i + 1:]))
+    assert call(3, 200) == SHAPE                                           # cols % 128
+    assert call(2, -3) == SHAPE
+    assert call(0, None) == NULLP
+    assert call(1, None) == NULLP                                          # gamma
+    assert call(5, None) == NULLP                                          # rstd is required
+    assert f(P16, P16, 16, 256, 1e-6, P16, None, None, None, None, None, None) == NULLP
+    assert call(1, P_ODD) == ALIGN
+    assert call(5, P_ODD) == ALIGN
+    assert call(4, -1e-6) == VALUE                                         # eps < 0
+    assert call(4, float("nan")) == VALUE
+    assert call(4, float("inf")) == VALUE
+    assert f(P16, P16, 0, 256, 1e-6, P16, P16, P16, None, None, None, None) == OK

@@ -64,8 +64,8 @@ def test_ingest_mfma_weights_by_duration_and_gates_on_code(tmp_path, monkeypatch
     assert entry["dispatches"] == 2 and entry["f8_flop_per_dispatch"] == 512e6
     # a comment edit keeps the entry, a code edit drops it
     src = tmp_path / "gemm.hip"
-    src.write_text(open(bench.GEMM_SOURCE).read() + "\n// a comment\n")
-    monkeypatch.setattr(bench, "GEMM_SOURCE", str(src))
+    src.write_text(open(bench.GEMM_SOURCES[0]).read() + "\n// a comment\n")
+    monkeypatch.setattr(bench, "GEMM_SOURCES", [str(src)] + bench.GEMM_SOURCES[1:])
     assert bench.mfma_busy_for("void puro::gemm_bs_kernel<0, 0>") == 55.0
     src.write_text(open(str(src)).read() + "int changed_code;\n")
     assert bench.mfma_busy_for("void puro::gemm_bs_kernel<0, 0>") is None

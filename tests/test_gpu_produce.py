@@ -1,0 +1,198 @@
+"""GPU parity of quantize-on-produce (SwiGLU forward and backward, RMSNorm
+forward, each writing FP8 operands straight from the op) against the CPU
+oracle.  Calls go through the C ABI.
+
+The oracle evaluates the op in double and rounds once to bf16; the device
+evaluates it in FP32 and may return any bf16 value within its error bound,
+TOL * M, of the exact one (the bound the C header states).  produce_check
+compares every tile bit for bit where it has one correct result, and checks
+the others against every correct (scale, codes).
+
+Sizes: small cases span several tiles and a ragged last row block; the
+block-stack sizes (32768 tokens, FFN 8192, hidden 2048) run in the launch
+configuration the benchmark uses and are checked on sampled row blocks
+(each row block fixes its 1x128 and 128x1 tiles completely)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import produce_check as pc
+import synth
+from parity import bf16_host_bits, dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2.0 ** -18
+
+
+@pytest.fixture(scope="module")
+def pf():
+    import fp8_block_scaled_tile_amd as pf
+    assert torch.cuda.is_available()
+    return pf
+
+
+def _host_outputs(out, rows=None, row_sel=None, rb_sel=None):
+    """Host copies of the device outputs; with row_sel / rb_sel only the
+    sampled rows (row codes and scales) and row blocks (transposed codes and
+    scales)."""
+    h = {}
+    if "y" in out:
+        y = out["y"] if row_sel is None else out["y"][row_sel]
+        h["y"] = bf16_host_bits(y)
+    if "q" in out:
+        h["q"] = host(out["q"] if row_sel is None else out["q"][row_sel])
+        h["s"] = host(out["s"] if row_sel is None else out["s"][:, row_sel])
+    if "qt" in out:
+        if rb_sel is None:
+            h["qt"] = host(out["qt"])
+            h["st"] = host(out["st"])
+        else:
+            cols_idx = torch.cat([torch.arange(128 * rb, 128 * rb + 128) for rb in rb_sel])
+            h["qt"] = host(out["qt"][:, cols_idx.to(out["qt"].device)])
+            h["st"] = host(out["st"][list(rb_sel)])
+    return h
+
+
+def _same(a, b):
+    """Bitwise equality of two device tensors of the same dtype and shape."""
+    return a.dtype == b.dtype and a.shape == b.shape and torch.equal(
+        a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8))
+
+
+def _assert_ok(res, what):
+    assert pc.all_ok(res), f"{what}: {res}"
+    say(what, "ok", {k: (v if not isinstance(v, dict) else
+                         {kk: (len(vv) if kk == 'bad' else vv) for kk, vv in v.items()})
+                     for k, v in res.items()})
+
+
+# ---- SwiGLU forward ------------------------------------------------------------
+
+@pytest.mark.parametrize("rows,f", [(1, 128), (200, 384), (384, 256), (1100, 640)])
+def test_swiglu_fwd_parity(pf, rows, f):
+    say("swiglu_quant", rows, f)
+    gu = synth.swiglu_inputs(rows, f, seed=rows + f, need=("gu",))["gu"]
+    out = pf.swiglu_quant(dev(gu), row=True, col=True, bf16_out=True)
+    y, lo, hi = oracle.swiglu_fwd(synth.bits(gu), TOL)
+    _assert_ok(pc.check_outputs(_host_outputs(out), y, lo, hi, rows), f"swiglu {rows}x{f}")
+
+
+def test_swiglu_fwd_output_subsets(pf):
+    """Each subset of outputs equals the same outputs of the all-output call."""
+    rows, f = 300, 256
+    gu = dev(synth.swiglu_inputs(rows, f, seed=5, need=("gu",))["gu"])
+    say("swiglu_quant subsets", rows, f)
+    full = pf.swiglu_quant(gu, row=True, col=True, bf16_out=True)
+    for row, col, yb in [(True, False, False), (False, True, False), (False, False, True),
+                         (True, True, False), (True, False, True), (False, True, True)]:
+        part = pf.swiglu_quant(gu, row=row, col=col, bf16_out=yb)
+        for k, v in part.items():
+            assert _same(v, full[k]), (k, row, col, yb)
+
+
+# ---- SwiGLU backward -----------------------------------------------------------
+
+@pytest.mark.parametrize("rows,f", [(130, 128), (256, 256), (700, 384)])
+def test_swiglu_bwd_parity(pf, rows, f):
+    say("swiglu_bwd_quant", rows, f)
+    d = synth.swiglu_inputs(rows, f, seed=3 * rows + f)
+    out = pf.swiglu_bwd_quant(dev(d["dh"]), dev(d["gu"]), row=True, col=True, bf16_out=True)
+    y, lo, hi = oracle.swiglu_bwd(synth.bits(d["dh"]), synth.bits(d["gu"]), TOL)
+    _assert_ok(pc.check_outputs(_host_outputs(out), y, lo, hi, rows), f"swiglu_bwd {rows}x{f}")
+
+
+@pytest.mark.parametrize("row,col", [(True, False), (False, True)])
+def test_swiglu_bwd_single_orientation(pf, row, col):
+    rows, f = 200, 256
+    d = synth.swiglu_inputs(rows, f, seed=9)
+    say("swiglu_bwd_quant single", row, col)
+    out = pf.swiglu_bwd_quant(dev(d["dh"]), dev(d["gu"]), row=row, col=col)
+    y, lo, hi = oracle.swiglu_bwd(synth.bits(d["dh"]), synth.bits(d["gu"]), TOL)
+    _assert_ok(pc.check_outputs(_host_outputs(out), y, lo, hi, rows), "swiglu_bwd single")
+
+
+# ---- RMSNorm forward -------------------------------------------------------------
+
+@pytest.mark.parametrize("rows,cols,eps", [(77, 128, 1e-6), (256, 2048, 1e-5),
+                                           (130, 8192, 0.0), (1000, 384, 1e-6)])
+def test_rmsnorm_parity(pf, rows, cols, eps):
+    say("rmsnorm_quant", rows, cols, eps)
+    d = synth.rmsnorm_inputs(rows, cols, seed=rows + cols)
+    out = pf.rmsnorm_quant(dev(d["x"]), dev(d["gamma"]), eps=eps, row=True, col=True,
+                           bf16_out=True)
+    y, lo, hi, rstd = oracle.rmsnorm_fwd(synth.bits(d["x"]), synth.bits(d["gamma"]),
+                                        float(np.float32(eps)), TOL)
+    got_rstd = host(out["rstd"]).astype(np.float64)
+    assert np.max(np.abs(got_rstd - rstd) / rstd) <= TOL
+    _assert_ok(pc.check_outputs(_host_outputs(out), y, lo, hi, rows), f"rmsnorm {rows}x{cols}")
+
+
+# ---- fused equals unfused ----------------------------------------------------------
+
+@pytest.mark.parametrize("op", ["swiglu", "swiglu_bwd", "rmsnorm"])
+def test_fused_codes_equal_quant_act_of_the_bf16_output(pf, op):
+    """The fused kernel's codes and scales are bit for bit those of the plain
+    activation quantizer applied to the same kernel's bf16 output."""
+    rows, f = 513, 256
+    say("fused vs unfused", op, rows, f)
+    if op == "swiglu":
+        out = pf.swiglu_quant(dev(synth.swiglu_inputs(rows, f, seed=1, need=("gu",))["gu"]),
+                              bf16_out=True)
+    elif op == "swiglu_bwd":
+        d = synth.swiglu_inputs(rows, f, seed=2)
+        out = pf.swiglu_bwd_quant(dev(d["dh"]), dev(d["gu"]), bf16_out=True)
+    else:
+        d = synth.rmsnorm_inputs(rows, 4 * f, seed=3)
+        out = pf.rmsnorm_quant(dev(d["x"]), dev(d["gamma"]), bf16_out=True)
+    ref = pf.quant_act(out["y"], row=True, col=True)
+    for k in ("q", "s", "qt", "st"):
+        assert _same(out[k], ref[k]), k
+
+
+# ---- block-stack sizes, sampled ------------------------------------------------------
+
+SAMPLE_RBS = (0, 97, 255)          # first, an inner and the last 128-row block of 32768
+
+
+def _sample_rows():
+    return torch.cat([torch.arange(128 * rb, 128 * rb + 128) for rb in SAMPLE_RBS])
+
+
+def test_swiglu_fwd_block_stack_sampled(pf):
+    rows, f = 32768, 8192
+    say("swiglu_quant block_stack", rows, f)
+    gu = synth.swiglu_inputs(rows, f, seed=0, need=("gu",))["gu"]
+    out = pf.swiglu_quant(dev(gu), row=True, col=True)
+    sel = _sample_rows()
+    h = _host_outputs(out, row_sel=sel.to("cuda:0"), rb_sel=SAMPLE_RBS)
+    y, lo, hi = oracle.swiglu_fwd(synth.bits(gu[sel]), TOL)
+    _assert_ok(pc.check_outputs(h, y, lo, hi, sel.numel()), "swiglu block_stack")
+
+
+def test_swiglu_bwd_block_stack_sampled(pf):
+    rows, f = 32768, 8192
+    say("swiglu_bwd_quant block_stack", rows, f)
+    d = synth.swiglu_inputs(rows, f, seed=0)
+    out = pf.swiglu_bwd_quant(dev(d["dh"]), dev(d["gu"]), row=True, col=True)
+    sel = _sample_rows()
+    h = _host_outputs(out, row_sel=sel.to("cuda:0"), rb_sel=SAMPLE_RBS)
+    y, lo, hi = oracle.swiglu_bwd(synth.bits(d["dh"][sel]), synth.bits(d["gu"][sel]), TOL)
+    _assert_ok(pc.check_outputs(h, y, lo, hi, sel.numel()), "swiglu_bwd block_stack")
+
+
+def test_rmsnorm_block_stack_sampled(pf):
+    rows, cols = 32768, 2048
+    say("rmsnorm_quant block_stack", rows, cols)
+    d = synth.rmsnorm_inputs(rows, cols, seed=0)
+    out = pf.rmsnorm_quant(dev(d["x"]), dev(d["gamma"]), eps=1e-6, row=True, col=True)
+    sel = _sample_rows()
+    h = _host_outputs(out, row_sel=sel.to("cuda:0"), rb_sel=SAMPLE_RBS)
+    y, lo, hi, rstd = oracle.rmsnorm_fwd(synth.bits(d["x"][sel]), synth.bits(d["gamma"]),
+                                        float(np.float32(1e-6)), TOL)
+    got_rstd = host(out["rstd"][sel.to("cuda:0")]).astype(np.float64)
+    assert np.max(np.abs(got_rstd - rstd) / rstd) <= TOL
+    _assert_ok(pc.check_outputs(h, y, lo, hi, sel.numel()), "rmsnorm block_stack")
