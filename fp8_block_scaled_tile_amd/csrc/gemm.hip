@@ -78,13 +78,20 @@ enum { OUT_BF16 = 0, OUT_FP32 = 1, OUT_FP32_ACC = 2, OUT_PARTIAL = 3 };
 // distinct 16-byte bank groups.
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-// FWD / DGRAD read their B slice in a permuted row order (see frag_off_b)
-// and store it with a swizzle built from row bits 1, 3 and 4 instead:
-// position = c ^ (2 * ((r >> 3) & 3) + ((r >> 1) & 1)).  Within a 16-lane
-// fragment phase the rows of equal parity then carry 8 distinct masks, so
-// the reads stay conflict-free; any per-row XOR keeps the staging writes
-// conflict-free.
-__device__ __forceinline__ int swz_b(int row) { return (((row >> 3) & 3) << 1) | ((row >> 1) & 1); }
+// FWD / DGRAD read their B slice in a permuted row order (see frag_off_b):
+// fragment lane i reads row r = 8*(i>>2) + (i&3) (+ 4, 32 or 36 for tiles
+// 1-3).  Its swizzle is the A swizzle of the lane index, written in the row
+// bits that carry it (bits 0, 1, 3, 4; bits 2 and 5 only select the tile):
+// position = c ^ swz(i).  Lanes 0-7 and 8-15 of every phase then hit 8
+// distinct 16-byte bank groups each, and the 16 lanes of a phase 16 distinct
+// ones, like the A reads.  (Masks built from row bits 1, 3 and 4 alone left
+// pairs of lanes 0-7 on one group: 2-way conflicts, 0.28 conflict cycles per
+// LDS access in the counters.)  The staging writes are linear in LDS, so any
+// per-row XOR keeps them conflict-free.
+__device__ __forceinline__ int swz_b(int row)
+{
+    return ((row & 3) | (((row >> 3) & 1) << 2)) ^ ((row >> 4) & 1);
+}
 template <int MODE>
 __device__ __forceinline__ int swz_stage_b(int row) { return MODE == 2 ? swz(row) : swz_b(row); }
 
@@ -112,7 +119,7 @@ __device__ __forceinline__ FragOff frag_off(int lane)
 // with (lane >> 4) == g hold output columns 8*g .. 8*g+7 (tiles 0, 1) and
 // 32+8*g .. 32+8*g+7 (tiles 2, 3).  One 16-byte bf16 store per lane then
 // covers 64 contiguous bytes of a row across the 4 lane groups.  The row's
-// swizzle mask does not depend on tn (it uses row bits 1, 3, 4), so tile tn
+// swizzle mask does not depend on tn (it uses row bits 0, 1, 3, 4), so tile tn
 // is the tn = 0 offsets plus b_tile_rows(tn) rows.
 __device__ __forceinline__ int b_tile_rows(int tn) { return 4 * (tn & 1) + 32 * (tn >> 1); }
 
