@@ -243,9 +243,8 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(
 
 // ---- launchers --------------------------------------------------------------
 
-namespace {
-
-// Instantiates KERNEL<ROW, COL, STORE_Y> for the requested outputs.
+// Instantiates KERNEL<ROW, COL, STORE_Y> for the requested outputs (q, qt
+// and yout are the launcher's output pointers; at least one is non-null).
 #define PURO_DISPATCH_OUTPUTS(KERNEL, GRID, ARGS)                                              \
     do {                                                                                       \
         const bool r_ = q != nullptr, c_ = qt != nullptr, y_ = yout != nullptr;                \
@@ -257,8 +256,6 @@ namespace {
         else if (c_)               KERNEL<false, true, false><<<GRID, 256, 0, stream>>> ARGS;  \
         else                       KERNEL<false, false, true><<<GRID, 256, 0, stream>>> ARGS;  \
     } while (0)
-
-}  // namespace
 
 hipError_t launch_swiglu_quant(const void* gu, int64_t rows, int64_t f, uint8_t* q, float* s,
                                uint8_t* qt, float* st, void* yout, hipStream_t stream)
@@ -306,5 +303,7 @@ hipError_t launch_rmsnorm_quant(const void* x, const void* gamma, int64_t rows, 
                           (xb, gb, rstd, rows, cols, rows_pad, q, s, qt, st, y, gr));
     return hipGetLastError();
 }
+
+#undef PURO_DISPATCH_OUTPUTS
 
 }  // namespace puro
