@@ -27,17 +27,17 @@
 
 namespace puro {
 
-// sigmoid(g) = 1 / (1 + e^-g) in FP32.  e^-g = 2^(-g * log2 e) on the
-// hardware base-2 exponential, then the hardware reciprocal, each within
-// 1 ulp.  Rounding -g * log2 e carries a relative error of up to |g| * 2^-24
-// into the exponent, which shows in e^-g but is damped by e^-g / (1 + e^-g)
-// in the result: sigmoid's relative error stays below (2|g| (1 - sigmoid) + 3)
-// units of 2^-24.  For g < -87 the exponential overflows and the result is
-// 0 (silu's exact value there is below 10^-36).
+// sigmoid(g) = 1 / (1 + e^-g) in FP32: the math library's expf (within
+// 1 ulp over its whole range, as the library is built without fast-math),
+// then the hardware reciprocal (within 1 ulp).  A relative error of e^-g
+// reaches sigmoid damped by e^-g / (1 + e^-g), so sigmoid stays within about
+// 5 units of 2^-24 for every g; for g < -88 the exponential overflows and the
+// result is 0.  (2^(-g * log2 e) on the bare hardware exponential would cost
+// 2 instructions instead of about 13, but its error grows with |g|: rounding
+// -g * log2 e alone carries |g| * 2^-24 into the exponent.)
 __device__ __forceinline__ float sigmoid_f32(float g)
 {
-    const float e = __builtin_amdgcn_exp2f(g * -1.44269504088896341f);
-    return __builtin_amdgcn_rcpf(1.0f + e);
+    return __builtin_amdgcn_rcpf(1.0f + expf(-g));
 }
 
 __device__ __forceinline__ uint4 load16(const uint16_t* p)

@@ -194,7 +194,7 @@ puro_status_t puro_fp8_probe_encode(uint32_t first_bits, int64_t n, uint8_t* out
  * the op where the exact value lies within the FP32 evaluation error of a
  * bf16 rounding boundary; it is then the other neighbour.  That error stays
  * below 2^-18 of the op's magnitude (|result|; for d gate,
- * |dh * up * sigmoid(gate)| * (1 + |gate|)) for |gate| <= 24 and, for
+ * |dh * up * sigmoid(gate)| * (1 + |gate|)) for |gate| <= 80 and, for
  * RMSNorm, rows up to 2^15 columns.
  */
 

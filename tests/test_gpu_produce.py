@@ -94,6 +94,33 @@ def test_swiglu_fwd_output_subsets(pf):
             assert _same(v, full[k]), (k, row, col, yb)
 
 
+def _wide_gate(rows, f, seed):
+    """gate | up with the gate spread over [-80, 80] (the range the C header
+    states the error bound for) and up ~ N(0, 1)."""
+    d = synth.swiglu_inputs(rows, f, seed=seed)
+    gu = d["gu"].float()
+    gu[:, :f] = (gu[:, :f] * 8.0).clamp(-80.0, 80.0)
+    return gu.to(torch.bfloat16), d["dh"]
+
+
+def test_swiglu_fwd_wide_gate(pf):
+    rows, f = 300, 256
+    gu, _ = _wide_gate(rows, f, seed=12)
+    say("swiglu_quant wide gate", rows, f, float(gu[:, :f].float().abs().max()))
+    out = pf.swiglu_quant(dev(gu), row=True, col=True, bf16_out=True)
+    y, lo, hi = oracle.swiglu_fwd(synth.bits(gu), TOL)
+    _assert_ok(pc.check_outputs(_host_outputs(out), y, lo, hi, rows), "swiglu wide gate")
+
+
+def test_swiglu_bwd_wide_gate(pf):
+    rows, f = 300, 256
+    gu, dh = _wide_gate(rows, f, seed=13)
+    say("swiglu_bwd_quant wide gate", rows, f)
+    out = pf.swiglu_bwd_quant(dev(dh), dev(gu), row=True, col=True, bf16_out=True)
+    y, lo, hi = oracle.swiglu_bwd(synth.bits(dh), synth.bits(gu), TOL)
+    _assert_ok(pc.check_outputs(_host_outputs(out), y, lo, hi, rows), "swiglu_bwd wide gate")
+
+
 # ---- SwiGLU backward -----------------------------------------------------------
 
 @pytest.mark.parametrize("rows,f", [(130, 128), (256, 256), (700, 384)])
