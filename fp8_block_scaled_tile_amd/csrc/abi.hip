@@ -288,7 +288,7 @@ const char* puro_fp8_status_string(puro_status_t status)
     case PURO_ERR_MISALIGNED:    return "PURO_ERR_MISALIGNED: a pointer is not 16-byte aligned";
     case PURO_ERR_BAD_ENUM:      return "PURO_ERR_BAD_ENUM: unknown mode or dtype, or a bad combination";
     case PURO_ERR_WORKSPACE:     return "PURO_ERR_WORKSPACE: workspace smaller than required";
-    case PURO_ERR_UNIMPLEMENTED: return "PURO_ERR_UNIMPLEMENTED: not supported by this build";
+    case PURO_ERR_UNIMPLEMENTED: return "PURO_ERR_UNIMPLEMENTED: not supported by this library version";
     case PURO_ERR_HIP:           return "PURO_ERR_HIP: the HIP runtime rejected a launch";
     case PURO_ERR_INTERNAL:      return "PURO_ERR_INTERNAL: unexpected internal failure";
     case PURO_ERR_BAD_VALUE:     return "PURO_ERR_BAD_VALUE: a scalar argument is out of range";

@@ -57,7 +57,7 @@ typedef enum {
     PURO_ERR_MISALIGNED = 3,    /* a base pointer is not 16-byte aligned      */
     PURO_ERR_BAD_ENUM = 4,      /* unknown mode / dtype, or a bad combination */
     PURO_ERR_WORKSPACE = 5,     /* workspace smaller than required            */
-    PURO_ERR_UNIMPLEMENTED = 6, /* valid request this build does not serve    */
+    PURO_ERR_UNIMPLEMENTED = 6, /* valid request this version does not serve  */
     PURO_ERR_HIP = 7,           /* the HIP runtime rejected a launch          */
     PURO_ERR_INTERNAL = 8,      /* unexpected failure inside the library      */
     PURO_ERR_BAD_VALUE = 9      /* a scalar argument out of range (e.g. eps)  */

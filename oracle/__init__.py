@@ -1,7 +1,7 @@
 """CPU oracle for the fine-grained block-quantized FP8 linear layer.
 
 TEST INFRASTRUCTURE ONLY.  This package is the ground truth that the HIP
-library is checked against.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+library is checked against.  Only ``tests/``, the smoke check and
 the ``cpu_baseline`` leg of ``bench.py`` may import it; the product package
 never does, and this package never imports the product package.
 
