@@ -2,6 +2,7 @@
 order, with that layer's shapes (checked with a stand-in binding, no GPU)."""
 from __future__ import annotations
 
+import sys
 import types
 
 import bench
@@ -97,3 +98,19 @@ def test_ingest_pmc_scales_by_the_copy_calibration(tmp_path, monkeypatch):
     assert e["dispatches"] == 2
     assert e["hbm_bytes_per_dispatch"] == 2000.0 * 1024 * 2.0 + 500.0 * 1024 * 1.0
     assert bench.traffic_for("void puro::gemm_bs_kernel<0, 0>") == e["hbm_bytes_per_dispatch"]
+
+
+def test_more_than_one_gpu_is_refused(capsys, monkeypatch):
+    """bench.py measures one GPU; --gpus N > 1 exits with status 2 and says
+    why, before touching the GPU."""
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--gpus", "2"])
+    assert bench.main() == 2
+    err = capsys.readouterr().err
+    assert "one GPU" in err or "single" in err
+
+
+def test_roofline_classes_are_gemm_classes():
+    """The classes timed inside the timed region are GEMM launch classes with
+    kernel symbols, so the roofline always names a GEMM kernel."""
+    for c in bench.ROOFLINE_CLASSES:
+        assert c.startswith("gemm") and c in bench.KERNEL_SYMBOLS
