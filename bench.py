@@ -24,7 +24,11 @@ again with events around every launch.
 For context, the same 12 products are also timed as plain BF16 GEMMs, after
 the FP8 timed region: with the vendor library (torch.matmul,
 "bf16_reference") and with this library's own tiling on the bf16 matrix
-cores ("bf16_tiled"), each with the FP8/BF16 step and GEMM speedups.
+cores ("bf16_tiled"), each with the FP8/BF16 step and GEMM speedups.  The
+vendor's FP8 GEMM with one scale per tensor (torch._scaled_mm,
+"fp8_tensorwise_reference") runs the same products on the step's FP8 codes:
+a tuned FP8 GEMM without block scales, as a yardstick for the block-scaled
+GEMMs (not the same method).
 
 Quantize-on-produce ("produce"): the BF16 neighbour ops of one block at the
 same token count (RMSNorm x2 before QKV and up/gate, SwiGLU forward before
@@ -94,7 +98,8 @@ def parse_args():
                    help="token slice for the CPU-oracle baseline (0 = skip)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-bf16-reference", action="store_true",
-                   help="skip the BF16 GEMM comparisons, vendor and own tiling (context only)")
+                   help="skip the GEMM comparisons: BF16 vendor and own tiling, and the vendor "
+                        "FP8 GEMM with per-tensor scales (context only)")
     p.add_argument("--no-cold-stats", action="store_true",
                    help="skip the per-launch cold-cache distribution (median / p10 / p90)")
     p.add_argument("--cold-iters", type=int, default=50,
@@ -569,6 +574,50 @@ def bf16_tiled(torch, pf, layers, steps, stream):
     return ms, flops / (ms * 1e-3) / 1e12
 
 
+def fp8_tensorwise_reference(torch, layers, steps):
+    """The same 12 products through the vendor library's FP8 GEMM
+    (torch._scaled_mm -> hipBLASLt) on the codes the step's quantizers wrote,
+    with ONE scale per tensor: no per-block scales and no fold, so it is not
+    the block-scaled method.  It shows what a tuned FP8 GEMM without block
+    scales takes on these shapes; context, not part of the measured step.
+    Outputs are bf16 for FWD / DGRAD and FP32 for WGRAD where the vendor path
+    serves FP32 (bf16 otherwise, reported).  Returns None if this torch build
+    has no FP8 GEMM."""
+    f8 = getattr(torch, "float8_e4m3fn", None)
+    if f8 is None or not hasattr(torch, "_scaled_mm"):
+        return None
+    one = torch.ones((), dtype=torch.float32, device="cuda:0")
+    calls = []
+    wgrad_dtype = torch.float32
+    for L in layers:
+        calls.append((L.qx.view(f8), L.qw.view(f8), torch.bfloat16))      # Y  = X . W^T
+        calls.append((L.qdy.view(f8), L.qtw.view(f8), torch.bfloat16))    # dX = dY . W
+        calls.append((L.qtdy.view(f8), L.qtx.view(f8), None))             # dW = dY^T . X
+    try:
+        a, b, _ = calls[2]
+        torch._scaled_mm(a, b.t(), scale_a=one, scale_b=one, out_dtype=torch.float32)
+    except RuntimeError:
+        wgrad_dtype = torch.bfloat16
+    try:
+        def step():
+            for a, b, dt in calls:
+                torch._scaled_mm(a, b.t(), scale_a=one, scale_b=one, out_dtype=dt or wgrad_dtype)
+        for _ in range(3):
+            step()
+    except RuntimeError:
+        return None
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = sum(2.0 * a.shape[0] * b.shape[0] * a.shape[1] for a, b, _ in calls)
+    return ms, flops / (ms * 1e-3) / 1e12, str(wgrad_dtype).replace("torch.", "")
+
+
 # ---- CPU baseline --------------------------------------------------------------
 
 def cpu_baseline(specs, host_tensors, tokens):
@@ -746,6 +795,18 @@ def main():
                     "fp8_step_speedup": round(tms / ms_per_step, 3),
                     "fp8_gemm_speedup": round(tms / gemm_ms, 3) if gemm_ms else None}
 
+    fp8_vendor = None
+    if not args.no_bf16_reference:
+        ref = fp8_tensorwise_reference(torch, layers, args.steps)
+        if ref is not None:
+            vms, vtf, wdt = ref
+            fp8_vendor = {"value": round(vtf, 1), "unit": "TFLOP/s", "ms_per_step": round(vms, 4),
+                          "kind": "vendor FP8 GEMM (torch._scaled_mm -> hipBLASLt) with one scale "
+                                  "per tensor (no block scales, not the block-scaled method), "
+                                  "same 12 products on the step's FP8 codes, bf16 FWD/DGRAD "
+                                  f"outputs, {wdt} WGRAD output; context, not timed above",
+                          "block_scaled_gemm_ratio": round(vms / gemm_ms, 3) if gemm_ms else None}
+
     produce = None
     if not args.no_produce:
         produce = produce_bench(torch, pf, spec0_tokens(specs), 2048, 8192, stream, args.produce_iters,
@@ -789,6 +850,7 @@ def main():
         "cpu_baseline": cpu,
         "bf16_reference": bf16,
         "bf16_tiled": bf16_own,
+        "fp8_tensorwise_reference": fp8_vendor,
         "produce": produce,
         "kernels_cold": cold,
         "hbm_copy_reference": copy_ref,
