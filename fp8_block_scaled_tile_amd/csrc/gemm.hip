@@ -709,28 +709,34 @@ static hipError_t launch_mode(int out, const uint8_t* a, const float* sa, const 
     if (KB <= 0 || (splits - 1) * kbps >= KB)   // every unit needs a K-block
         return hipErrorInvalidValue;
     const dim3 grid((unsigned)persistent_grid(tiles_m * tiles_n * splits, stream));
+    const dim3 block(NTHREADS);
     if (splits > 1) {
-        gemm_bs_kernel<MODE, OUT_PARTIAL><<<grid, NTHREADS, 0, stream>>>(
-            a, sa, b, sb, ws, M, N, K, tiles_m, tiles_n, splits, kbps);
+        const hipError_t e = launch_kernel(gemm_bs_kernel<MODE, OUT_PARTIAL>, grid, block, stream,
+                                           a, sa, b, sb, ws, M, N, K, tiles_m, tiles_n, splits, kbps);
+        if (e != hipSuccess)
+            return e;
         const int64_t count4 = (int64_t)M * N / 4;
         const int64_t blocks = (count4 + 255) / 256;
-        const unsigned rgrid = (unsigned)(blocks < 8192 ? blocks : 8192);
+        const dim3 rgrid((unsigned)(blocks < 8192 ? blocks : 8192));
         const float* wsf = static_cast<const float*>(ws);
+        const int64_t total = (int64_t)M * N;
         if (out == OUT_BF16)
-            splitk_reduce_kernel<OUT_BF16><<<rgrid, 256, 0, stream>>>(wsf, c, count4, splits, (int64_t)M * N);
-        else if (out == OUT_FP32)
-            splitk_reduce_kernel<OUT_FP32><<<rgrid, 256, 0, stream>>>(wsf, c, count4, splits, (int64_t)M * N);
-        else
-            splitk_reduce_kernel<OUT_FP32_ACC><<<rgrid, 256, 0, stream>>>(wsf, c, count4, splits, (int64_t)M * N);
-        return hipGetLastError();
+            return launch_kernel(splitk_reduce_kernel<OUT_BF16>, rgrid, dim3(256), stream, wsf, c,
+                                 count4, splits, total);
+        if (out == OUT_FP32)
+            return launch_kernel(splitk_reduce_kernel<OUT_FP32>, rgrid, dim3(256), stream, wsf, c,
+                                 count4, splits, total);
+        return launch_kernel(splitk_reduce_kernel<OUT_FP32_ACC>, rgrid, dim3(256), stream, wsf, c,
+                             count4, splits, total);
     }
     if (out == OUT_BF16)
-        gemm_bs_kernel<MODE, OUT_BF16><<<grid, NTHREADS, 0, stream>>>(a, sa, b, sb, c, M, N, K, tiles_m, tiles_n, 1, KB);
-    else if (out == OUT_FP32)
-        gemm_bs_kernel<MODE, OUT_FP32><<<grid, NTHREADS, 0, stream>>>(a, sa, b, sb, c, M, N, K, tiles_m, tiles_n, 1, KB);
-    else
-        gemm_bs_kernel<MODE, OUT_FP32_ACC><<<grid, NTHREADS, 0, stream>>>(a, sa, b, sb, c, M, N, K, tiles_m, tiles_n, 1, KB);
-    return hipGetLastError();
+        return launch_kernel(gemm_bs_kernel<MODE, OUT_BF16>, grid, block, stream, a, sa, b, sb, c,
+                             M, N, K, tiles_m, tiles_n, 1, KB);
+    if (out == OUT_FP32)
+        return launch_kernel(gemm_bs_kernel<MODE, OUT_FP32>, grid, block, stream, a, sa, b, sb, c,
+                             M, N, K, tiles_m, tiles_n, 1, KB);
+    return launch_kernel(gemm_bs_kernel<MODE, OUT_FP32_ACC>, grid, block, stream, a, sa, b, sb, c,
+                         M, N, K, tiles_m, tiles_n, 1, KB);
 }
 
 size_t gemm_bf16_workspace_bytes(int64_t M, int64_t N, int64_t K)

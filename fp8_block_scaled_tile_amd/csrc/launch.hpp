@@ -6,7 +6,32 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <type_traits>
+#include <utility>
+
 namespace puro {
+
+// Launches `kernel` through hipLaunchKernel and returns that launch's own
+// status.  (hipGetLastError after a triple-chevron launch reports the last
+// error of any runtime call on the thread: it could blame the launch for an
+// earlier, unrelated failure of the caller's, and would clear it.)  The
+// arguments are converted to the kernel's parameter types first, as a
+// triple-chevron launch converts them.
+template <typename... P, typename... A>
+hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t stream,
+                         A&&... args)
+{
+    static_assert(sizeof...(P) == sizeof...(A) && sizeof...(P) > 0, "kernel argument count");
+    std::tuple<std::decay_t<P>...> vals(static_cast<std::decay_t<P>>(std::forward<A>(args))...);
+    return std::apply(
+        [&](auto&... v) {
+            void* ptrs[] = {const_cast<void*>(static_cast<const void*>(&v))...};
+            return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, 0,
+                                   stream);
+        },
+        vals);
+}
 
 hipError_t launch_quant_act(const void* x, int64_t rows, int64_t cols, uint8_t* q, float* s,
                             uint8_t* qt, float* st, hipStream_t stream);

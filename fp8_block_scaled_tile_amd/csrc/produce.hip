@@ -243,19 +243,28 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(
 
 // ---- launchers --------------------------------------------------------------
 
-// Instantiates KERNEL<ROW, COL, STORE_Y> for the requested outputs (q, qt
-// and yout are the launcher's output pointers; at least one is non-null).
+// Launches KERNEL<ROW, COL, STORE_Y> for the requested outputs (q, qt and
+// yout are the launcher's output pointers; at least one is non-null) and
+// evaluates to the launch's status.  ARGS is the parenthesized argument list.
+#define PURO_EXPAND(...) __VA_ARGS__
 #define PURO_DISPATCH_OUTPUTS(KERNEL, GRID, ARGS)                                              \
-    do {                                                                                       \
+    [&]() -> hipError_t {                                                                      \
         const bool r_ = q != nullptr, c_ = qt != nullptr, y_ = yout != nullptr;                \
-        if (r_ && c_ && y_)        KERNEL<true, true, true><<<GRID, 256, 0, stream>>> ARGS;    \
-        else if (r_ && c_)         KERNEL<true, true, false><<<GRID, 256, 0, stream>>> ARGS;   \
-        else if (r_ && y_)         KERNEL<true, false, true><<<GRID, 256, 0, stream>>> ARGS;   \
-        else if (r_)               KERNEL<true, false, false><<<GRID, 256, 0, stream>>> ARGS;  \
-        else if (c_ && y_)         KERNEL<false, true, true><<<GRID, 256, 0, stream>>> ARGS;   \
-        else if (c_)               KERNEL<false, true, false><<<GRID, 256, 0, stream>>> ARGS;  \
-        else                       KERNEL<false, false, true><<<GRID, 256, 0, stream>>> ARGS;  \
-    } while (0)
+        const dim3 b_(256);                                                                    \
+        if (r_ && c_ && y_)                                                                    \
+            return launch_kernel(KERNEL<true, true, true>, GRID, b_, stream, PURO_EXPAND ARGS);  \
+        if (r_ && c_)                                                                          \
+            return launch_kernel(KERNEL<true, true, false>, GRID, b_, stream, PURO_EXPAND ARGS); \
+        if (r_ && y_)                                                                          \
+            return launch_kernel(KERNEL<true, false, true>, GRID, b_, stream, PURO_EXPAND ARGS); \
+        if (r_)                                                                                \
+            return launch_kernel(KERNEL<true, false, false>, GRID, b_, stream, PURO_EXPAND ARGS); \
+        if (c_ && y_)                                                                          \
+            return launch_kernel(KERNEL<false, true, true>, GRID, b_, stream, PURO_EXPAND ARGS); \
+        if (c_)                                                                                \
+            return launch_kernel(KERNEL<false, true, false>, GRID, b_, stream, PURO_EXPAND ARGS); \
+        return launch_kernel(KERNEL<false, false, true>, GRID, b_, stream, PURO_EXPAND ARGS);    \
+    }()
 
 hipError_t launch_swiglu_quant(const void* gu, int64_t rows, int64_t f, uint8_t* q, float* s,
                                uint8_t* qt, float* st, void* yout, hipStream_t stream)
@@ -265,8 +274,8 @@ hipError_t launch_swiglu_quant(const void* gu, int64_t rows, int64_t f, uint8_t*
     const uint16_t* g = static_cast<const uint16_t*>(gu);
     uint16_t* h = static_cast<uint16_t*>(yout);
     const int gr = quant_group_rows(false, f);
-    PURO_DISPATCH_OUTPUTS(swiglu_quant_kernel, grid, (g, rows, f, rows_pad, q, s, qt, st, h, gr));
-    return hipGetLastError();
+    return PURO_DISPATCH_OUTPUTS(swiglu_quant_kernel, grid,
+                                 (g, rows, f, rows_pad, q, s, qt, st, h, gr));
 }
 
 hipError_t launch_swiglu_bwd_quant(const void* dh, const void* gu, int64_t rows, int64_t f,
@@ -279,9 +288,8 @@ hipError_t launch_swiglu_bwd_quant(const void* dh, const void* gu, int64_t rows,
     const uint16_t* g = static_cast<const uint16_t*>(gu);
     uint16_t* dgu = static_cast<uint16_t*>(yout);
     const int gr = quant_group_rows(false, 2 * f);
-    PURO_DISPATCH_OUTPUTS(swiglu_bwd_quant_kernel, grid,
-                          (d, g, rows, f, rows_pad, q, s, qt, st, dgu, gr));
-    return hipGetLastError();
+    return PURO_DISPATCH_OUTPUTS(swiglu_bwd_quant_kernel, grid,
+                                 (d, g, rows, f, rows_pad, q, s, qt, st, dgu, gr));
 }
 
 hipError_t launch_rmsnorm_quant(const void* x, const void* gamma, int64_t rows, int64_t cols,
@@ -291,19 +299,18 @@ hipError_t launch_rmsnorm_quant(const void* x, const void* gamma, int64_t rows, 
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     const uint16_t* gb = static_cast<const uint16_t*>(gamma);
     uint16_t* y = static_cast<uint16_t*>(yout);
-    rmsnorm_rstd_kernel<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, stream>>>(xb, rows, cols, eps,
-                                                                             rstd);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = launch_kernel(rmsnorm_rstd_kernel, dim3((unsigned)((rows + 3) / 4)),
+                                       dim3(256), stream, xb, rows, cols, eps, rstd);
     if (e != hipSuccess)
         return e;
     const int64_t rows_pad = (rows + 127) / 128 * 128;
     const dim3 grid((unsigned)((rows_pad / 128) * (cols / 128)));
     const int gr = quant_group_rows(false, cols);
-    PURO_DISPATCH_OUTPUTS(rmsnorm_quant_kernel, grid,
-                          (xb, gb, rstd, rows, cols, rows_pad, q, s, qt, st, y, gr));
-    return hipGetLastError();
+    return PURO_DISPATCH_OUTPUTS(rmsnorm_quant_kernel, grid,
+                                 (xb, gb, rstd, rows, cols, rows_pad, q, s, qt, st, y, gr));
 }
 
 #undef PURO_DISPATCH_OUTPUTS
+#undef PURO_EXPAND
 
 }  // namespace puro

@@ -63,12 +63,13 @@ hipError_t launch_quant_act(const void* x, int64_t rows, int64_t cols, uint8_t* 
     const bool row = q != nullptr, col = qt != nullptr;
     const int gr = quant_group_rows(false, cols);
     if (row && col)
-        quant_block_kernel<true, true, false, false><<<grid, 256, 0, stream>>>(xb, rows, cols, rows_pad, q, s, qt, st, gr);
-    else if (row)
-        quant_block_kernel<true, false, false, false><<<grid, 256, 0, stream>>>(xb, rows, cols, rows_pad, q, s, qt, st, gr);
-    else
-        quant_block_kernel<false, true, false, false><<<grid, 256, 0, stream>>>(xb, rows, cols, rows_pad, q, s, qt, st, gr);
-    return hipGetLastError();
+        return launch_kernel(quant_block_kernel<true, true, false, false>, grid, dim3(256), stream,
+                             xb, rows, cols, rows_pad, q, s, qt, st, gr);
+    if (row)
+        return launch_kernel(quant_block_kernel<true, false, false, false>, grid, dim3(256), stream,
+                             xb, rows, cols, rows_pad, q, s, qt, st, gr);
+    return launch_kernel(quant_block_kernel<false, true, false, false>, grid, dim3(256), stream,
+                         xb, rows, cols, rows_pad, q, s, qt, st, gr);
 }
 
 hipError_t launch_quant_weight(const void* w, int64_t n, int64_t k, uint8_t* q, uint8_t* qt,
@@ -78,18 +79,17 @@ hipError_t launch_quant_weight(const void* w, int64_t n, int64_t k, uint8_t* q, 
     const uint16_t* wb = static_cast<const uint16_t*>(w);
     const int gr = quant_group_rows(true, k);
     if (qt)
-        quant_block_kernel<false, false, true, true><<<grid, 256, 0, stream>>>(wb, n, k, n, q, s, qt, nullptr, gr);
-    else
-        quant_block_kernel<false, false, true, false><<<grid, 256, 0, stream>>>(wb, n, k, n, q, s, nullptr, nullptr, gr);
-    return hipGetLastError();
+        return launch_kernel(quant_block_kernel<false, false, true, true>, grid, dim3(256), stream,
+                             wb, n, k, n, q, s, qt, nullptr, gr);
+    return launch_kernel(quant_block_kernel<false, false, true, false>, grid, dim3(256), stream,
+                         wb, n, k, n, q, s, nullptr, nullptr, gr);
 }
 
 hipError_t launch_probe_encode(uint32_t first, int64_t n, uint8_t* out, hipStream_t stream)
 {
     const int64_t blocks_needed = (n + 1023) / 1024;
     const unsigned grid = (unsigned)(blocks_needed < 65536 ? blocks_needed : 65536);
-    probe_encode_kernel<<<grid, 256, 0, stream>>>(first, n, out);
-    return hipGetLastError();
+    return launch_kernel(probe_encode_kernel, dim3(grid), dim3(256), stream, first, n, out);
 }
 
 }  // namespace puro
