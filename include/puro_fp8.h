@@ -30,7 +30,9 @@
  *   - Calls are asynchronous: they validate arguments, enqueue kernels on
  *     `stream` and return.  Argument errors return synchronously before any
  *     work is enqueued and have no side effects.  A launch failure returns
- *     PURO_ERR_HIP.  A device fault surfaces at the caller's next
+ *     PURO_ERR_HIP; the status is that of this call's own launches, so an
+ *     earlier, unread error of another HIP call on the thread is neither
+ *     reported nor cleared.  A device fault surfaces at the caller's next
  *     synchronization.  No C++ exception crosses this boundary.
  *   - Tensors are dense and row-major.  Every base pointer must be 16-byte
  *     aligned.  Outputs must not alias inputs.  NaN / Inf inputs give
