@@ -138,15 +138,30 @@ def _need(t, dtype, shape, name):
     return t
 
 
+def _bf16_2d(t, name):
+    """A 2-D bfloat16 CUDA tensor, made contiguous.  The device check keeps a
+    host tensor's pointer from ever reaching a kernel."""
+    torch = _torch()
+    if t.dtype != torch.bfloat16 or t.dim() != 2:
+        raise TypeError(f"{name}: expected a 2-D bfloat16 tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: expected a CUDA tensor, got one on {t.device}")
+    return t.contiguous()
+
+
+def _same_device(first, *others):
+    for t in others:
+        if t.device != first.device:
+            raise ValueError(f"tensors on different devices: {first.device} and {t.device}")
+
+
 def quant_act(x, row: bool = True, col: bool = False, stream=None):
     """1x128 (row) and/or 128x1 (col, transposed) quantization of a bf16
     [rows, cols] CUDA tensor.  Returns a dict with ``q`` u8 [rows, cols] and
     ``s`` f32 [cols/128, rows] (row), ``qt`` u8 [cols, rows_pad] and ``st``
     f32 [rows_pad/128, cols] (col)."""
     torch = _torch()
-    if x.dtype != torch.bfloat16 or x.dim() != 2:
-        raise TypeError("quant_act expects a 2-D bfloat16 tensor")
-    x = x.contiguous()
+    x = _bf16_2d(x, "x")
     rows, cols = x.shape
     rp = (rows + 127) // 128 * 128
     out = {}
@@ -177,13 +192,6 @@ def _produce_outputs(rows, cols, dev, row, col, bf16_out):
     return out
 
 
-def _bf16_2d(t, name):
-    torch = _torch()
-    if t.dtype != torch.bfloat16 or t.dim() != 2:
-        raise TypeError(f"{name}: expected a 2-D bfloat16 tensor")
-    return t.contiguous()
-
-
 def swiglu_quant(gu, row: bool = True, col: bool = True, bf16_out: bool = False, stream=None):
     """SwiGLU of gu = (gate | up) [rows, 2f] written as FP8 operands: ``q``/``s``
     (1x128), ``qt``/``st`` (128x1, transposed) and optionally ``y`` (bf16 h),
@@ -203,6 +211,7 @@ def swiglu_bwd_quant(dh, gu, row: bool = True, col: bool = True, bf16_out: bool 
     written as FP8 operands (and optionally bf16 ``y``)."""
     dh = _bf16_2d(dh, "dh")
     gu = _bf16_2d(gu, "gu")
+    _same_device(dh, gu)
     rows, f = dh.shape
     if tuple(gu.shape) != (rows, 2 * f):
         raise ValueError("gu must be [rows, 2f] for dh [rows, f]")
@@ -222,6 +231,7 @@ def rmsnorm_quant(x, gamma, eps: float = 1e-6, row: bool = True, col: bool = Tru
     rows, cols = x.shape
     if gamma.dtype != torch.bfloat16 or tuple(gamma.shape) != (cols,):
         raise TypeError("gamma: expected a bfloat16 tensor of shape [cols]")
+    _same_device(x, gamma)
     gamma = gamma.contiguous()
     out = _produce_outputs(rows, cols, x.device, row, col, bf16_out)
     out["rstd"] = torch.empty(rows, dtype=torch.float32, device=x.device)
@@ -235,9 +245,7 @@ def quant_weight(w, transpose: bool = True, stream=None):
     """128x128 block quantization of a bf16 [n, k] CUDA tensor.  Returns a dict
     with ``q`` u8 [n, k], ``s`` f32 [n/128, k/128] and ``qt`` u8 [k, n]."""
     torch = _torch()
-    if w.dtype != torch.bfloat16 or w.dim() != 2:
-        raise TypeError("quant_weight expects a 2-D bfloat16 tensor")
-    w = w.contiguous()
+    w = _bf16_2d(w, "w")
     n, k = w.shape
     dev = w.device
     out = {"q": torch.empty((n, k), dtype=torch.uint8, device=dev),
@@ -254,6 +262,10 @@ def gemm_blockscaled(mode: int, a, sa, b, sb, out_dtype=None, out=None, accumula
     """Block-scaled FP8 GEMM: C[M, N] (+)= blocks of a[M, K] . b[N, K]^T with
     scales sa [K/128, M] and sb (see the C header for each mode's layout)."""
     torch = _torch()
+    if mode not in (GEMM_FWD, GEMM_DGRAD, GEMM_WGRAD):
+        raise ValueError(f"unknown GEMM mode {mode}")
+    if a.dim() != 2 or b.dim() != 2:
+        raise ValueError("a and b must be 2-D")
     M, K = a.shape
     N = b.shape[0]
     if out_dtype is None:
@@ -267,15 +279,20 @@ def gemm_blockscaled(mode: int, a, sa, b, sb, out_dtype=None, out=None, accumula
     sb_shape = {GEMM_FWD: (N // 128, K // 128), GEMM_DGRAD: (K // 128, N // 128),
                 GEMM_WGRAD: (K // 128, N)}[mode]
     _need(sb, torch.float32, sb_shape, "sb")
+    _same_device(a, sa, b, sb)
     if out is None:
         out = (torch.zeros if accumulate else torch.empty)((M, N), dtype=out_dtype, device=a.device)
     else:
         _need(out, out_dtype, (M, N), "out")
+        _same_device(a, out)
     need = puro_fp8_gemm_workspace_bytes(mode, M, N, K)
     ws_ptr, ws_bytes = None, 0
     if need:
         if workspace is None or workspace.numel() * workspace.element_size() < need:
             workspace = torch.empty(need, dtype=torch.uint8, device=a.device)
+        _same_device(a, workspace)
+        if not workspace.is_contiguous():
+            raise ValueError("workspace: expected a contiguous tensor")
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     _check(puro_fp8_gemm_blockscaled(mode, M, N, K, _ptr(a), _ptr(sa), _ptr(b), _ptr(sb),
                                      _ptr(out), c_dtype, 1 if accumulate else 0, ws_ptr, ws_bytes,
@@ -303,6 +320,9 @@ def gemm_bf16_nt(a, b, out=None, workspace=None, stream=None):
     if need:
         if workspace is None or workspace.numel() * workspace.element_size() < need:
             workspace = torch.empty(need, dtype=torch.uint8, device=a.device)
+        _same_device(a, workspace)
+        if not workspace.is_contiguous():
+            raise ValueError("workspace: expected a contiguous tensor")
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     _check(puro_bf16_gemm_nt(M, N, K, _ptr(a), _ptr(b), _ptr(out), ws_ptr, ws_bytes,
                              _stream(stream)))
