@@ -4,7 +4,7 @@
  * -fsanitize=address,undefined and run by tests/test_oracle_sanitize.py.
  * Any out-of-bounds access, use of uninitialised heap memory through ASan's
  * checks, or undefined behaviour (shifts, overflow, misaligned access) aborts
- * the program.  A few values are also checked, so that a driver that stopped
+ * the program.  A few values are also checked, so that a harness that stopped
  * calling the code would not pass silently.
  *
  * Cases: ragged row counts (1, 129, 300), tiles that are all zero, tiles whose

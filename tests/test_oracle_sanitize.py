@@ -1,5 +1,5 @@
 """The CPU oracle under AddressSanitizer and UndefinedBehaviorSanitizer: a
-driver (tests/pins/oracle_sanitize.c) calls every entry point of
+program (tests/pins/oracle_sanitize.c) calls every entry point of
 oracle/puro_oracle.c on small and edge-case inputs (ragged rows, zero and
 tiny tiles, all three GEMM modes, the neighbour ops); any out-of-bounds
 access or undefined behaviour aborts it.  Built with gcc, run on the CPU."""
@@ -14,7 +14,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc is needed to build the driver")
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc is needed to build the sanitizer program")
 def test_oracle_under_asan_and_ubsan(tmp_path):
     exe = str(tmp_path / "oracle_sanitize")
     subprocess.run(["gcc", "-std=c11", "-O1", "-g", "-fno-omit-frame-pointer",
