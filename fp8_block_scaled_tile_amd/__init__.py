@@ -28,7 +28,8 @@ __all__ = [
     "PuroError", "GEMM_FWD", "GEMM_DGRAD", "GEMM_WGRAD", "OUT_BF16", "OUT_FP32",
     "puro_fp8_quant_act", "puro_fp8_quant_weight", "puro_fp8_gemm_blockscaled",
     "puro_fp8_gemm_workspace_bytes", "puro_fp8_status_string", "puro_fp8_abi_version",
-    "puro_fp8_probe_encode", "quant_act", "quant_weight", "gemm_blockscaled",
+    "puro_fp8_probe_encode", "puro_fp8_probe_sigmoid", "quant_act", "quant_weight",
+    "gemm_blockscaled",
     "puro_bf16_gemm_nt", "puro_bf16_gemm_nt_workspace_bytes", "gemm_bf16_nt",
     "puro_fp8_swiglu_quant", "puro_fp8_swiglu_bwd_quant", "puro_fp8_rmsnorm_quant",
     "swiglu_quant", "swiglu_bwd_quant", "rmsnorm_quant", "library_path",
@@ -79,6 +80,10 @@ def puro_fp8_abi_version() -> int:
 
 def puro_fp8_probe_encode(first_bits, n, out, stream) -> int:
     return _lib.get().puro_fp8_probe_encode(first_bits, n, out, stream)
+
+
+def puro_fp8_probe_sigmoid(first_bits, n, out, stream) -> int:
+    return _lib.get().puro_fp8_probe_sigmoid(first_bits, n, out, stream)
 
 
 def puro_bf16_gemm_nt(M, N, K, a, b, c, workspace, workspace_bytes, stream) -> int:

@@ -16,6 +16,7 @@ EXPORTS = (
     "puro_fp8_gemm_workspace_bytes", "puro_fp8_status_string", "puro_fp8_abi_version",
     "puro_fp8_probe_encode", "puro_bf16_gemm_nt", "puro_bf16_gemm_nt_workspace_bytes",
     "puro_fp8_swiglu_quant", "puro_fp8_swiglu_bwd_quant", "puro_fp8_rmsnorm_quant",
+    "puro_fp8_probe_sigmoid",
 )
 
 
@@ -50,6 +51,8 @@ def get():
         lib.puro_fp8_abi_version.argtypes = []
         lib.puro_fp8_probe_encode.restype = I
         lib.puro_fp8_probe_encode.argtypes = [ctypes.c_uint32, I64, P, P]
+        lib.puro_fp8_probe_sigmoid.restype = I
+        lib.puro_fp8_probe_sigmoid.argtypes = [ctypes.c_uint32, I64, P, P]
         lib.puro_bf16_gemm_nt.restype = I
         lib.puro_bf16_gemm_nt.argtypes = [I64, I64, I64, P, P, P, P, ctypes.c_size_t, P]
         lib.puro_bf16_gemm_nt_workspace_bytes.restype = ctypes.c_size_t

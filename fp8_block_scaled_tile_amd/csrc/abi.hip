@@ -279,6 +279,22 @@ puro_status_t puro_fp8_probe_encode(uint32_t first_bits, int64_t n, uint8_t* out
     });
 }
 
+puro_status_t puro_fp8_probe_sigmoid(uint32_t first_bits, int64_t n, float* out, void* stream)
+{
+    return guarded([&]() -> puro_status_t {
+        if (n < 0)
+            return PURO_ERR_BAD_SHAPE;
+        if (n == 0)
+            return PURO_OK;
+        if (!out)
+            return PURO_ERR_NULL_POINTER;
+        if ((reinterpret_cast<uintptr_t>(out) & 3u) != 0)
+            return PURO_ERR_MISALIGNED;
+        return from_hip(puro::launch_probe_sigmoid(first_bits, n, out,
+                                                   static_cast<hipStream_t>(stream)));
+    });
+}
+
 const char* puro_fp8_status_string(puro_status_t status)
 {
     switch (status) {

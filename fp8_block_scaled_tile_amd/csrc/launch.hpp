@@ -46,6 +46,7 @@ hipError_t launch_rmsnorm_quant(const void* x, const void* gamma, int64_t rows, 
                                 float eps, float* rstd, uint8_t* q, float* s, uint8_t* qt,
                                 float* st, void* y, hipStream_t stream);
 hipError_t launch_probe_encode(uint32_t first, int64_t n, uint8_t* out, hipStream_t stream);
+hipError_t launch_probe_sigmoid(uint32_t first, int64_t n, float* out, hipStream_t stream);
 
 size_t gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* a,

@@ -175,6 +175,16 @@ puro_status_t puro_fp8_probe_encode(uint32_t first_bits, int64_t n, uint8_t* out
                                     void* stream);
 
 /*
+ * Diagnostic: the FP32 sigmoid 1 / (1 + e^-g) that the SwiGLU producers
+ * evaluate (puro_fp8_swiglu_quant, puro_fp8_swiglu_bwd_quant), applied to the
+ * binary32 values whose bit patterns are first_bits, first_bits + 1, ...,
+ * first_bits + n - 1 (wrapping modulo 2^32).  out: f32 [n] device buffer,
+ * 4-byte aligned.  Lets a test hold the device evaluation to its error bound
+ * over whole ranges of inputs.  Requires n >= 0.
+ */
+puro_status_t puro_fp8_probe_sigmoid(uint32_t first_bits, int64_t n, float* out, void* stream);
+
+/*
  * Quantize-on-produce: the BF16 ops next to the FP8 GEMMs, each writing its
  * result straight as FP8 operands (and, optionally, as bf16).
  *

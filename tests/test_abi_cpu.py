@@ -40,7 +40,8 @@ def test_header_declares_the_entry_points():
     for n in ("puro_fp8_quant_act", "puro_fp8_quant_weight", "puro_fp8_gemm_blockscaled",
               "puro_fp8_gemm_workspace_bytes", "puro_fp8_status_string",
               "puro_fp8_abi_version", "puro_fp8_probe_encode", "puro_fp8_swiglu_quant",
-              "puro_fp8_swiglu_bwd_quant", "puro_fp8_rmsnorm_quant", "puro_bf16_gemm_nt"):
+              "puro_fp8_swiglu_bwd_quant", "puro_fp8_rmsnorm_quant", "puro_bf16_gemm_nt",
+              "puro_fp8_probe_sigmoid"):
         assert n in names
 
 
@@ -127,6 +128,10 @@ def test_probe_validation(lib):
     assert lib.puro_fp8_probe_encode(0, -1, P16, None) == SHAPE
     assert lib.puro_fp8_probe_encode(0, 10, None, None) == NULLP
     assert lib.puro_fp8_probe_encode(0, 0, None, None) == OK
+    assert lib.puro_fp8_probe_sigmoid(0, -1, P16, None) == SHAPE
+    assert lib.puro_fp8_probe_sigmoid(0, 10, None, None) == NULLP
+    assert lib.puro_fp8_probe_sigmoid(0, 10, P16 + 2, None) == ALIGN
+    assert lib.puro_fp8_probe_sigmoid(0, 0, None, None) == OK
 
 
 def test_plain_host_consumer_compiles_and_links(tmp_path):
