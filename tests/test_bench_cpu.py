@@ -114,3 +114,11 @@ def test_roofline_classes_are_gemm_classes():
     kernel symbols, so the roofline always names a GEMM kernel."""
     for c in bench.ROOFLINE_CLASSES:
         assert c.startswith("gemm") and c in bench.KERNEL_SYMBOLS
+
+
+def test_vendor_fp8_leg_is_omitted_without_fp8_support():
+    """A torch build without an FP8 dtype or _scaled_mm gives no context leg
+    (None) rather than an error, so the bench line is still printed."""
+    assert bench.fp8_tensorwise_reference(types.SimpleNamespace(), [], 1) is None
+    no_mm = types.SimpleNamespace(float8_e4m3fn=object())
+    assert bench.fp8_tensorwise_reference(no_mm, [], 1) is None
