@@ -295,6 +295,23 @@ puro_status_t puro_fp8_probe_sigmoid(uint32_t first_bits, int64_t n, float* out,
     });
 }
 
+puro_status_t puro_fp8_probe_mfma(int form, const uint8_t* a, const uint8_t* b, int scale_a,
+                                  int scale_b, float* d, void* stream)
+{
+    return guarded([&]() -> puro_status_t {
+        if (form < 0 || form > 5)
+            return PURO_ERR_BAD_ENUM;
+        if (!a || !b || !d)
+            return PURO_ERR_NULL_POINTER;
+        if (!aligned16(a) || !aligned16(b) || !aligned16(d))
+            return PURO_ERR_MISALIGNED;
+        if (scale_a < 0 || scale_a > 255 || scale_b < 0 || scale_b > 255)
+            return PURO_ERR_BAD_VALUE;
+        return from_hip(puro::launch_probe_mfma(form, a, b, scale_a, scale_b, d,
+                                                static_cast<hipStream_t>(stream)));
+    });
+}
+
 const char* puro_fp8_status_string(puro_status_t status)
 {
     switch (status) {

@@ -160,6 +160,18 @@ __device__ __forceinline__ v8bf load_chunk_bf16(const uint8_t* base, int off)
     return __builtin_bit_cast(v8bf, v);
 }
 
+// One 16x16x128 E4M3 x E4M3 product with a zero accumulator input.  The
+// builtin is the scaled form; with its scale operands the compile-time
+// constant 0 the compiler emits the unscaled v_mfma_f32_16x16x128_f8f6f4,
+// i.e. unit scales.  (The scaled instruction reads E8M0 bytes: 127 is 1.0,
+// and a byte of 0 at run time would scale the product by 2^-127 -- pinned,
+// with the emitted form's unit scale, by tests/test_gpu_mfma_accum.py.)
+__device__ __forceinline__ v4f mfma_e4m3(const v8i& x, const v8i& y)
+{
+    const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, zero, 0, 0, 0, 0, 0, 0);
+}
+
 // One K-block (128 deep) staged in LDS: A and B code slices and their scales.
 struct Stage {
     uint8_t a[TILE_BYTES];
@@ -390,8 +402,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
                         for (int r = 0; r < 4; ++r)
                             acc[sm - 1][tn][r] = __builtin_fmaf(p[tn][r], sa_prev[r] * sbn[tn], acc[sm - 1][tn][r]);
                     }
-                    const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-                    p[tn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[tn], zero, 0, 0, 0, 0, 0, 0);
+                    p[tn] = mfma_e4m3(af, bf[tn]);
                 }
                 sa_prev = sa4;
                 if (sm == 0) {
@@ -436,8 +447,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
                         acc[fold_sm][tn][r] = __builtin_fmaf(p[tn][r], sc_prev, acc[fold_sm][tn][r]);
-                    const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-                    p[tn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[tn], af, zero, 0, 0, 0, 0, 0, 0);
+                    p[tn] = mfma_e4m3(bf[tn], af);
                     __builtin_amdgcn_sched_barrier(0);   // MFMAs in tn order
                 }
                 sc_carry = sa * sb_wave;
@@ -645,6 +655,81 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
             *dst = *dst + s;
         }
     }
+}
+
+// Diagnostic: one matrix-core instruction of the given form on raw per-lane
+// operand bytes, with a zero accumulator input.  a, b: u8 [64][32] (lane l's
+// operand bytes at 32*l; the 8-byte forms use the first 8, the bf16 form the
+// first 16); d: f32 [64][16] (lane l's result registers at 16*l, unused
+// slots zero).  One wave.  Lets a test see how each form adds its products.
+//   form 0: v_mfma_f32_16x16x128_f8f6f4 (E4M3 x E4M3), as the GEMM issues it
+//   form 1: v_mfma_f32_32x32x64_f8f6f4  (E4M3 x E4M3)
+//   form 2: v_mfma_f32_16x16x32_fp8_fp8
+//   form 3: v_mfma_f32_32x32x16_fp8_fp8
+//   form 4: v_mfma_f32_16x16x32_bf16
+//   form 5: v_mfma_scale_f32_16x16x128_f8f6f4 with the E8M0 scale bytes
+//           scale_a, scale_b taken from the arguments at run time (opsel 0)
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef long v1l;
+__global__ __launch_bounds__(64) void probe_mfma_kernel(int form, const uint8_t* __restrict__ a,
+                                                        const uint8_t* __restrict__ b, int scale_a,
+                                                        int scale_b, float* __restrict__ d)
+{
+    const int lane = threadIdx.x;
+    const v8i av = *reinterpret_cast<const v8i*>(a + 32 * lane);
+    const v8i bv = *reinterpret_cast<const v8i*>(b + 32 * lane);
+    float out[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        out[i] = 0.0f;
+    const v4f z4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (form == 0 || form == 2 || form == 4 || form == 5) {
+        v4f r = z4;
+        if (form == 0) {
+            r = mfma_e4m3(av, bv);
+        } else if (form == 2) {
+            const long al = (long)(uint32_t)av[0] | ((long)(uint32_t)av[1] << 32);
+            const long bl = (long)(uint32_t)bv[0] | ((long)(uint32_t)bv[1] << 32);
+            r = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(al, bl, z4, 0, 0, 0);
+        } else if (form == 4) {
+            v8bf ab, bb;
+            const uint4 au = {(uint32_t)av[0], (uint32_t)av[1], (uint32_t)av[2], (uint32_t)av[3]};
+            const uint4 bu = {(uint32_t)bv[0], (uint32_t)bv[1], (uint32_t)bv[2], (uint32_t)bv[3]};
+            ab = __builtin_bit_cast(v8bf, au);
+            bb = __builtin_bit_cast(v8bf, bu);
+            r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, bb, z4, 0, 0, 0);
+        } else {
+            r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, z4, 0, 0, 0, scale_a, 0,
+                                                                scale_b);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            out[i] = r[i];
+    } else {
+        const v16f z16 = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f,
+                          0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+        v16f r = z16;
+        if (form == 1) {
+            r = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, z16, 0, 0, 0, 0, 0, 0);
+        } else {
+            const long al = (long)(uint32_t)av[0] | ((long)(uint32_t)av[1] << 32);
+            const long bl = (long)(uint32_t)bv[0] | ((long)(uint32_t)bv[1] << 32);
+            r = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(al, bl, z16, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            out[i] = r[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        d[16 * lane + i] = out[i];
+}
+
+hipError_t launch_probe_mfma(int form, const uint8_t* a, const uint8_t* b, int scale_a,
+                             int scale_b, float* d, hipStream_t stream)
+{
+    return launch_kernel(probe_mfma_kernel, dim3(1), dim3(64), stream, form, a, b, scale_a,
+                         scale_b, d);
 }
 
 // Split-K factor: only when the tile grid leaves most of the 256 CUs idle.

@@ -47,6 +47,8 @@ hipError_t launch_rmsnorm_quant(const void* x, const void* gamma, int64_t rows, 
                                 float* st, void* y, hipStream_t stream);
 hipError_t launch_probe_encode(uint32_t first, int64_t n, uint8_t* out, hipStream_t stream);
 hipError_t launch_probe_sigmoid(uint32_t first, int64_t n, float* out, hipStream_t stream);
+hipError_t launch_probe_mfma(int form, const uint8_t* a, const uint8_t* b, int scale_a,
+                             int scale_b, float* d, hipStream_t stream);
 
 size_t gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* a,

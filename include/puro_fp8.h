@@ -185,6 +185,27 @@ puro_status_t puro_fp8_probe_encode(uint32_t first_bits, int64_t n, uint8_t* out
 puro_status_t puro_fp8_probe_sigmoid(uint32_t first_bits, int64_t n, float* out, void* stream);
 
 /*
+ * Diagnostic: one matrix-core instruction on raw per-lane operand bytes, so
+ * a test can see how each form adds its products (the GEMM's accuracy
+ * depends on it).  One wave of 64 lanes; the accumulator input is zero.
+ *   a, b  u8  [64][32]  lane l's operand bytes at offset 32*l (the 8-byte
+ *                       forms use the first 8 of them, the bf16 form 16)
+ *   d     f32 [64][16]  lane l's result registers at offset 16*l; unused
+ *                       slots are written as 0
+ *   form  0  v_mfma_f32_16x16x128_f8f6f4, E4M3 x E4M3 (the GEMM's form)
+ *         1  v_mfma_f32_32x32x64_f8f6f4,  E4M3 x E4M3
+ *         2  v_mfma_f32_16x16x32_fp8_fp8
+ *         3  v_mfma_f32_32x32x16_fp8_fp8
+ *         4  v_mfma_f32_16x16x32_bf16
+ *         5  v_mfma_scale_f32_16x16x128_f8f6f4 with E8M0 scale bytes scale_a,
+ *            scale_b passed at run time (0 .. 255)
+ * PURO_ERR_BAD_ENUM for another form, PURO_ERR_BAD_VALUE for a scale byte
+ * out of range; pointers 16-byte aligned.
+ */
+puro_status_t puro_fp8_probe_mfma(int form, const uint8_t* a, const uint8_t* b, int scale_a,
+                                  int scale_b, float* d, void* stream);
+
+/*
  * Quantize-on-produce: the BF16 ops next to the FP8 GEMMs, each writing its
  * result straight as FP8 operands (and, optionally, as bf16).
  *

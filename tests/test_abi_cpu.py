@@ -41,7 +41,7 @@ def test_header_declares_the_entry_points():
               "puro_fp8_gemm_workspace_bytes", "puro_fp8_status_string",
               "puro_fp8_abi_version", "puro_fp8_probe_encode", "puro_fp8_swiglu_quant",
               "puro_fp8_swiglu_bwd_quant", "puro_fp8_rmsnorm_quant", "puro_bf16_gemm_nt",
-              "puro_fp8_probe_sigmoid"):
+              "puro_fp8_probe_sigmoid", "puro_fp8_probe_mfma"):
         assert n in names
 
 
@@ -132,6 +132,12 @@ def test_probe_validation(lib):
     assert lib.puro_fp8_probe_sigmoid(0, 10, None, None) == NULLP
     assert lib.puro_fp8_probe_sigmoid(0, 10, P16 + 2, None) == ALIGN
     assert lib.puro_fp8_probe_sigmoid(0, 0, None, None) == OK
+    assert lib.puro_fp8_probe_mfma(6, P16, P16, 0, 0, P16, None) == ENUM
+    assert lib.puro_fp8_probe_mfma(-1, P16, P16, 0, 0, P16, None) == ENUM
+    assert lib.puro_fp8_probe_mfma(0, None, P16, 0, 0, P16, None) == NULLP
+    assert lib.puro_fp8_probe_mfma(0, P16, P16, 0, 0, P16 + 4, None) == ALIGN
+    assert lib.puro_fp8_probe_mfma(5, P16, P16, 256, 0, P16, None) == VALUE
+    assert lib.puro_fp8_probe_mfma(5, P16, P16, 0, -1, P16, None) == VALUE
 
 
 def test_plain_host_consumer_compiles_and_links(tmp_path):
