@@ -28,6 +28,7 @@ __all__ = [
     "PuroError", "GEMM_FWD", "GEMM_DGRAD", "GEMM_WGRAD", "OUT_BF16", "OUT_FP32",
     "puro_fp8_quant_act", "puro_fp8_quant_weight", "puro_fp8_gemm_blockscaled",
     "puro_fp8_gemm_workspace_bytes", "puro_fp8_status_string", "puro_fp8_abi_version",
+    "puro_fp8_gemm_blockscaled_noalloc", "PURO_FP8_NOALLOC_SCRATCH_BYTES",
     "puro_fp8_probe_encode", "puro_fp8_probe_sigmoid", "puro_fp8_probe_mfma", "quant_act", "quant_weight",
     "gemm_blockscaled",
     "puro_bf16_gemm_nt", "puro_bf16_gemm_nt_workspace_bytes", "gemm_bf16_nt",
@@ -37,6 +38,7 @@ __all__ = [
 
 GEMM_FWD, GEMM_DGRAD, GEMM_WGRAD = 0, 1, 2
 OUT_BF16, OUT_FP32 = 0, 1
+PURO_FP8_NOALLOC_SCRATCH_BYTES = 64 << 20
 PURO_OK = 0
 
 
@@ -64,6 +66,12 @@ def puro_fp8_gemm_blockscaled(mode, M, N, K, a, sa, b, sb, c, c_dtype, accumulat
                               workspace_bytes, stream) -> int:
     return _lib.get().puro_fp8_gemm_blockscaled(mode, M, N, K, a, sa, b, sb, c, c_dtype,
                                                 accumulate, workspace, workspace_bytes, stream)
+
+
+def puro_fp8_gemm_blockscaled_noalloc(mode, M, N, K, a, sa, b, sb, c, c_dtype, accumulate,
+                                      stream) -> int:
+    return _lib.get().puro_fp8_gemm_blockscaled_noalloc(mode, M, N, K, a, sa, b, sb, c, c_dtype,
+                                                        accumulate, stream)
 
 
 def puro_fp8_gemm_workspace_bytes(mode, M, N, K) -> int:

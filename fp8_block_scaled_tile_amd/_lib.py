@@ -16,7 +16,7 @@ EXPORTS = (
     "puro_fp8_gemm_workspace_bytes", "puro_fp8_status_string", "puro_fp8_abi_version",
     "puro_fp8_probe_encode", "puro_bf16_gemm_nt", "puro_bf16_gemm_nt_workspace_bytes",
     "puro_fp8_swiglu_quant", "puro_fp8_swiglu_bwd_quant", "puro_fp8_rmsnorm_quant",
-    "puro_fp8_probe_sigmoid", "puro_fp8_probe_mfma",
+    "puro_fp8_probe_sigmoid", "puro_fp8_probe_mfma", "puro_fp8_gemm_blockscaled_noalloc",
 )
 
 
@@ -43,6 +43,8 @@ def get():
         lib.puro_fp8_gemm_blockscaled.restype = I
         lib.puro_fp8_gemm_blockscaled.argtypes = [I, I64, I64, I64, P, P, P, P, P, I, I, P,
                                                   ctypes.c_size_t, P]
+        lib.puro_fp8_gemm_blockscaled_noalloc.restype = I
+        lib.puro_fp8_gemm_blockscaled_noalloc.argtypes = [I, I64, I64, I64, P, P, P, P, P, I, I, P]
         lib.puro_fp8_gemm_workspace_bytes.restype = ctypes.c_size_t
         lib.puro_fp8_gemm_workspace_bytes.argtypes = [I, I64, I64, I64]
         lib.puro_fp8_status_string.restype = ctypes.c_char_p

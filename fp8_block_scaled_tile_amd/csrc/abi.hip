@@ -234,6 +234,35 @@ puro_status_t puro_fp8_gemm_blockscaled(puro_gemm_mode_t mode, int64_t M, int64_
     });
 }
 
+puro_status_t puro_fp8_gemm_blockscaled_noalloc(puro_gemm_mode_t mode, int64_t M, int64_t N,
+                                                int64_t K, const uint8_t* a, const float* sa,
+                                                const uint8_t* b, const float* sb, void* c,
+                                                puro_out_dtype_t c_dtype, int accumulate,
+                                                void* stream)
+{
+    return guarded([&]() -> puro_status_t {
+        if ((int)mode < 0 || (int)mode > 2)
+            return PURO_ERR_BAD_ENUM;
+        if ((int)c_dtype != PURO_OUT_BF16 && (int)c_dtype != PURO_OUT_FP32)
+            return PURO_ERR_BAD_ENUM;
+        if (accumulate && c_dtype != PURO_OUT_FP32)
+            return PURO_ERR_BAD_ENUM;
+        if (!gemm_shape_ok(M, N, K))
+            return PURO_ERR_BAD_SHAPE;
+        if (M == 0)
+            return PURO_OK;
+        if (!a || !sa || !b || !sb || !c)
+            return PURO_ERR_NULL_POINTER;
+        if (!aligned16(a) || !aligned16(sa) || !aligned16(b) || !aligned16(sb) || !aligned16(c))
+            return PURO_ERR_MISALIGNED;
+        if (puro::gemm_workspace_bytes((int)mode, M, N, K) > puro::gemm_noalloc_scratch_bytes())
+            return PURO_ERR_WORKSPACE;
+        return from_hip(puro::launch_gemm_noalloc((int)mode, M, N, K, a, sa, b, sb, c,
+                                                  c_dtype == PURO_OUT_FP32, accumulate ? 1 : 0,
+                                                  static_cast<hipStream_t>(stream)));
+    });
+}
+
 size_t puro_bf16_gemm_nt_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
     if (!bf16_shape_ok(M, N, K) || M == 0)

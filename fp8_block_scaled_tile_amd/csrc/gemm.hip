@@ -41,6 +41,8 @@
 #include "device_common.hpp"
 #include "launch.hpp"
 
+#include <mutex>
+
 namespace puro {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -852,6 +854,73 @@ hipError_t launch_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t*
     case MODE_DGRAD: return launch_mode<MODE_DGRAD>(out, a, sa, b, sb, c, ws, m, n, k, splits, stream);
     default:         return launch_mode<MODE_WGRAD>(out, a, sa, b, sb, c, ws, m, n, k, splits, stream);
     }
+}
+
+// ---- the allocation-free variant: split-K partials in a static device array --
+// Callers that cannot allocate (code under graph capture, tight serving
+// loops) get the split-K workspace from `scratch`, a fixed array that every
+// GPU the library runs on holds until the process ends.  In host code the
+// array's name is only a stand-in: its device address, which differs per
+// GPU, comes from hipGetSymbolAddress, looked up once per device with that
+// device current, and only that address is passed to the kernels.  Every
+// call on one GPU shares the array; each split overwrites its whole plane of
+// partials before the reduce reads it, so nothing needs clearing, and calls
+// that overlap on one GPU (other streams, other threads) race.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on `dev` (looked up on first use).
+hipError_t scratch_address(int dev, void** out)
+{
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        int prev = -1;
+        hipError_t e = hipGetDevice(&prev);
+        if (e != hipSuccess)
+            return e;
+        if (prev != dev && (e = hipSetDevice(dev)) != hipSuccess)
+            return e;
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (prev != dev) {
+            const hipError_t r = hipSetDevice(prev);
+            if (e == hipSuccess)
+                e = r;
+        }
+        if (e != hipSuccess)
+            return e;
+        if (!ptr)
+            return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+}  // namespace
+
+size_t gemm_noalloc_scratch_bytes() { return kNoAllocScratchBytes; }
+
+hipError_t launch_gemm_noalloc(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* a,
+                               const float* sa, const uint8_t* b, const float* sb, void* c,
+                               int out_fp32, int accumulate, hipStream_t stream)
+{
+    void* ws = nullptr;
+    if (gemm_workspace_bytes(mode, M, N, K) > 0) {
+        int dev = 0;
+        hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+        if (e != hipSuccess)
+            return e;
+        if ((e = scratch_address(dev, &ws)) != hipSuccess)
+            return e;
+    }
+    return launch_gemm(mode, M, N, K, a, sa, b, sb, c, out_fp32, accumulate, ws, stream);
 }
 
 }  // namespace puro

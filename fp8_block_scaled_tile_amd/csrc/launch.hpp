@@ -55,6 +55,11 @@ hipError_t launch_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t*
                        const float* sa, const uint8_t* b, const float* sb, void* c, int out_fp32,
                        int accumulate, void* ws, hipStream_t stream);
 
+size_t gemm_noalloc_scratch_bytes();
+hipError_t launch_gemm_noalloc(int mode, int64_t M, int64_t N, int64_t K, const uint8_t* a,
+                               const float* sa, const uint8_t* b, const float* sb, void* c,
+                               int out_fp32, int accumulate, hipStream_t stream);
+
 size_t gemm_bf16_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_bf16_nt(int64_t M, int64_t N, int64_t K, const void* a, const void* b,
                                void* c, void* ws, hipStream_t stream);

@@ -158,6 +158,28 @@ puro_status_t puro_fp8_gemm_blockscaled(puro_gemm_mode_t mode, int64_t M, int64_
 size_t puro_fp8_gemm_workspace_bytes(puro_gemm_mode_t mode, int64_t M, int64_t N,
                                      int64_t K);
 
+/*
+ * Block-scaled FP8 GEMM that allocates nothing, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, layouts, results and
+ * errors as puro_fp8_gemm_blockscaled, without the workspace: when the
+ * problem splits K across work-groups, the FP32 partials go to a static
+ * device array of PURO_FP8_NOALLOC_SCRATCH_BYTES that each GPU the library
+ * runs on holds until the process ends.  Problems whose
+ * puro_fp8_gemm_workspace_bytes exceeds that size return PURO_ERR_WORKSPACE
+ * before anything is enqueued.  The first call on a device looks up the
+ * array's address on that device (hipGetSymbolAddress); no call allocates or
+ * frees memory.  Every call on one GPU shares the array: calls that overlap
+ * on one GPU (on other streams or from other threads) race and must be
+ * serialized by the caller.
+ */
+#define PURO_FP8_NOALLOC_SCRATCH_BYTES (64u << 20)
+puro_status_t puro_fp8_gemm_blockscaled_noalloc(puro_gemm_mode_t mode, int64_t M, int64_t N,
+                                                int64_t K, const uint8_t* a, const float* sa,
+                                                const uint8_t* b, const float* sb, void* c,
+                                                puro_out_dtype_t c_dtype, int accumulate,
+                                                void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* puro_fp8_status_string(puro_status_t status);
 

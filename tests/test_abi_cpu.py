@@ -41,7 +41,8 @@ def test_header_declares_the_entry_points():
               "puro_fp8_gemm_workspace_bytes", "puro_fp8_status_string",
               "puro_fp8_abi_version", "puro_fp8_probe_encode", "puro_fp8_swiglu_quant",
               "puro_fp8_swiglu_bwd_quant", "puro_fp8_rmsnorm_quant", "puro_bf16_gemm_nt",
-              "puro_fp8_probe_sigmoid", "puro_fp8_probe_mfma"):
+              "puro_fp8_probe_sigmoid", "puro_fp8_probe_mfma",
+              "puro_fp8_gemm_blockscaled_noalloc"):
         assert n in names
 
 
@@ -122,6 +123,24 @@ def test_workspace_query(lib):
     assert q(2, 2048, 2048, 32768) % (2048 * 2048 * 4) == 0
     assert q(0, 256, 100, 256) == 0                        # invalid shape -> 0
     assert q(5, 256, 256, 256) == 0
+
+
+def test_noalloc_gemm_validation(lib):
+    """The allocation-free GEMM refuses bad arguments, and problems whose
+    split-K partials exceed its static array, before touching a device."""
+    f = lib.puro_fp8_gemm_blockscaled_noalloc
+    assert f(3, 256, 256, 256, P16, P16, P16, P16, P16, 0, 0, None) == ENUM
+    assert f(0, 256, 256, 256, P16, P16, P16, P16, P16, 0, 1, None) == ENUM      # += needs FP32
+    assert f(0, 256, 200, 256, P16, P16, P16, P16, P16, 0, 0, None) == SHAPE
+    assert f(0, 0, 256, 256, None, None, None, None, None, 0, 0, None) == OK
+    assert f(0, 256, 256, 256, None, P16, P16, P16, P16, 0, 0, None) == NULLP
+    assert f(0, 256, 256, 256, P16 + 8, P16, P16, P16, P16, 0, 0, None) == ALIGN
+    big = lib.puro_fp8_gemm_workspace_bytes(2, 2560, 2560, 8192)
+    assert big > lib.PURO_FP8_NOALLOC_SCRATCH_BYTES
+    assert f(2, 2560, 2560, 8192, P16, P16, P16, P16, P16, 1, 0, None) == WS
+    header = open(HEADER).read()
+    assert "#define PURO_FP8_NOALLOC_SCRATCH_BYTES (64u << 20)" in header
+    assert lib.PURO_FP8_NOALLOC_SCRATCH_BYTES == 64 << 20
 
 
 def test_probe_validation(lib):
