@@ -25,7 +25,7 @@ import os
 from . import _lib
 
 __all__ = [
-    "PuroError", "GEMM_FWD", "GEMM_DGRAD", "GEMM_WGRAD", "OUT_BF16", "OUT_FP32",
+    "PuroError", "GEMM_FWD", "GEMM_DGRAD", "GEMM_WGRAD", "GEMM_DGRAD_W", "OUT_BF16", "OUT_FP32",
     "puro_fp8_quant_act", "puro_fp8_quant_weight", "puro_fp8_gemm_blockscaled",
     "puro_fp8_gemm_workspace_bytes", "puro_fp8_status_string", "puro_fp8_abi_version",
     "puro_fp8_gemm_blockscaled_noalloc", "PURO_FP8_NOALLOC_SCRATCH_BYTES",
@@ -36,7 +36,7 @@ __all__ = [
     "swiglu_quant", "swiglu_bwd_quant", "rmsnorm_quant", "library_path",
 ]
 
-GEMM_FWD, GEMM_DGRAD, GEMM_WGRAD = 0, 1, 2
+GEMM_FWD, GEMM_DGRAD, GEMM_WGRAD, GEMM_DGRAD_W = 0, 1, 2, 3
 OUT_BF16, OUT_FP32 = 0, 1
 PURO_FP8_NOALLOC_SCRATCH_BYTES = 64 << 20
 PURO_OK = 0
@@ -279,22 +279,22 @@ def gemm_blockscaled(mode: int, a, sa, b, sb, out_dtype=None, out=None, accumula
     """Block-scaled FP8 GEMM: C[M, N] (+)= blocks of a[M, K] . b[N, K]^T with
     scales sa [K/128, M] and sb (see the C header for each mode's layout)."""
     torch = _torch()
-    if mode not in (GEMM_FWD, GEMM_DGRAD, GEMM_WGRAD):
+    if mode not in (GEMM_FWD, GEMM_DGRAD, GEMM_WGRAD, GEMM_DGRAD_W):
         raise ValueError(f"unknown GEMM mode {mode}")
     if a.dim() != 2 or b.dim() != 2:
         raise ValueError("a and b must be 2-D")
     M, K = a.shape
-    N = b.shape[0]
+    N = b.shape[1] if mode == GEMM_DGRAD_W else b.shape[0]
     if out_dtype is None:
         out_dtype = out.dtype if out is not None else torch.bfloat16
     c_dtype = OUT_FP32 if out_dtype == torch.float32 else OUT_BF16
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("out_dtype must be bfloat16 or float32")
     _need(a, torch.uint8, (M, K), "a")
-    _need(b, torch.uint8, (N, K), "b")
+    _need(b, torch.uint8, (K, N) if mode == GEMM_DGRAD_W else (N, K), "b")
     _need(sa, torch.float32, (K // 128, M), "sa")
     sb_shape = {GEMM_FWD: (N // 128, K // 128), GEMM_DGRAD: (K // 128, N // 128),
-                GEMM_WGRAD: (K // 128, N)}[mode]
+                GEMM_DGRAD_W: (K // 128, N // 128), GEMM_WGRAD: (K // 128, N)}[mode]
     _need(sb, torch.float32, sb_shape, "sb")
     _same_device(a, sa, b, sb)
     if out is None:

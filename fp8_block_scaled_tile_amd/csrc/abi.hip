@@ -15,6 +15,9 @@ constexpr int64_t kMaxDim = std::numeric_limits<int32_t>::max();
 // The GEMM addresses a row of a 256-row tile with a 32-bit offset
 // row * K + k from the tile's 64-bit base, so K is limited to 2^24.
 constexpr int64_t kMaxGemmK = int64_t(1) << 24;
+// DGRAD_W stages four weight rows per copy with a 32-bit lane offset
+// (row * N + column < 4 N).
+constexpr int64_t kMaxDgradWN = int64_t(1) << 29;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -195,7 +198,7 @@ puro_status_t puro_fp8_rmsnorm_quant(const void* x, const void* gamma, int64_t r
 
 size_t puro_fp8_gemm_workspace_bytes(puro_gemm_mode_t mode, int64_t M, int64_t N, int64_t K)
 {
-    if ((int)mode < 0 || (int)mode > 2 || !gemm_shape_ok(M, N, K) || M == 0)
+    if ((int)mode < 0 || (int)mode > 3 || !gemm_shape_ok(M, N, K) || M == 0)
         return 0;
     return puro::gemm_workspace_bytes((int)mode, M, N, K);
 }
@@ -207,13 +210,13 @@ puro_status_t puro_fp8_gemm_blockscaled(puro_gemm_mode_t mode, int64_t M, int64_
                                         void* stream)
 {
     return guarded([&]() -> puro_status_t {
-        if ((int)mode < 0 || (int)mode > 2)
+        if ((int)mode < 0 || (int)mode > 3)
             return PURO_ERR_BAD_ENUM;
         if ((int)c_dtype != PURO_OUT_BF16 && (int)c_dtype != PURO_OUT_FP32)
             return PURO_ERR_BAD_ENUM;
         if (accumulate && c_dtype != PURO_OUT_FP32)
             return PURO_ERR_BAD_ENUM;
-        if (!gemm_shape_ok(M, N, K))
+        if (!gemm_shape_ok(M, N, K) || (mode == PURO_GEMM_DGRAD_W && N > kMaxDgradWN))
             return PURO_ERR_BAD_SHAPE;
         if (M == 0)
             return PURO_OK;
@@ -241,13 +244,13 @@ puro_status_t puro_fp8_gemm_blockscaled_noalloc(puro_gemm_mode_t mode, int64_t M
                                                 void* stream)
 {
     return guarded([&]() -> puro_status_t {
-        if ((int)mode < 0 || (int)mode > 2)
+        if ((int)mode < 0 || (int)mode > 3)
             return PURO_ERR_BAD_ENUM;
         if ((int)c_dtype != PURO_OUT_BF16 && (int)c_dtype != PURO_OUT_FP32)
             return PURO_ERR_BAD_ENUM;
         if (accumulate && c_dtype != PURO_OUT_FP32)
             return PURO_ERR_BAD_ENUM;
-        if (!gemm_shape_ok(M, N, K))
+        if (!gemm_shape_ok(M, N, K) || (mode == PURO_GEMM_DGRAD_W && N > kMaxDgradWN))
             return PURO_ERR_BAD_SHAPE;
         if (M == 0)
             return PURO_OK;

@@ -70,7 +70,11 @@ constexpr int GROUP_M = 4;
 // MODE_BF16 is the BF16 comparator: C = A . B^T on bf16 operands with the
 // same tiling, staging and schedule, no block scales.  K is passed in bytes
 // (2 per element), so a 128-byte K-block holds 64 bf16 values.
-enum { MODE_FWD = 0, MODE_DGRAD = 1, MODE_WGRAD = 2, MODE_BF16 = 3 };
+// MODE_DGRAD_W is DGRAD with B read straight from the weight's codes
+// W [K = out][N = in] (N-contiguous) instead of their transposed copy: the
+// K-block's 128 weight rows are staged as they lie and the B fragments are
+// read with the gfx950 LDS transpose read (ds_read_b64_tr_b8).
+enum { MODE_FWD = 0, MODE_DGRAD = 1, MODE_WGRAD = 2, MODE_BF16 = 3, MODE_DGRAD_W = 4 };
 enum { OUT_BF16 = 0, OUT_FP32 = 1, OUT_FP32_ACC = 2, OUT_PARTIAL = 3 };
 
 // LDS rows are 128 bytes (one K-block of one row).  The 16-byte chunk c of
@@ -131,6 +135,50 @@ __device__ __forceinline__ FragOff frag_off_b(int lane)
     const int r = 8 * (i >> 2) + (i & 3);
     const int c0 = 2 * (lane >> 4);
     return {r * BK + ((c0 ^ swz_b(r)) << 4), r * BK + (((c0 + 1) ^ swz_b(r)) << 4)};
+}
+
+// MODE_DGRAD_W: the staged B slice is 128 weight rows (k) of 256 bytes (the
+// tile's 256 columns n).  The 16-byte unit u of row r is stored at unit
+// position u ^ swz_w(r).  A transpose read (below) has its 32 lanes of one
+// pass read one 16-byte unit in each of 16 rows r = 32*g + 8*j + m (g = 0, 1;
+// m = 0..7); the mask gives those 16 rows 16 distinct unit positions, so the
+// pass touches every bank once.  The staging copies are linear in LDS.
+__device__ __forceinline__ int swz_w(int row) { return (row & 7) | (((row >> 5) & 1) << 3); }
+
+// ds_read_b64_tr_b8 on gfx950 (measured): within each 16-lane group, input
+// lane 2*m + p supplies an 8-byte chunk and output lane t receives byte
+// (t & 7) of the chunks of input lanes (t >> 3) + 2*m, m = 0..7, as its
+// bytes m.  So if input lanes 2m and 2m+1 address columns c..c+7 and
+// c+8..c+15 of weight row k0 + m, output lane t holds rows k0..k0+7 of column
+// c + t: 8 consecutive k of one n.  Read j (0..3) of lane group g takes
+// k0 = 32*g + 8*j, giving the lane bytes 8j..8j+7 of the MFMA fragment with
+// k = 32*g .. 32*g+31 -- the A fragments' k <-> (lane, byte) mapping.  The
+// fragment's 16 rows are the 16 consecutive columns 16*tn .. 16*tn+15 of the
+// wave's 64.  Returns the lane's LDS byte offset for read j of tile tn
+// (wn = the wave's column quarter).
+__device__ __forceinline__ int frag_off_w(int lane, int wn, int tn, int j)
+{
+    const int g = lane >> 4;
+    const int m = (lane & 15) >> 1;
+    const int p = lane & 1;
+    const int r = 32 * g + 8 * j + m;
+    return r * 256 + (((4 * wn + tn) ^ swz_w(r)) << 4) + 8 * p;
+}
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i lds_v2i;
+
+__device__ __forceinline__ v8i load_frag_w(const uint8_t* base, int off0, int off1, int off2,
+                                           int off3)
+{
+    const v2i r0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(base + off0));
+    const v2i r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(base + off1));
+    const v2i r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(base + off2));
+    const v2i r3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(base + off3));
+    v8i f;
+    f[0] = r0[0]; f[1] = r0[1]; f[2] = r1[0]; f[3] = r1[1];
+    f[4] = r2[0]; f[5] = r2[1]; f[6] = r3[0]; f[7] = r3[1];
+    return f;
 }
 
 // `base` is an LDS array and `off` the slice's byte offset in it; each read
@@ -211,17 +259,34 @@ __device__ __forceinline__ void issue_stage(Stage& st, const uint8_t* At, const 
                                             int KB, int wave, int lane)
 {
     const uint8_t* ab = uniform_ptr(At + (size_t)kb * BK);
-    const uint8_t* bb = uniform_ptr(Bt + (size_t)kb * BK);
     const int r0 = 32 * wave + (lane >> 3);
+    if constexpr (MODE == MODE_DGRAD_W) {
+        // B = the weight's rows kb*128 .. +127, columns n0 .. n0+255 (N-contiguous,
+        // N = the row pitch); each wave copies 16 rows, lane L of instruction i
+        // fills row 16*wave + 4*i + L/16 at unit position L % 16.  Columns past N
+        // (a half tile) read the row's last 16 bytes instead (never stored).
+        const uint8_t* wb = uniform_ptr(Bt + (size_t)kb * BK * (size_t)N);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * wave + 4 * i + (lane >> 4);
+            const int col = min(n0 + 16 * ((lane & 15) ^ swz_w(row)), N - 16);
+            const uint8_t* rb = uniform_ptr(wb + (size_t)(16 * wave + 4 * i) * (size_t)N);
+            const uint32_t bo = (uint32_t)(lane >> 4) * (uint32_t)N + (uint32_t)col;
+            __builtin_amdgcn_global_load_lds(rb + bo, (lds_void*)(st.b + (16 * wave + 4 * i) * 256), 16, 0, 0);
+        }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int row = r0 + 8 * i;
         const uint32_t ca = 16u * (uint32_t)((lane & 7) ^ swz(row));
-        const uint32_t cb = 16u * (uint32_t)((lane & 7) ^ swz_stage_b<MODE>(row));
         const uint32_t ao = (uint32_t)min(row, rows_a - 1) * (uint32_t)K + ca;
-        const uint32_t bo = (uint32_t)min(row, rows_b - 1) * (uint32_t)K + cb;
         __builtin_amdgcn_global_load_lds(ab + ao, (lds_void*)(st.a + (32 * wave + 8 * i) * BK), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(bb + bo, (lds_void*)(st.b + (32 * wave + 8 * i) * BK), 16, 0, 0);
+        if constexpr (MODE != MODE_DGRAD_W) {
+            const uint8_t* bb = uniform_ptr(Bt + (size_t)kb * BK);
+            const uint32_t cb = 16u * (uint32_t)((lane & 7) ^ swz_stage_b<MODE>(row));
+            const uint32_t bo = (uint32_t)min(row, rows_b - 1) * (uint32_t)K + cb;
+            __builtin_amdgcn_global_load_lds(bb + bo, (lds_void*)(st.b + (32 * wave + 8 * i) * BK), 16, 0, 0);
+        }
     }
     if constexpr (MODE == MODE_BF16)
         return;                                  // no block scales
@@ -317,6 +382,12 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
     // K-block and one float4 of sA per tile.
     const FragOff fo = frag_off(lane);
     const FragOff fob = (MODE == MODE_WGRAD) ? fo : frag_off_b(lane);
+    // MODE_DGRAD_W: per tile, the lane's offset of transpose read j = 0 (read
+    // j adds 8 weight rows, 2048 bytes)
+    int fow[TN];
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+        fow[tn] = frag_off_w(lane, wn, tn, 0);
     const int a_off = wm * WM * BK;    // this wave's 128 A rows
     const int b_off = wn * WN * BK;    // this wave's 64 B rows
     v4f p[TN];
@@ -427,7 +498,11 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
 #pragma unroll
             for (int tn = 0; tn < TN; ++tn) {
                 __builtin_amdgcn_sched_barrier(0);
-                bf[tn] = load_frag(st.b, b_off + b_tile_rows(tn) * BK, fob);
+                if constexpr (MODE == MODE_DGRAD_W)
+                    bf[tn] = load_frag_w(st.b, fow[tn], fow[tn] + 2048, fow[tn] + 4096,
+                                         fow[tn] + 6144);
+                else
+                    bf[tn] = load_frag(st.b, b_off + b_tile_rows(tn) * BK, fob);
             }
             __builtin_amdgcn_sched_barrier(0);
             const float sb_wave = st.sb[(wn * WN) / BK];
@@ -491,7 +566,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
         }
     };
     auto epilogue = [&](const Unit& t) __attribute__((always_inline)) {
-        if constexpr (MODE == MODE_FWD || MODE == MODE_DGRAD)
+        if constexpr (MODE == MODE_FWD || MODE == MODE_DGRAD || MODE == MODE_DGRAD_W)
             fold_row(TM - 1, sc_carry);               // the unit's last row
         if ((t.n0 + wn * WN) >= N)
             return;
@@ -510,6 +585,47 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
                             store1((size_t)m * N + n_lane + 16 * tn, t.split, acc[sm][tn][r]);
                     }
                 }
+        } else if constexpr (MODE == MODE_DGRAD_W) {
+            // lane: row m = m_lane + 16*sm; columns n_lane + 16*tn + r (the
+            // fragments' natural column order, g = lane >> 4).  FP32: one
+            // 16-byte store per tile.  bf16: lane groups g and g ^ 1 (lanes l
+            // and l ^ 16, the same row) trade halves of tiles 2q and 2q + 1,
+            // so an even group holds columns 16*(2q) + 4g .. +7 and an odd one
+            // 16*(2q+1) + 4g - 4 .. +7; across the four groups that is 64
+            // contiguous bytes of the row per tile pair, one 16-byte store per
+            // lane, as in the other modes.
+            const int g = lane >> 4;
+            const bool odd = (g & 1) != 0;
+            const int m_lane = t.m0 + wm * WM + (lane & 15);
+            const int n_lane = t.n0 + wn * WN + 4 * g;
+#pragma unroll
+            for (int sm = 0; sm < TM; ++sm) {
+                const int m = m_lane + 16 * sm;
+                if (m >= M)
+                    continue;                  // lanes l and l ^ 16 share m
+                const size_t idx = (size_t)m * N + n_lane;
+                if constexpr (OUT == OUT_BF16) {
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        const int ta = 2 * q, tb = 2 * q + 1;
+                        const uint32_t a0 = pack_bf16(acc[sm][ta][0], acc[sm][ta][1]);
+                        const uint32_t a1 = pack_bf16(acc[sm][ta][2], acc[sm][ta][3]);
+                        const uint32_t b0 = pack_bf16(acc[sm][tb][0], acc[sm][tb][1]);
+                        const uint32_t b1 = pack_bf16(acc[sm][tb][2], acc[sm][tb][3]);
+                        // swizzle pattern: lane ^ 16 within each half wave
+                        const uint32_t y0 = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(odd ? a0 : b0), 0x401F);
+                        const uint32_t y1 = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(odd ? a1 : b1), 0x401F);
+                        const v4u w = odd ? v4u{y0, y1, b0, b1} : v4u{a0, a1, y0, y1};
+                        const size_t col = odd ? idx + 16 * tb - 4 : idx + 16 * ta;
+                        __builtin_nontemporal_store(
+                            w, reinterpret_cast<v4u*>(static_cast<uint16_t*>(C) + col));
+                    }
+                } else {
+#pragma unroll
+                    for (int tn = 0; tn < TN; ++tn)
+                        store4(idx + 16 * tn, t.split, acc[sm][tn]);
+                }
+            }
         } else {
             // lane: row m = m_lane + 16*sm; columns n_lane + b_tile_rows(tn) + r,
             // i.e. 8 consecutive columns from tiles 0, 1 and 8 more, 32 columns
@@ -569,7 +685,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
     // first block is already in LDS when the last block of a unit is done.
     auto issue = [&](Stage& st, const Unit& t, int kb) __attribute__((always_inline)) {
         const uint8_t* At = A + (size_t)t.m0 * K;
-        const uint8_t* Bt = B + (size_t)t.n0 * K;
+        const uint8_t* Bt = (MODE == MODE_DGRAD_W) ? B : B + (size_t)t.n0 * K;
         issue_stage<MODE>(st, At, SA, Bt, SB, kb, t.m0, t.n0, min(M - t.m0, BM),
                           min(N - t.n0, BN), M, N, K, KB, wave, lane);
     };
@@ -852,6 +968,8 @@ hipError_t launch_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t*
     switch (mode) {
     case MODE_FWD:   return launch_mode<MODE_FWD>(out, a, sa, b, sb, c, ws, m, n, k, splits, stream);
     case MODE_DGRAD: return launch_mode<MODE_DGRAD>(out, a, sa, b, sb, c, ws, m, n, k, splits, stream);
+    case 3:          // the C ABI's PURO_GEMM_DGRAD_W
+        return launch_mode<MODE_DGRAD_W>(out, a, sa, b, sb, c, ws, m, n, k, splits, stream);
     default:         return launch_mode<MODE_WGRAD>(out, a, sa, b, sb, c, ws, m, n, k, splits, stream);
     }
 }

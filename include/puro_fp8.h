@@ -66,9 +66,11 @@ typedef enum {
 } puro_status_t;
 
 typedef enum {
-    PURO_GEMM_FWD = 0,   /* Y  = X . W^T   : M = tokens, N = out, K = in      */
-    PURO_GEMM_DGRAD = 1, /* dX = dY . W    : M = tokens, N = in,  K = out     */
-    PURO_GEMM_WGRAD = 2  /* dW = dY^T . X  : M = out,    N = in,  K = tokens  */
+    PURO_GEMM_FWD = 0,    /* Y  = X . W^T   : M = tokens, N = out, K = in     */
+    PURO_GEMM_DGRAD = 1,  /* dX = dY . W    : M = tokens, N = in,  K = out    */
+    PURO_GEMM_WGRAD = 2,  /* dW = dY^T . X  : M = out,    N = in,  K = tokens */
+    PURO_GEMM_DGRAD_W = 3 /* dX = dY . W as DGRAD, with b the weight's own
+                             codes W [out][in] = [K][N] (no transposed copy)  */
 } puro_gemm_mode_t;
 
 typedef enum {
@@ -124,16 +126,22 @@ puro_status_t puro_fp8_quant_weight(const void* w, int64_t n, int64_t k,
  *
  *   a   u8  [M][K]   E4M3 codes, K-contiguous
  *   sa  f32 [K/128][M]
- *   b   u8  [N][K]   E4M3 codes, K-contiguous
- *   sb  f32 FWD   [N/128][K/128]   (the weight's block scales)
- *           DGRAD [K/128][N/128]   (the weight's block scales as stored for
+ *   b   u8  [N][K]   E4M3 codes, K-contiguous (DGRAD_W: [K][N], N-contiguous)
+ *   sb  f32 FWD     [N/128][K/128] (the weight's block scales)
+ *           DGRAD   [K/128][N/128] (the weight's block scales as stored for
  *                                   W [K][N]; b is the transposed code copy)
- *           WGRAD [K/128][N]       (per-column 128x1 scales)
+ *           DGRAD_W [K/128][N/128] (the same scales; b is W's codes as the
+ *                                   weight quantizer writes them)
+ *           WGRAD   [K/128][N]     (per-column 128x1 scales)
  *   c   bf16 or f32 [M][N] according to c_dtype
  *
  * How a linear layer with W [out][in] and T tokens maps onto the modes:
  *   FWD:   a = q(X) [T][in],   sa = s(X),  b = q(W) [out][in],  sb = s(W)
  *   DGRAD: a = q(dY) [T][out], sa = s(dY), b = qt(W) [in][out], sb = s(W)
+ *   DGRAD_W: a = q(dY), sa = s(dY), b = q(W) [out][in], sb = s(W); the
+ *          weight quantizer's transposed copy is then not needed (qt = NULL).
+ *          The result equals DGRAD's (the same products); requires
+ *          N <= 2^29 (N = in).
  *   WGRAD: a = qt(dY) [out][T_pad], sa = st(dY), b = qt(X) [in][T_pad],
  *          sb = st(X)
  *

@@ -95,8 +95,10 @@ def test_gemm_validation(lib):
         return f(d["mode"], d["M"], d["N"], d["K"], d["a"], d["sa"], d["b"], d["sb"], d["c"],
                  d["c_dtype"], d["acc"], d["ws"], d["wsb"], None)
 
-    assert call(mode=3) == ENUM
+    assert call(mode=4) == ENUM
     assert call(mode=-1) == ENUM
+    assert call(mode=3, N=(1 << 29) + 128) == SHAPE          # DGRAD_W: N <= 2^29
+    assert call(mode=3, a=None) == NULLP
     assert call(c_dtype=2) == ENUM
     assert call(acc=1, c_dtype=0) == ENUM                  # accumulate needs FP32
     assert call(N=200) == SHAPE
@@ -123,13 +125,14 @@ def test_workspace_query(lib):
     assert q(2, 2048, 2048, 32768) % (2048 * 2048 * 4) == 0
     assert q(0, 256, 100, 256) == 0                        # invalid shape -> 0
     assert q(5, 256, 256, 256) == 0
+    assert q(3, 256, 256, 4096) == q(1, 256, 256, 4096) > 0     # DGRAD_W splits as DGRAD
 
 
 def test_noalloc_gemm_validation(lib):
     """The allocation-free GEMM refuses bad arguments, and problems whose
     split-K partials exceed its static array, before touching a device."""
     f = lib.puro_fp8_gemm_blockscaled_noalloc
-    assert f(3, 256, 256, 256, P16, P16, P16, P16, P16, 0, 0, None) == ENUM
+    assert f(4, 256, 256, 256, P16, P16, P16, P16, P16, 0, 0, None) == ENUM
     assert f(0, 256, 256, 256, P16, P16, P16, P16, P16, 0, 1, None) == ENUM      # += needs FP32
     assert f(0, 256, 200, 256, P16, P16, P16, P16, P16, 0, 0, None) == SHAPE
     assert f(0, 0, 256, 256, None, None, None, None, None, 0, 0, None) == OK

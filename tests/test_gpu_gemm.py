@@ -19,7 +19,7 @@ from parity import bf16_host_bits, dev, fmt, gemm_gates, host, random_bf16, say
 
 pytestmark = pytest.mark.gpu
 
-FWD, DGRAD, WGRAD = 0, 1, 2
+FWD, DGRAD, WGRAD, DGRAD_W = 0, 1, 2, 3
 
 
 @pytest.fixture(scope="module")
@@ -42,6 +42,10 @@ def device_operands(pf, mode, x, w, dy):
         qa = pf.quant_act(dev(dy), row=True)
         qw = pf.quant_weight(dev(w), transpose=True)
         return qa["q"], qa["s"], qw["qt"], qw["s"]
+    if mode == DGRAD_W:                  # the weight's own codes, no transposed copy
+        qa = pf.quant_act(dev(dy), row=True)
+        qw = pf.quant_weight(dev(w), transpose=False)
+        return qa["q"], qa["s"], qw["q"], qw["s"]
     qa = pf.quant_act(dev(dy), row=False, col=True)
     qb = pf.quant_act(dev(x), row=False, col=True)
     return qa["qt"], qa["st"], qb["qt"], qb["st"]
@@ -52,7 +56,7 @@ def oracle_operands(mode, x, w, dy):
         qa, sa = oracle.quant_rowwise(synth.bits(x))
         qw, _, sw = oracle.quant_weight(synth.bits(w), transpose=False)
         return qa, sa, qw, sw
-    if mode == DGRAD:
+    if mode in (DGRAD, DGRAD_W):        # DGRAD_W computes DGRAD's products
         qa, sa = oracle.quant_rowwise(synth.bits(dy))
         _, qwt, sw = oracle.quant_weight(synth.bits(w), transpose=True)
         return qa, sa, qwt, sw
@@ -71,10 +75,10 @@ def make_inputs(T, d_in, d_out, seed):
 
 def run_case(pf, mode, T, d_in, d_out, out_dtype, seed=0, accumulate=False):
     x, w, dy = make_inputs(T, d_in, d_out, seed)
-    say("gemm", ["fwd", "dgrad", "wgrad"][mode], f"T={T} in={d_in} out={d_out}", out_dtype,
+    say("gemm", MODE_NAMES[mode], f"T={T} in={d_in} out={d_out}", out_dtype,
         "acc" if accumulate else "")
     a, sa, b, sb = device_operands(pf, mode, x, w, dy)
-    M, N = a.shape[0], b.shape[0]
+    M, N = a.shape[0], (b.shape[1] if mode == DGRAD_W else b.shape[0])
     c0 = None
     out = None
     if accumulate:
@@ -83,10 +87,12 @@ def run_case(pf, mode, T, d_in, d_out, out_dtype, seed=0, accumulate=False):
     c = pf.gemm_blockscaled(mode, a, sa, b, sb, out_dtype=out_dtype, out=out,
                             accumulate=accumulate)
     oa, osa, ob, osb = oracle_operands(mode, x, w, dy)
-    assert np.array_equal(host(a), oa) and np.array_equal(host(b), ob)
-    ref = oracle.gemm_blockscaled(mode, oa, osa, ob, osb)
+    omode = DGRAD if mode == DGRAD_W else mode
+    assert np.array_equal(host(a), oa)
+    assert np.array_equal(host(b).T if mode == DGRAD_W else host(b), ob)
+    ref = oracle.gemm_blockscaled(omode, oa, osa, ob, osb)
     ii, jj = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
-    bound = hw_accum.bounds(mode, oa, osa, ob, osb, ii.ravel(), jj.ravel(), ref.ravel())
+    bound = hw_accum.bounds(omode, oa, osa, ob, osb, ii.ravel(), jj.ravel(), ref.ravel())
     if accumulate:
         ref = (c0.numpy() + ref).astype(np.float32)
         extra = 2.0 ** -22 * np.abs(ref.ravel())             # the final read-add-write
@@ -97,6 +103,9 @@ def run_case(pf, mode, T, d_in, d_out, out_dtype, seed=0, accumulate=False):
     say("   " + fmt(g))
     assert g["ok"], g
     return g
+
+
+MODE_NAMES = {FWD: "fwd", DGRAD: "dgrad", WGRAD: "wgrad", DGRAD_W: "dgrad_w"}
 
 
 def device_values(c):
@@ -133,18 +142,34 @@ def test_wgrad_small(pf, T, d_in, d_out):
     run_case(pf, WGRAD, T, d_in, d_out, torch.float32, accumulate=True)
 
 
-@pytest.mark.parametrize("mode", [FWD, DGRAD, WGRAD])
+@pytest.mark.parametrize("T,d_in,d_out", SMALL)
+def test_dgrad_from_weight_codes_small(pf, T, d_in, d_out):
+    """DGRAD_W reads the weight's own codes W [out][in] through LDS transpose
+    reads: the oracle's gates, and bit for bit the DGRAD result on the
+    transposed copy (the fragments pair the same k in the same order)."""
+    for dt in (torch.float32, torch.bfloat16):
+        run_case(pf, DGRAD_W, T, d_in, d_out, dt)
+    x, w, dy = make_inputs(T, d_in, d_out, 0)
+    a, sa, bt, sb = device_operands(pf, DGRAD, x, w, dy)
+    _, _, bw, _ = device_operands(pf, DGRAD_W, x, w, dy)
+    for dt in (torch.float32, torch.bfloat16):
+        c1 = pf.gemm_blockscaled(DGRAD, a, sa, bt, sb, out_dtype=dt)
+        c2 = pf.gemm_blockscaled(DGRAD_W, a, sa, bw, sb, out_dtype=dt)
+        assert torch.equal(c1, c2)
+
+
+@pytest.mark.parametrize("mode", [FWD, DGRAD, WGRAD, DGRAD_W])
 def test_split_k_paths(pf, mode):
     """Few output tiles and a long K: the K range is split across work-groups
     and reduced in a second kernel (FP32 and bf16 outputs, accumulate)."""
     T, d_in, d_out = (2048, 256, 256) if mode != WGRAD else (4096, 256, 256)
     if mode == FWD:
         T, d_in, d_out = 256, 2048, 256
-    elif mode == DGRAD:
+    elif mode in (DGRAD, DGRAD_W):
         T, d_in, d_out = 256, 256, 2048
     M = T if mode != WGRAD else d_out
     N = d_out if mode == FWD else d_in
-    K = d_in if mode == FWD else (d_out if mode == DGRAD else T)
+    K = d_in if mode == FWD else (d_out if mode in (DGRAD, DGRAD_W) else T)
     assert pf.puro_fp8_gemm_workspace_bytes(mode, M, N, K) > 0
     run_case(pf, mode, T, d_in, d_out, torch.float32)
     run_case(pf, mode, T, d_in, d_out, torch.bfloat16)
@@ -161,7 +186,7 @@ def test_bf16_output_is_rne_of_fp32(pf, mode, T, d_in, d_out):
     bf16 output equals the oracle's RNE of the same GEMM's FP32 output, bit
     for bit (the tolerance gates alone would not tell RNE from truncation)."""
     x, w, dy = make_inputs(T, d_in, d_out, 21)
-    say("bf16 rounding", ["fwd", "dgrad", "wgrad"][mode], f"T={T} in={d_in} out={d_out}")
+    say("bf16 rounding", MODE_NAMES[mode], f"T={T} in={d_in} out={d_out}")
     a, sa, b, sb = device_operands(pf, mode, x, w, dy)
     c32 = pf.gemm_blockscaled(mode, a, sa, b, sb, out_dtype=torch.float32)
     c16 = pf.gemm_blockscaled(mode, a, sa, b, sb, out_dtype=torch.bfloat16)
@@ -235,6 +260,7 @@ def test_gemm_deterministic(pf):
 # ---- full transformer-shaped sizes, sampled outputs ----------------------------
 
 def _sampled_check(mode, c_dev, out_dtype, oa, osa, ob, osb, n_samples, seed, literal=True):
+    mode = DGRAD if mode == DGRAD_W else mode        # the same products
     M, N = c_dev.shape
     rng = np.random.default_rng(seed)
     ii = rng.integers(0, M, n_samples)
@@ -254,7 +280,7 @@ def _unquantized_at(mode, t, ii, jj, chunk=512):
     reported, not gated (the pages give no bound for it)."""
     if mode == FWD:                    # Y[i,j] = x[i,:] . w[j,:]
         L, R = t["x"].float().numpy(), t["w"].float().numpy()
-    elif mode == DGRAD:                # dX[i,j] = dy[i,:] . w[:,j]
+    elif mode in (DGRAD, DGRAD_W):     # dX[i,j] = dy[i,:] . w[:,j]
         L, R = t["dy"].float().numpy(), t["w"].float().numpy().T
     else:                              # dW[i,j] = dy[:,i] . x[:,j]
         L, R = t["dy"].float().numpy().T, t["x"].float().numpy().T
@@ -270,13 +296,14 @@ def _unquantized_at(mode, t, ii, jj, chunk=512):
     ("qkv_fwd", FWD, torch.bfloat16),
     ("upgate_fwd", FWD, torch.bfloat16),
     ("down_bwd", DGRAD, torch.bfloat16),
+    ("down_bwd", DGRAD_W, torch.bfloat16),
     ("down_bwd", WGRAD, torch.float32),
 ])
 def test_workload_full_size_sampled(pf, name, mode, out_dtype):
     spec = synth.workload(name).linears[0]
-    need = {FWD: ("x", "w"), DGRAD: ("w", "dy"), WGRAD: ("x", "dy")}[mode]
+    need = {FWD: ("x", "w"), DGRAD: ("w", "dy"), DGRAD_W: ("w", "dy"), WGRAD: ("x", "dy")}[mode]
     t = synth.linear_inputs(spec, seed=0, need=need)
-    say("full-size", name, ["fwd", "dgrad", "wgrad"][mode])
+    say("full-size", name, MODE_NAMES[mode])
     a, sa, b, sb = device_operands(pf, mode, t.get("x"), t.get("w"), t.get("dy"))
     c = pf.gemm_blockscaled(mode, a, sa, b, sb, out_dtype=out_dtype)
     oa, osa, ob, osb = oracle_operands(mode, t.get("x"), t.get("w"), t.get("dy"))
@@ -306,6 +333,31 @@ def test_block_stack_wgrad_split_sampled(pf):
     c = pf.gemm_blockscaled(WGRAD, a, sa, b, sb, out_dtype=torch.float32)
     oa, osa, ob, osb = oracle_operands(WGRAD, t["x"], None, t["dy"])
     g = _sampled_check(WGRAD, c, torch.float32, oa, osa, ob, osb, 4000, 2)
+    say("   sampled " + fmt(g))
+    assert g["ok"], g
+
+
+@pytest.mark.parametrize("linear,mode,out_dtype", [
+    (0, FWD, torch.bfloat16),       # QKV forward, M = 32768 tokens
+    (2, DGRAD, torch.bfloat16),     # up/gate dgrad, dX [32768 x 2048], K = 16384
+    (2, DGRAD_W, torch.bfloat16),   # the same from the weight's own codes
+    (2, WGRAD, torch.float32),      # up/gate wgrad, dW [16384 x 2048], K = 32768 tokens
+])
+def test_block_stack_headline_sampled(pf, linear, mode, out_dtype):
+    """The transformer-block workload's own shapes (32768 tokens), quantized
+    and multiplied in the launch configuration the benchmark step uses;
+    20,000 random elements plus whole rows and a column against the oracle."""
+    spec = synth.workload("block_stack").linears[linear]
+    need = {FWD: ("x", "w"), DGRAD: ("w", "dy"), DGRAD_W: ("w", "dy"), WGRAD: ("x", "dy")}[mode]
+    t = synth.linear_inputs(spec, seed=0, need=need)
+    say("block_stack", spec.name, MODE_NAMES[mode], f"T={spec.tokens} in={spec.d_in} out={spec.d_out}")
+    a, sa, b, sb = device_operands(pf, mode, t.get("x"), t.get("w"), t.get("dy"))
+    c = pf.gemm_blockscaled(mode, a, sa, b, sb, out_dtype=out_dtype)
+    oa, osa, ob, osb = oracle_operands(mode, t.get("x"), t.get("w"), t.get("dy"))
+    assert np.array_equal(host(sa).view(np.uint32), osa.view(np.uint32))
+    assert np.array_equal(host(sb).view(np.uint32), osb.view(np.uint32))
+    # block inputs have outlier channels: FWD is the named exemption of parity.py
+    g = _sampled_check(mode, c, out_dtype, oa, osa, ob, osb, 20000, 3, literal=mode != FWD)
     say("   sampled " + fmt(g))
     assert g["ok"], g
 
@@ -385,7 +437,7 @@ def test_persistent_multi_unit(pf, mode, M, N, K, out_dtype, accumulate):
     Sampled elements, whole first / last rows and a whole column."""
     rng = np.random.default_rng(M + N + K + mode)
     a, sa, b, sb = _operands_codes(rng, M, N, K, mode)
-    say("persistent multi-unit", ["fwd", "dgrad", "wgrad"][mode], M, N, K, out_dtype,
+    say("persistent multi-unit", MODE_NAMES[mode], M, N, K, out_dtype,
         "acc" if accumulate else "")
     out = None
     c0 = None
@@ -410,6 +462,26 @@ def test_persistent_multi_unit(pf, mode, M, N, K, out_dtype, accumulate):
                    literal=False)
     say("   " + fmt(g))
     assert g["ok"], g
+
+
+@pytest.mark.parametrize("M,N,K,out_dtype", [
+    (70000, 1152, 512, torch.bfloat16),     # several units per work-group, half last tile
+    (40000, 2048, 128, torch.float32),      # one K-block per unit
+    (3000, 384, 8192, torch.float32),       # split-K
+])
+def test_dgrad_w_equals_dgrad_on_random_codes(pf, M, N, K, out_dtype):
+    """Codes over the whole E4M3 range: DGRAD_W on b^T [K][N] gives DGRAD's
+    result on b [N][K] bit for bit, through the persistent multi-unit walk,
+    half-empty last column tiles and the split-K path."""
+    rng = np.random.default_rng(M + N + K)
+    a, sa, b, sb = _operands_codes(rng, M, N, K, DGRAD)
+    say("dgrad_w vs dgrad, random codes", M, N, K, out_dtype)
+    ad, sad, sbd = dev(torch.from_numpy(a)), dev(torch.from_numpy(sa)), dev(torch.from_numpy(sb))
+    c1 = pf.gemm_blockscaled(DGRAD, ad, sad, dev(torch.from_numpy(b)), sbd, out_dtype=out_dtype)
+    c2 = pf.gemm_blockscaled(DGRAD_W, ad, sad, dev(torch.from_numpy(np.ascontiguousarray(b.T))),
+                             sbd, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2)
 
 
 # ---- streams and host threads ---------------------------------------------------
