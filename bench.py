@@ -6,10 +6,10 @@ One step = the full FP8 path of every linear layer of one transformer block
 up/gate 2048->16384, down 8192->2048) on a micro-batch of 8 x 4096 = 32768
 tokens, inputs already resident in HBM:
 
-  per linear:  quant_act(X, 1x128 + 128x1^T)   quant_weight(W, 128x128 + W^T)
+  per linear:  quant_act(X, 1x128 + 128x1^T)   quant_weight(W, 128x128)
                FWD    Y  = X . W^T      (bf16 out)
                quant_act(dY, 1x128 + 128x1^T)
-               DGRAD  dX = dY . W       (bf16 out)
+               DGRAD  dX = dY . W       (bf16 out, from the weight's own codes)
                WGRAD  dW = dY^T . X     (FP32 out)
 
 The metric is the GEMM work of the step (2*M*N*K summed over the 12 GEMMs,
@@ -71,19 +71,32 @@ GEMM_SOURCES = [os.path.join(_CSRC, n) for n in ("gemm.hip", "device_common.hpp"
 QUANT_SOURCES = [os.path.join(_CSRC, n) for n in ("quant.hip", "quant_block.hpp", "device_common.hpp")]
 
 # the GEMM classes whose launches carry events inside the timed region: the
-# dominant kernel is the one of these with the most time per step (FWD and
-# DGRAD are within a few percent of each other; the WGRAD classes run fewer
-# FLOP per step)
-ROOFLINE_CLASSES = ("gemm_fwd_bf16", "gemm_dgrad_bf16")
+# dominant kernel is the one of these with the most time per step (the
+# WGRAD classes run fewer FLOP per step)
+ROOFLINE_CLASSES = ("gemm_fwd_bf16", "gemm_fwd_t_bf16", "gemm_dgrad_bf16", "gemm_dgrad_w_bf16")
 
 # kernel symbol of each launch class (for matching rocprofv3 summaries)
 KERNEL_SYMBOLS = {
     "gemm_fwd_bf16": "void puro::gemm_bs_kernel<0, 0>",
+    "gemm_fwd_t_bf16": "void puro::gemm_bs_kernel<5, 0>",
     "gemm_dgrad_bf16": "void puro::gemm_bs_kernel<1, 0>",
+    "gemm_dgrad_w_bf16": "void puro::gemm_bs_kernel<4, 0>",
     "gemm_wgrad_fp32": "void puro::gemm_bs_kernel<2, 1>",
     "gemm_wgrad_splitk": "void puro::gemm_bs_kernel<2, 3> + splitk_reduce_kernel<1>",
     "quant_act_dual": "void puro::quant_block_kernel<true, true, false, false>",
     "quant_weight_t": "void puro::quant_block_kernel<false, false, true, true>",
+    "quant_weight": "void puro::quant_block_kernel<false, false, true, false>",
+}
+
+# Operand layout of each linear layer's FWD and DGRAD GEMMs in the step.  The
+# layouts compute the same results bit for bit.  "w": FWD and DGRAD_W both
+# read the weight's own codes, so the weight quantizer writes no transposed
+# copy; "nk": FWD + DGRAD on the transposed copy.  Measured in this step on
+# the MI355X (30 steps, one box): w 7.61 ms, nk 7.65 ms; FWD_T on every
+# layer 7.67 ms, DGRAD_W on QKV and up/gate only 7.62 ms.
+LAYOUTS = {
+    "w": {n: ("fwd", "dgrad_w") for n in ("qkv", "out_proj", "up_gate", "down")},
+    "nk": {},
 }
 
 
@@ -94,6 +107,9 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="block_stack")
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--layout", choices=sorted(LAYOUTS), default="w",
+                   help="operand layout of each layer's FWD / DGRAD GEMMs (w: both on the "
+                        "weight's own codes, no transposed copy; nk: DGRAD on the transposed copy)")
     p.add_argument("--cpu-tokens", type=int, default=3072,
                    help="token slice for the CPU-oracle baseline (0 = skip)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -142,15 +158,23 @@ def act_dual_bytes(rows, cols):
     return rows * cols * (2 + 1 + 1) + 2 * (rows * cols // 128) * 4
 
 
-def weight_t_bytes(n, k):
-    return n * k * (2 + 1 + 1) + (n * k // (128 * 128)) * 4
+def weight_bytes(n, k, copies):
+    # read bf16, write `copies` code arrays (q and / or q^T), the block scales
+    return n * k * (2 + copies) + (n * k // (128 * 128)) * 4
 
 
 class Linear:
     """Device buffers of one linear layer's FP8 path (allocated once)."""
 
-    def __init__(self, torch, pf, spec, tensors):
+    def __init__(self, torch, pf, spec, tensors, layout):
         T, din, dout = spec.tokens, spec.d_in, spec.d_out
+        fwd, dgrad = layout.get(spec.name, ("fwd", "dgrad"))
+        self.fwd_mode = pf.GEMM_FWD_T if fwd == "fwd_t" else pf.GEMM_FWD
+        self.dgrad_mode = pf.GEMM_DGRAD_W if dgrad == "dgrad_w" else pf.GEMM_DGRAD
+        self.layout = (fwd, dgrad)
+        # which weight code copies the two GEMMs read
+        self.need_q = self.fwd_mode == pf.GEMM_FWD or self.dgrad_mode == pf.GEMM_DGRAD_W
+        self.need_qt = self.fwd_mode == pf.GEMM_FWD_T or self.dgrad_mode == pf.GEMM_DGRAD
         Tp = (T + 127) // 128 * 128
         d = "cuda:0"
         u8, f32, bf16 = torch.uint8, torch.float32, torch.bfloat16
@@ -173,9 +197,12 @@ class Linear:
         self.stdy = torch.empty((Tp // 128, dout), dtype=f32, device=d)
         self.dx = torch.empty((T, din), dtype=bf16, device=d)
         self.dw = torch.empty((dout, din), dtype=f32, device=d)
+        self.fwd_b = self.qw if self.fwd_mode == pf.GEMM_FWD else self.qtw
+        self.dgrad_b = self.qtw if self.dgrad_mode == pf.GEMM_DGRAD else self.qw
         self.gemms = [  # (class, mode, M, N, K)
-            ("gemm_fwd_bf16", pf.GEMM_FWD, T, dout, din),
-            ("gemm_dgrad_bf16", pf.GEMM_DGRAD, T, din, dout),
+            ("gemm_fwd_t_bf16" if fwd == "fwd_t" else "gemm_fwd_bf16", self.fwd_mode, T, dout, din),
+            ("gemm_dgrad_w_bf16" if dgrad == "dgrad_w" else "gemm_dgrad_bf16", self.dgrad_mode,
+             T, din, dout),
             (None, pf.GEMM_WGRAD, dout, din, Tp),
         ]
         ws_need = max(pf.puro_fp8_gemm_workspace_bytes(m, M, N, K) for _, m, M, N, K in self.gemms)
@@ -206,16 +233,19 @@ def step_calls(pf, layers, stream):
         return [
             ("quant_act_dual", act_dual_bytes(L.T, L.din), lambda: pf.puro_fp8_quant_act(
                 P(L.x), L.T, L.din, P(L.qx), P(L.sx), P(L.qtx), P(L.stx), stream)),
-            ("quant_weight_t", weight_t_bytes(L.dout, L.din), lambda: pf.puro_fp8_quant_weight(
-                P(L.w), L.dout, L.din, P(L.qw), P(L.qtw), P(L.sw), stream)),
+            ("quant_weight_t" if L.need_qt else "quant_weight",
+             weight_bytes(L.dout, L.din, int(L.need_q) + int(L.need_qt)),
+             lambda: pf.puro_fp8_quant_weight(
+                P(L.w), L.dout, L.din, P(L.qw) if L.need_q else None,
+                P(L.qtw) if L.need_qt else None, P(L.sw), stream)),
             (L.gemms[0][0], 2.0 * L.T * L.dout * L.din, lambda: pf.puro_fp8_gemm_blockscaled(
-                pf.GEMM_FWD, L.T, L.dout, L.din, P(L.qx), P(L.sx), P(L.qw), P(L.sw), P(L.y),
+                L.fwd_mode, L.T, L.dout, L.din, P(L.qx), P(L.sx), P(L.fwd_b), P(L.sw), P(L.y),
                 pf.OUT_BF16, 0, P(L.ws), L.ws.numel(), stream)),
             ("quant_act_dual", act_dual_bytes(L.T, L.dout), lambda: pf.puro_fp8_quant_act(
                 P(L.dy), L.T, L.dout, P(L.qdy), P(L.sdy), P(L.qtdy), P(L.stdy), stream)),
             (L.gemms[1][0], 2.0 * L.T * L.din * L.dout, lambda: pf.puro_fp8_gemm_blockscaled(
-                pf.GEMM_DGRAD, L.T, L.din, L.dout, P(L.qdy), P(L.sdy), P(L.qtw), P(L.sw), P(L.dx),
-                pf.OUT_BF16, 0, P(L.ws), L.ws.numel(), stream)),
+                L.dgrad_mode, L.T, L.din, L.dout, P(L.qdy), P(L.sdy), P(L.dgrad_b), P(L.sw),
+                P(L.dx), pf.OUT_BF16, 0, P(L.ws), L.ws.numel(), stream)),
             (L.gemms[2][0], 2.0 * L.dout * L.din * L.Tp, lambda: pf.puro_fp8_gemm_blockscaled(
                 pf.GEMM_WGRAD, L.dout, L.din, L.Tp, P(L.qtdy), P(L.stdy), P(L.qtx), P(L.stx),
                 P(L.dw), pf.OUT_FP32, 0, P(L.ws), L.ws.numel(), stream)),
@@ -574,7 +604,7 @@ def bf16_tiled(torch, pf, layers, steps, stream):
     return ms, flops / (ms * 1e-3) / 1e12
 
 
-def fp8_tensorwise_reference(torch, layers, steps):
+def fp8_tensorwise_reference(torch, pf, layers, steps):
     """The same 12 products through the vendor library's FP8 GEMM
     (torch._scaled_mm -> hipBLASLt) on the codes the step's quantizers wrote,
     with ONE scale per tensor: no per-block scales and no fold, so it is not
@@ -589,6 +619,11 @@ def fp8_tensorwise_reference(torch, layers, steps):
     one = torch.ones((), dtype=torch.float32, device="cuda:0")
     calls = []
     wgrad_dtype = torch.float32
+    for L in layers:       # both weight code copies (the step may write only one)
+        rc = pf.puro_fp8_quant_weight(L.w.data_ptr(), L.dout, L.din, L.qw.data_ptr(),
+                                      L.qtw.data_ptr(), L.sw.data_ptr(),
+                                      torch.cuda.current_stream().cuda_stream)
+        check(pf, rc, "quant_weight")
     for L in layers:
         calls.append((L.qx.view(f8), L.qw.view(f8), torch.bfloat16))      # Y  = X . W^T
         calls.append((L.qdy.view(f8), L.qtw.view(f8), torch.bfloat16))    # dX = dY . W
@@ -620,15 +655,22 @@ def fp8_tensorwise_reference(torch, layers, steps):
 
 # ---- CPU baseline --------------------------------------------------------------
 
-def cpu_baseline(specs, host_tensors, tokens):
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_slice(specs, host_tensors, tokens):
     """The oracle (quantize + block-scaled GEMM, all three modes) on the first
-    `tokens` tokens of every linear layer; GEMM FLOP of that slice / time."""
-    import numpy as np
+    `tokens` tokens of every linear layer: (GEMM FLOP, seconds)."""
     import oracle
     import synth
-    oracle.build(force=False)
-    # the host's share of cores: OMP_NUM_THREADS where the host sets it
-    oracle.set_threads(max(1, min(os.cpu_count() or 1, int(os.environ.get("OMP_NUM_THREADS", "16")))))
     flops = 0.0
     t0 = time.perf_counter()
     for spec, t in zip(specs, host_tensors):
@@ -645,12 +687,38 @@ def cpu_baseline(specs, host_tensors, tokens):
         oracle.gemm_blockscaled(oracle.MODE_WGRAD, qtdy, stdy, qtx, stx)
         tp = qtx.shape[1]
         flops += 2.0 * tokens * spec.d_out * spec.d_in * 2 + 2.0 * spec.d_out * spec.d_in * tp
-    dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.get_threads(),
+    return flops, time.perf_counter() - t0
+
+
+def cpu_baseline(specs, host_tensors, tokens, single_tokens=256):
+    """The oracle on bounded slices of the same workload: the first `tokens`
+    tokens of every layer on all the host cores this process may use (every
+    core unless OMP_NUM_THREADS caps it), and the first `single_tokens` on one
+    thread.  GEMM FLOP of the slice / time; a baseline, not a target."""
+    import oracle
+    oracle.build(force=False)
+    host_cores = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS")
+    threads = max(1, min(host_cores, int(env))) if env and env.isdigit() else host_cores
+    oracle.set_threads(threads)
+    flops, dt = _oracle_slice(specs, host_tensors, tokens)
+    used = oracle.get_threads()
+    single = None
+    if single_tokens > 0:
+        oracle.set_threads(1)
+        f1, d1 = _oracle_slice(specs, host_tensors, single_tokens)
+        single = {"value": f1 / d1 / 1e12, "unit": "TFLOP/s", "threads": 1,
+                  "seconds": round(d1, 2),
+                  "sample": f"first {single_tokens} tokens of each layer ({f1 / 1e9:.1f} GFLOP)"}
+        oracle.set_threads(used)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": used,
             "kind": "oracle", "seconds": round(dt, 2),
+            "host_cpu_count": host_cores, "cpu_model": _cpu_model(),
+            "threads_from": "OMP_NUM_THREADS" if env else "os.cpu_count()",
+            "single_thread": single,
             "sample": (f"first {tokens} tokens of each of the {len(specs)} linear layers: "
                        f"quantize X, dY (1x128 and 128x1), W (128x128) and the FWD, DGRAD and "
-                       f"WGRAD GEMMs of that slice ({flops / 1e9:.1f} GFLOP)")}
+                       f"WGRAD GEMMs of that slice ({flops / 1e9:.1f} GFLOP), on {used} threads")}
 
 
 # ---- main --------------------------------------------------------------------------
@@ -694,7 +762,7 @@ def main():
     t_gen = time.perf_counter()
     host_tensors = [synth.linear_inputs(s, seed=args.seed) for s in specs]
     gen_s = time.perf_counter() - t_gen
-    layers = [Linear(torch, pf, s, t) for s, t in zip(specs, host_tensors)]
+    layers = [Linear(torch, pf, s, t, LAYOUTS[args.layout]) for s, t in zip(specs, host_tensors)]
     if args.no_cpu_baseline or args.cpu_tokens <= 0:
         del host_tensors
         host_tensors = None
@@ -797,7 +865,7 @@ def main():
 
     fp8_vendor = None
     if not args.no_bf16_reference:
-        ref = fp8_tensorwise_reference(torch, layers, args.steps)
+        ref = fp8_tensorwise_reference(torch, pf, layers, args.steps)
         if ref is not None:
             vms, vtf, wdt = ref
             fp8_vendor = {"value": round(vtf, 1), "unit": "TFLOP/s", "ms_per_step": round(vms, 4),
@@ -839,6 +907,7 @@ def main():
         "config": {"workload": wl.name, "tokens": spec0.tokens, "hidden": 2048, "heads": 16,
                    "ffn": 8192, "linears": {s.name: [s.d_in, s.d_out] for s in specs},
                    "gemm_tflop_per_step": round(step_flops / 1e12, 4),
+                   "operand_layout": {L.spec.name: list(L.layout) for L in layers},
                    "parallelism": "single GPU"},
         "pct_of_fp8_peak": round(100.0 * value / FP8_PEAK_TFLOPS, 2),
         "gemm_only_tflops": round(step_flops / (gemm_ms * 1e-3) / 1e12, 1) if gemm_ms else None,

@@ -25,7 +25,7 @@ import os
 from . import _lib
 
 __all__ = [
-    "PuroError", "GEMM_FWD", "GEMM_DGRAD", "GEMM_WGRAD", "GEMM_DGRAD_W", "OUT_BF16", "OUT_FP32",
+    "PuroError", "GEMM_FWD", "GEMM_DGRAD", "GEMM_WGRAD", "GEMM_DGRAD_W", "GEMM_FWD_T", "OUT_BF16", "OUT_FP32",
     "puro_fp8_quant_act", "puro_fp8_quant_weight", "puro_fp8_gemm_blockscaled",
     "puro_fp8_gemm_workspace_bytes", "puro_fp8_status_string", "puro_fp8_abi_version",
     "puro_fp8_gemm_blockscaled_noalloc", "PURO_FP8_NOALLOC_SCRATCH_BYTES",
@@ -36,7 +36,7 @@ __all__ = [
     "swiglu_quant", "swiglu_bwd_quant", "rmsnorm_quant", "library_path",
 ]
 
-GEMM_FWD, GEMM_DGRAD, GEMM_WGRAD, GEMM_DGRAD_W = 0, 1, 2, 3
+GEMM_FWD, GEMM_DGRAD, GEMM_WGRAD, GEMM_DGRAD_W, GEMM_FWD_T = 0, 1, 2, 3, 4
 OUT_BF16, OUT_FP32 = 0, 1
 PURO_FP8_NOALLOC_SCRATCH_BYTES = 64 << 20
 PURO_OK = 0
@@ -258,18 +258,22 @@ def rmsnorm_quant(x, gamma, eps: float = 1e-6, row: bool = True, col: bool = Tru
     return out
 
 
-def quant_weight(w, transpose: bool = True, stream=None):
+def quant_weight(w, transpose: bool = True, codes: bool = True, stream=None):
     """128x128 block quantization of a bf16 [n, k] CUDA tensor.  Returns a dict
-    with ``q`` u8 [n, k], ``s`` f32 [n/128, k/128] and ``qt`` u8 [k, n]."""
+    with ``s`` f32 [n/128, k/128], ``q`` u8 [n, k] (unless codes=False) and
+    ``qt`` u8 [k, n] (if transpose)."""
     torch = _torch()
     w = _bf16_2d(w, "w")
     n, k = w.shape
     dev = w.device
-    out = {"q": torch.empty((n, k), dtype=torch.uint8, device=dev),
-           "s": torch.empty((n // 128, k // 128), dtype=torch.float32, device=dev)}
+    if not codes and not transpose:
+        raise ValueError("quant_weight: nothing to write (codes=False, transpose=False)")
+    out = {"s": torch.empty((n // 128, k // 128), dtype=torch.float32, device=dev)}
+    if codes:
+        out["q"] = torch.empty((n, k), dtype=torch.uint8, device=dev)
     if transpose:
         out["qt"] = torch.empty((k, n), dtype=torch.uint8, device=dev)
-    _check(puro_fp8_quant_weight(_ptr(w), n, k, _ptr(out["q"]), _ptr(out.get("qt")),
+    _check(puro_fp8_quant_weight(_ptr(w), n, k, _ptr(out.get("q")), _ptr(out.get("qt")),
                                  _ptr(out["s"]), _stream(stream)))
     return out
 
@@ -279,22 +283,24 @@ def gemm_blockscaled(mode: int, a, sa, b, sb, out_dtype=None, out=None, accumula
     """Block-scaled FP8 GEMM: C[M, N] (+)= blocks of a[M, K] . b[N, K]^T with
     scales sa [K/128, M] and sb (see the C header for each mode's layout)."""
     torch = _torch()
-    if mode not in (GEMM_FWD, GEMM_DGRAD, GEMM_WGRAD, GEMM_DGRAD_W):
+    if mode not in (GEMM_FWD, GEMM_DGRAD, GEMM_WGRAD, GEMM_DGRAD_W, GEMM_FWD_T):
         raise ValueError(f"unknown GEMM mode {mode}")
     if a.dim() != 2 or b.dim() != 2:
         raise ValueError("a and b must be 2-D")
     M, K = a.shape
-    N = b.shape[1] if mode == GEMM_DGRAD_W else b.shape[0]
+    b_kn = mode in (GEMM_DGRAD_W, GEMM_FWD_T)       # b stored [K][N]
+    N = b.shape[1] if b_kn else b.shape[0]
     if out_dtype is None:
         out_dtype = out.dtype if out is not None else torch.bfloat16
     c_dtype = OUT_FP32 if out_dtype == torch.float32 else OUT_BF16
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("out_dtype must be bfloat16 or float32")
     _need(a, torch.uint8, (M, K), "a")
-    _need(b, torch.uint8, (K, N) if mode == GEMM_DGRAD_W else (N, K), "b")
+    _need(b, torch.uint8, (K, N) if b_kn else (N, K), "b")
     _need(sa, torch.float32, (K // 128, M), "sa")
-    sb_shape = {GEMM_FWD: (N // 128, K // 128), GEMM_DGRAD: (K // 128, N // 128),
-                GEMM_DGRAD_W: (K // 128, N // 128), GEMM_WGRAD: (K // 128, N)}[mode]
+    sb_shape = {GEMM_FWD: (N // 128, K // 128), GEMM_FWD_T: (N // 128, K // 128),
+                GEMM_DGRAD: (K // 128, N // 128), GEMM_DGRAD_W: (K // 128, N // 128),
+                GEMM_WGRAD: (K // 128, N)}[mode]
     _need(sb, torch.float32, sb_shape, "sb")
     _same_device(a, sa, b, sb)
     if out is None:

@@ -15,7 +15,7 @@ constexpr int64_t kMaxDim = std::numeric_limits<int32_t>::max();
 // The GEMM addresses a row of a 256-row tile with a 32-bit offset
 // row * K + k from the tile's 64-bit base, so K is limited to 2^24.
 constexpr int64_t kMaxGemmK = int64_t(1) << 24;
-// DGRAD_W stages four weight rows per copy with a 32-bit lane offset
+// DGRAD_W and FWD_T stage four B rows per copy with a 32-bit lane offset
 // (row * N + column < 4 N).
 constexpr int64_t kMaxDgradWN = int64_t(1) << 29;
 
@@ -63,9 +63,9 @@ puro_status_t check_weight(const void* w, int64_t n, int64_t k, const uint8_t* q
     if (n <= 0 || k <= 0 || n % 128 != 0 || k % 128 != 0 || n > kMaxDim || k > kMaxDim ||
         (n / 128) * (k / 128) > kMaxDim)
         return PURO_ERR_BAD_SHAPE;
-    if (!w || !q || !s)
+    if (!w || !s || (!q && !qt))
         return PURO_ERR_NULL_POINTER;
-    if (!aligned16(w) || !aligned16(q) || !aligned16(s) || (qt && !aligned16(qt)))
+    if (!aligned16(w) || (q && !aligned16(q)) || !aligned16(s) || (qt && !aligned16(qt)))
         return PURO_ERR_MISALIGNED;
     return PURO_OK;
 }
@@ -198,7 +198,7 @@ puro_status_t puro_fp8_rmsnorm_quant(const void* x, const void* gamma, int64_t r
 
 size_t puro_fp8_gemm_workspace_bytes(puro_gemm_mode_t mode, int64_t M, int64_t N, int64_t K)
 {
-    if ((int)mode < 0 || (int)mode > 3 || !gemm_shape_ok(M, N, K) || M == 0)
+    if ((int)mode < 0 || (int)mode > 4 || !gemm_shape_ok(M, N, K) || M == 0)
         return 0;
     return puro::gemm_workspace_bytes((int)mode, M, N, K);
 }
@@ -210,13 +210,13 @@ puro_status_t puro_fp8_gemm_blockscaled(puro_gemm_mode_t mode, int64_t M, int64_
                                         void* stream)
 {
     return guarded([&]() -> puro_status_t {
-        if ((int)mode < 0 || (int)mode > 3)
+        if ((int)mode < 0 || (int)mode > 4)
             return PURO_ERR_BAD_ENUM;
         if ((int)c_dtype != PURO_OUT_BF16 && (int)c_dtype != PURO_OUT_FP32)
             return PURO_ERR_BAD_ENUM;
         if (accumulate && c_dtype != PURO_OUT_FP32)
             return PURO_ERR_BAD_ENUM;
-        if (!gemm_shape_ok(M, N, K) || (mode == PURO_GEMM_DGRAD_W && N > kMaxDgradWN))
+        if (!gemm_shape_ok(M, N, K) || ((mode == PURO_GEMM_DGRAD_W || mode == PURO_GEMM_FWD_T) && N > kMaxDgradWN))
             return PURO_ERR_BAD_SHAPE;
         if (M == 0)
             return PURO_OK;
@@ -244,13 +244,13 @@ puro_status_t puro_fp8_gemm_blockscaled_noalloc(puro_gemm_mode_t mode, int64_t M
                                                 void* stream)
 {
     return guarded([&]() -> puro_status_t {
-        if ((int)mode < 0 || (int)mode > 3)
+        if ((int)mode < 0 || (int)mode > 4)
             return PURO_ERR_BAD_ENUM;
         if ((int)c_dtype != PURO_OUT_BF16 && (int)c_dtype != PURO_OUT_FP32)
             return PURO_ERR_BAD_ENUM;
         if (accumulate && c_dtype != PURO_OUT_FP32)
             return PURO_ERR_BAD_ENUM;
-        if (!gemm_shape_ok(M, N, K) || (mode == PURO_GEMM_DGRAD_W && N > kMaxDgradWN))
+        if (!gemm_shape_ok(M, N, K) || ((mode == PURO_GEMM_DGRAD_W || mode == PURO_GEMM_FWD_T) && N > kMaxDgradWN))
             return PURO_ERR_BAD_SHAPE;
         if (M == 0)
             return PURO_OK;

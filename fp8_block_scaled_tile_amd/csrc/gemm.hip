@@ -73,8 +73,13 @@ constexpr int GROUP_M = 4;
 // MODE_DGRAD_W is DGRAD with B read straight from the weight's codes
 // W [K = out][N = in] (N-contiguous) instead of their transposed copy: the
 // K-block's 128 weight rows are staged as they lie and the B fragments are
-// read with the gfx950 LDS transpose read (ds_read_b64_tr_b8).
-enum { MODE_FWD = 0, MODE_DGRAD = 1, MODE_WGRAD = 2, MODE_BF16 = 3, MODE_DGRAD_W = 4 };
+// read with the gfx950 LDS transpose read (ds_read_b64_tr_b8).  MODE_FWD_T
+// is FWD the same way, with B the transposed weight codes W^T [K = in][N =
+// out] and the FWD scale indexing.
+enum { MODE_FWD = 0, MODE_DGRAD = 1, MODE_WGRAD = 2, MODE_BF16 = 3, MODE_DGRAD_W = 4,
+       MODE_FWD_T = 5 };
+// B staged as [K][N] rows and read with transpose reads
+constexpr bool b_kn(int mode) { return mode == MODE_DGRAD_W || mode == MODE_FWD_T; }
 enum { OUT_BF16 = 0, OUT_FP32 = 1, OUT_FP32_ACC = 2, OUT_PARTIAL = 3 };
 
 // LDS rows are 128 bytes (one K-block of one row).  The 16-byte chunk c of
@@ -137,7 +142,7 @@ __device__ __forceinline__ FragOff frag_off_b(int lane)
     return {r * BK + ((c0 ^ swz_b(r)) << 4), r * BK + (((c0 + 1) ^ swz_b(r)) << 4)};
 }
 
-// MODE_DGRAD_W: the staged B slice is 128 weight rows (k) of 256 bytes (the
+// [K][N] modes (DGRAD_W, FWD_T): the staged B slice is 128 rows (k) of 256 bytes (the
 // tile's 256 columns n).  The 16-byte unit u of row r is stored at unit
 // position u ^ swz_w(r).  A transpose read (below) has its 32 lanes of one
 // pass read one 16-byte unit in each of 16 rows r = 32*g + 8*j + m (g = 0, 1;
@@ -260,9 +265,9 @@ __device__ __forceinline__ void issue_stage(Stage& st, const uint8_t* At, const 
 {
     const uint8_t* ab = uniform_ptr(At + (size_t)kb * BK);
     const int r0 = 32 * wave + (lane >> 3);
-    if constexpr (MODE == MODE_DGRAD_W) {
-        // B = the weight's rows kb*128 .. +127, columns n0 .. n0+255 (N-contiguous,
-        // N = the row pitch); each wave copies 16 rows, lane L of instruction i
+    if constexpr (b_kn(MODE)) {
+        // B = rows kb*128 .. +127 of the [K][N] codes, columns n0 .. n0+255
+        // (N-contiguous, N = the row pitch); each wave copies 16 rows, lane L of instruction i
         // fills row 16*wave + 4*i + L/16 at unit position L % 16.  Columns past N
         // (a half tile) read the row's last 16 bytes instead (never stored).
         const uint8_t* wb = uniform_ptr(Bt + (size_t)kb * BK * (size_t)N);
@@ -281,7 +286,7 @@ __device__ __forceinline__ void issue_stage(Stage& st, const uint8_t* At, const 
         const uint32_t ca = 16u * (uint32_t)((lane & 7) ^ swz(row));
         const uint32_t ao = (uint32_t)min(row, rows_a - 1) * (uint32_t)K + ca;
         __builtin_amdgcn_global_load_lds(ab + ao, (lds_void*)(st.a + (32 * wave + 8 * i) * BK), 16, 0, 0);
-        if constexpr (MODE != MODE_DGRAD_W) {
+        if constexpr (!b_kn(MODE)) {
             const uint8_t* bb = uniform_ptr(Bt + (size_t)kb * BK);
             const uint32_t cb = 16u * (uint32_t)((lane & 7) ^ swz_stage_b<MODE>(row));
             const uint32_t bo = (uint32_t)min(row, rows_b - 1) * (uint32_t)K + cb;
@@ -302,7 +307,8 @@ __device__ __forceinline__ void issue_stage(Stage& st, const uint8_t* At, const 
                                              (lds_void*)(st.sb), 16, 0, 0);
         } else if (lane < 2) {
             const int nb = min(n0 / BK + lane, N / BK - 1);
-            const size_t idx = (MODE == MODE_FWD) ? (size_t)nb * KB + kb : (size_t)kb * (N / BK) + nb;
+            const size_t idx = (MODE == MODE_FWD || MODE == MODE_FWD_T) ? (size_t)nb * KB + kb
+                                                                        : (size_t)kb * (N / BK) + nb;
             __builtin_amdgcn_global_load_lds(SB + idx, (lds_void*)(st.sb), 4, 0, 0);
         }
     }
@@ -382,7 +388,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
     // K-block and one float4 of sA per tile.
     const FragOff fo = frag_off(lane);
     const FragOff fob = (MODE == MODE_WGRAD) ? fo : frag_off_b(lane);
-    // MODE_DGRAD_W: per tile, the lane's offset of transpose read j = 0 (read
+    // [K][N] modes: per tile, the lane's offset of transpose read j = 0 (read
     // j adds 8 weight rows, 2048 bytes)
     int fow[TN];
 #pragma unroll
@@ -498,7 +504,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
 #pragma unroll
             for (int tn = 0; tn < TN; ++tn) {
                 __builtin_amdgcn_sched_barrier(0);
-                if constexpr (MODE == MODE_DGRAD_W)
+                if constexpr (b_kn(MODE))
                     bf[tn] = load_frag_w(st.b, fow[tn], fow[tn] + 2048, fow[tn] + 4096,
                                          fow[tn] + 6144);
                 else
@@ -566,7 +572,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
         }
     };
     auto epilogue = [&](const Unit& t) __attribute__((always_inline)) {
-        if constexpr (MODE == MODE_FWD || MODE == MODE_DGRAD || MODE == MODE_DGRAD_W)
+        if constexpr (MODE != MODE_WGRAD && MODE != MODE_BF16)
             fold_row(TM - 1, sc_carry);               // the unit's last row
         if ((t.n0 + wn * WN) >= N)
             return;
@@ -585,7 +591,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
                             store1((size_t)m * N + n_lane + 16 * tn, t.split, acc[sm][tn][r]);
                     }
                 }
-        } else if constexpr (MODE == MODE_DGRAD_W) {
+        } else if constexpr (b_kn(MODE)) {
             // lane: row m = m_lane + 16*sm; columns n_lane + 16*tn + r (the
             // fragments' natural column order, g = lane >> 4).  FP32: one
             // 16-byte store per tile.  bf16: lane groups g and g ^ 1 (lanes l
@@ -685,7 +691,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
     // first block is already in LDS when the last block of a unit is done.
     auto issue = [&](Stage& st, const Unit& t, int kb) __attribute__((always_inline)) {
         const uint8_t* At = A + (size_t)t.m0 * K;
-        const uint8_t* Bt = (MODE == MODE_DGRAD_W) ? B : B + (size_t)t.n0 * K;
+        const uint8_t* Bt = b_kn(MODE) ? B : B + (size_t)t.n0 * K;
         issue_stage<MODE>(st, At, SA, Bt, SB, kb, t.m0, t.n0, min(M - t.m0, BM),
                           min(N - t.n0, BN), M, N, K, KB, wave, lane);
     };
@@ -970,6 +976,8 @@ hipError_t launch_gemm(int mode, int64_t M, int64_t N, int64_t K, const uint8_t*
     case MODE_DGRAD: return launch_mode<MODE_DGRAD>(out, a, sa, b, sb, c, ws, m, n, k, splits, stream);
     case 3:          // the C ABI's PURO_GEMM_DGRAD_W
         return launch_mode<MODE_DGRAD_W>(out, a, sa, b, sb, c, ws, m, n, k, splits, stream);
+    case 4:          // the C ABI's PURO_GEMM_FWD_T
+        return launch_mode<MODE_FWD_T>(out, a, sa, b, sb, c, ws, m, n, k, splits, stream);
     default:         return launch_mode<MODE_WGRAD>(out, a, sa, b, sb, c, ws, m, n, k, splits, stream);
     }
 }

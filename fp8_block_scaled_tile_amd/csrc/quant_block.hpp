@@ -105,7 +105,8 @@ __device__ __forceinline__ void quant_block_body(const uint4 (&v)[8], int64_t ro
     }
 
     // ---- codes in input orientation (1x128 tiles, or the weight block) --
-    if constexpr (ROW || WEIGHT) {
+    // (a weight quantized for the transposed copy only passes q = NULL)
+    if (ROW || (WEIGHT && q != nullptr)) {
         // Row tiles: every lane of a DPP row gets the 8 row maxima; lane qd
         // computes the parameters of row qd & 7 only, lanes 0..7 store their
         // row's scale, and r is broadcast from lane p of the DPP row.

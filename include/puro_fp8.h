@@ -69,8 +69,10 @@ typedef enum {
     PURO_GEMM_FWD = 0,    /* Y  = X . W^T   : M = tokens, N = out, K = in     */
     PURO_GEMM_DGRAD = 1,  /* dX = dY . W    : M = tokens, N = in,  K = out    */
     PURO_GEMM_WGRAD = 2,  /* dW = dY^T . X  : M = out,    N = in,  K = tokens */
-    PURO_GEMM_DGRAD_W = 3 /* dX = dY . W as DGRAD, with b the weight's own
-                             codes W [out][in] = [K][N] (no transposed copy)  */
+    PURO_GEMM_DGRAD_W = 3, /* dX = dY . W as DGRAD, with b the weight's own
+                              codes W [out][in] = [K][N] (no transposed copy) */
+    PURO_GEMM_FWD_T = 4    /* Y = X . W^T as FWD, with b the transposed codes
+                              W^T [in][out] = [K][N] (no untransposed copy)   */
 } puro_gemm_mode_t;
 
 typedef enum {
@@ -106,12 +108,13 @@ puro_status_t puro_fp8_quant_act(const void* x, int64_t rows, int64_t cols,
  * Weight quantizer (128x128 blocks).
  *
  *   w   bf16 [n][k]          input weight (out features n, in features k)
- *   q   u8   [n][k]          codes
+ *   q   u8   [n][k]          codes (NULL = skip: a layer whose GEMMs are
+ *                            FWD_T and DGRAD reads only qt)
  *   qt  u8   [k][n]          the same codes transposed (NULL = skip); DGRAD
- *                            uses it as its K-contiguous B operand
+ *                            and FWD_T read it
  *   s   f32  [n/128][k/128]  one scale per block
  *
- * Requires n, k > 0 and multiples of 128.
+ * Requires n, k > 0 and multiples of 128; s and at least one of q, qt.
  * Defined by: the same passages as puro_fp8_quant_act.
  */
 puro_status_t puro_fp8_quant_weight(const void* w, int64_t n, int64_t k,
@@ -126,8 +129,9 @@ puro_status_t puro_fp8_quant_weight(const void* w, int64_t n, int64_t k,
  *
  *   a   u8  [M][K]   E4M3 codes, K-contiguous
  *   sa  f32 [K/128][M]
- *   b   u8  [N][K]   E4M3 codes, K-contiguous (DGRAD_W: [K][N], N-contiguous)
- *   sb  f32 FWD     [N/128][K/128] (the weight's block scales)
+ *   b   u8  [N][K]   E4M3 codes, K-contiguous (DGRAD_W, FWD_T: [K][N],
+ *                    N-contiguous)
+ *   sb  f32 FWD     [N/128][K/128] (the weight's block scales; FWD_T too)
  *           DGRAD   [K/128][N/128] (the weight's block scales as stored for
  *                                   W [K][N]; b is the transposed code copy)
  *           DGRAD_W [K/128][N/128] (the same scales; b is W's codes as the
@@ -142,6 +146,12 @@ puro_status_t puro_fp8_quant_weight(const void* w, int64_t n, int64_t k,
  *          weight quantizer's transposed copy is then not needed (qt = NULL).
  *          The result equals DGRAD's (the same products); requires
  *          N <= 2^29 (N = in).
+ *   FWD_T: a = q(X), sa = s(X), b = qt(W) [in][out], sb = s(W); the result
+ *          equals FWD's; requires N <= 2^29 (N = out).  A layer that runs
+ *          FWD_T and DGRAD needs only the transposed weight codes.
+ * The two [K][N] modes read B with LDS transpose reads; which layout runs
+ * faster depends on the shape (the FWD and DGRAD kernels are the same
+ * otherwise).
  *   WGRAD: a = qt(dY) [out][T_pad], sa = st(dY), b = qt(X) [in][T_pad],
  *          sb = st(X)
  *

@@ -80,9 +80,10 @@ def test_quant_weight_validation(lib):
     assert f(P16, 100, 128, P16, None, P16, None) == SHAPE
     assert f(P16, 128, 0, P16, None, P16, None) == SHAPE
     assert f(None, 128, 128, P16, None, P16, None) == NULLP
-    assert f(P16, 128, 128, None, None, P16, None) == NULLP
+    assert f(P16, 128, 128, None, None, P16, None) == NULLP      # neither q nor qt
     assert f(P16, 128, 128, P16, None, None, None) == NULLP
     assert f(P16, 128, 128, P16, P_ODD, P16, None) == ALIGN
+    assert f(P16, 128, 128, P_ODD, P16, P16, None) == ALIGN
 
 
 def test_gemm_validation(lib):
@@ -95,7 +96,8 @@ def test_gemm_validation(lib):
         return f(d["mode"], d["M"], d["N"], d["K"], d["a"], d["sa"], d["b"], d["sb"], d["c"],
                  d["c_dtype"], d["acc"], d["ws"], d["wsb"], None)
 
-    assert call(mode=4) == ENUM
+    assert call(mode=5) == ENUM
+    assert call(mode=4, N=(1 << 29) + 128) == SHAPE          # FWD_T: N <= 2^29
     assert call(mode=-1) == ENUM
     assert call(mode=3, N=(1 << 29) + 128) == SHAPE          # DGRAD_W: N <= 2^29
     assert call(mode=3, a=None) == NULLP
@@ -132,7 +134,7 @@ def test_noalloc_gemm_validation(lib):
     """The allocation-free GEMM refuses bad arguments, and problems whose
     split-K partials exceed its static array, before touching a device."""
     f = lib.puro_fp8_gemm_blockscaled_noalloc
-    assert f(4, 256, 256, 256, P16, P16, P16, P16, P16, 0, 0, None) == ENUM
+    assert f(5, 256, 256, 256, P16, P16, P16, P16, P16, 0, 0, None) == ENUM
     assert f(0, 256, 256, 256, P16, P16, P16, P16, P16, 0, 1, None) == ENUM      # += needs FP32
     assert f(0, 256, 200, 256, P16, P16, P16, P16, P16, 0, 0, None) == SHAPE
     assert f(0, 0, 256, 256, None, None, None, None, None, 0, 0, None) == OK

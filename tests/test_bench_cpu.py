@@ -16,35 +16,54 @@ class _Buf:
         return 16
 
 
-def _layer(name, T, din, dout):
+class _Ptr(_Buf):
+    def __init__(self, v):
+        self.v = v
+
+    def data_ptr(self):
+        return self.v
+
+
+def _layer(name, T, din, dout, fwd_mode=0, dgrad_mode=1):
     L = types.SimpleNamespace(spec=types.SimpleNamespace(name=name), T=T, Tp=T, din=din, dout=dout)
-    for a in ("x", "qx", "sx", "qtx", "stx", "w", "qw", "qtw", "sw", "y", "dy", "qdy", "sdy",
+    for a in ("x", "qx", "sx", "qtx", "stx", "w", "sw", "y", "dy", "qdy", "sdy",
               "qtdy", "stdy", "dx", "dw", "ws"):
         setattr(L, a, _Buf())
-    L.gemms = [("gemm_fwd_bf16", 0, T, dout, din), ("gemm_dgrad_bf16", 1, T, din, dout),
+    L.qw, L.qtw = _Ptr(16), _Ptr(32)         # tell the two weight code copies apart
+    L.fwd_mode, L.dgrad_mode = fwd_mode, dgrad_mode
+    L.need_q = fwd_mode == 0 or dgrad_mode == 3
+    L.need_qt = fwd_mode == 4 or dgrad_mode == 1
+    L.fwd_b = L.qw if fwd_mode == 0 else L.qtw
+    L.dgrad_b = L.qtw if dgrad_mode == 1 else L.qw
+    L.gemms = [("gemm_fwd_bf16", fwd_mode, T, dout, din), ("gemm_dgrad_bf16", dgrad_mode, T, din, dout),
                ("gemm_wgrad_fp32", 2, dout, din, T)]
     return L
 
 
 def test_step_calls_bind_each_layer():
+    """Each layer's launches, in order, with its own shapes, GEMM modes and
+    weight code copies: layer a runs FWD + DGRAD (reads q and q^T), layer b
+    FWD_T + DGRAD (reads q^T only, so the weight quantizer skips q)."""
     seen = []
     pf = types.SimpleNamespace(
-        GEMM_FWD=0, GEMM_DGRAD=1, GEMM_WGRAD=2, OUT_BF16=0, OUT_FP32=1,
+        GEMM_FWD=0, GEMM_DGRAD=1, GEMM_WGRAD=2, GEMM_DGRAD_W=3, GEMM_FWD_T=4, OUT_BF16=0,
+        OUT_FP32=1,
         puro_fp8_quant_act=lambda x, r, c, *a: seen.append(("act", r, c)) or 0,
-        puro_fp8_quant_weight=lambda w, n, k, *a: seen.append(("weight", n, k)) or 0,
-        puro_fp8_gemm_blockscaled=lambda m, M, N, K, *a: seen.append(("gemm", m, M, N, K)) or 0)
-    layers = [_layer("a", 256, 128, 384), _layer("b", 512, 256, 128)]
+        puro_fp8_quant_weight=lambda w, n, k, q, qt, s, st: seen.append(("weight", n, k, q, qt)) or 0,
+        puro_fp8_gemm_blockscaled=lambda m, M, N, K, a, sa, b, *r: seen.append(("gemm", m, M, N, K, b)) or 0)
+    layers = [_layer("a", 256, 128, 384), _layer("b", 512, 256, 128, fwd_mode=4, dgrad_mode=1)]
     calls = bench.step_calls(pf, layers, None)
     assert [c[0] for c in calls] == ["a"] * 6 + ["b"] * 6
     for _, _, _, fn in calls:
         assert fn() == 0
-    expect = []
-    for T, din, dout in ((256, 128, 384), (512, 256, 128)):
-        expect += [("act", T, din), ("weight", dout, din), ("gemm", 0, T, dout, din),
-                   ("act", T, dout), ("gemm", 1, T, din, dout), ("gemm", 2, dout, din, T)]
+    expect = [("act", 256, 128), ("weight", 384, 128, 16, 32), ("gemm", 0, 256, 384, 128, 16),
+              ("act", 256, 384), ("gemm", 1, 256, 128, 384, 32), ("gemm", 2, 384, 128, 256, 0),
+              ("act", 512, 256), ("weight", 128, 256, None, 32), ("gemm", 4, 512, 128, 256, 32),
+              ("act", 512, 128), ("gemm", 1, 512, 256, 128, 32), ("gemm", 2, 128, 256, 512, 0)]
     assert seen == expect
     works = [c[2] for c in calls]
     assert works[2] == 2.0 * 256 * 384 * 128 and works[8] == 2.0 * 512 * 128 * 256
+    assert works[1] == bench.weight_bytes(384, 128, 2) and works[7] == bench.weight_bytes(128, 256, 1)
 
 
 def test_ingest_mfma_weights_by_duration_and_gates_on_code(tmp_path, monkeypatch):
@@ -119,6 +138,6 @@ def test_roofline_classes_are_gemm_classes():
 def test_vendor_fp8_leg_is_omitted_without_fp8_support():
     """A torch build without an FP8 dtype or _scaled_mm gives no context leg
     (None) rather than an error, so the bench line is still printed."""
-    assert bench.fp8_tensorwise_reference(types.SimpleNamespace(), [], 1) is None
+    assert bench.fp8_tensorwise_reference(types.SimpleNamespace(), None, [], 1) is None
     no_mm = types.SimpleNamespace(float8_e4m3fn=object())
-    assert bench.fp8_tensorwise_reference(no_mm, [], 1) is None
+    assert bench.fp8_tensorwise_reference(no_mm, None, [], 1) is None

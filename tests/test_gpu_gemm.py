@@ -19,7 +19,7 @@ from parity import bf16_host_bits, dev, fmt, gemm_gates, host, random_bf16, say
 
 pytestmark = pytest.mark.gpu
 
-FWD, DGRAD, WGRAD, DGRAD_W = 0, 1, 2, 3
+FWD, DGRAD, WGRAD, DGRAD_W, FWD_T = 0, 1, 2, 3, 4
 
 
 @pytest.fixture(scope="module")
@@ -46,13 +46,17 @@ def device_operands(pf, mode, x, w, dy):
         qa = pf.quant_act(dev(dy), row=True)
         qw = pf.quant_weight(dev(w), transpose=False)
         return qa["q"], qa["s"], qw["q"], qw["s"]
+    if mode == FWD_T:                    # the transposed weight codes
+        qa = pf.quant_act(dev(x), row=True)
+        qw = pf.quant_weight(dev(w), transpose=True)
+        return qa["q"], qa["s"], qw["qt"], qw["s"]
     qa = pf.quant_act(dev(dy), row=False, col=True)
     qb = pf.quant_act(dev(x), row=False, col=True)
     return qa["qt"], qa["st"], qb["qt"], qb["st"]
 
 
 def oracle_operands(mode, x, w, dy):
-    if mode == FWD:
+    if mode in (FWD, FWD_T):            # FWD_T computes FWD's products
         qa, sa = oracle.quant_rowwise(synth.bits(x))
         qw, _, sw = oracle.quant_weight(synth.bits(w), transpose=False)
         return qa, sa, qw, sw
@@ -78,7 +82,7 @@ def run_case(pf, mode, T, d_in, d_out, out_dtype, seed=0, accumulate=False):
     say("gemm", MODE_NAMES[mode], f"T={T} in={d_in} out={d_out}", out_dtype,
         "acc" if accumulate else "")
     a, sa, b, sb = device_operands(pf, mode, x, w, dy)
-    M, N = a.shape[0], (b.shape[1] if mode == DGRAD_W else b.shape[0])
+    M, N = a.shape[0], (b.shape[1] if mode in B_KN else b.shape[0])
     c0 = None
     out = None
     if accumulate:
@@ -87,9 +91,9 @@ def run_case(pf, mode, T, d_in, d_out, out_dtype, seed=0, accumulate=False):
     c = pf.gemm_blockscaled(mode, a, sa, b, sb, out_dtype=out_dtype, out=out,
                             accumulate=accumulate)
     oa, osa, ob, osb = oracle_operands(mode, x, w, dy)
-    omode = DGRAD if mode == DGRAD_W else mode
+    omode = ORACLE_MODE[mode]
     assert np.array_equal(host(a), oa)
-    assert np.array_equal(host(b).T if mode == DGRAD_W else host(b), ob)
+    assert np.array_equal(host(b).T if mode in B_KN else host(b), ob)
     ref = oracle.gemm_blockscaled(omode, oa, osa, ob, osb)
     ii, jj = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
     bound = hw_accum.bounds(omode, oa, osa, ob, osb, ii.ravel(), jj.ravel(), ref.ravel())
@@ -99,13 +103,15 @@ def run_case(pf, mode, T, d_in, d_out, out_dtype, seed=0, accumulate=False):
         bound = (bound[0] + extra, bound[1] + extra)
     # FWD reads X with outlier channels (x20): the named exemption of parity.py
     g = gemm_gates(device_values(c), ref, bound, out_dtype == torch.bfloat16,
-                   literal=mode != FWD)
+                   literal=omode != FWD)
     say("   " + fmt(g))
     assert g["ok"], g
     return g
 
 
-MODE_NAMES = {FWD: "fwd", DGRAD: "dgrad", WGRAD: "wgrad", DGRAD_W: "dgrad_w"}
+MODE_NAMES = {FWD: "fwd", DGRAD: "dgrad", WGRAD: "wgrad", DGRAD_W: "dgrad_w", FWD_T: "fwd_t"}
+B_KN = (DGRAD_W, FWD_T)                  # modes whose b is stored [K][N]
+ORACLE_MODE = {FWD: FWD, DGRAD: DGRAD, WGRAD: WGRAD, DGRAD_W: DGRAD, FWD_T: FWD}
 
 
 def device_values(c):
@@ -158,18 +164,33 @@ def test_dgrad_from_weight_codes_small(pf, T, d_in, d_out):
         assert torch.equal(c1, c2)
 
 
-@pytest.mark.parametrize("mode", [FWD, DGRAD, WGRAD, DGRAD_W])
+@pytest.mark.parametrize("T,d_in,d_out", SMALL)
+def test_fwd_from_transposed_weight_codes_small(pf, T, d_in, d_out):
+    """FWD_T reads the transposed weight codes W^T [in][out] through LDS
+    transpose reads: the oracle's gates, and bit for bit the FWD result."""
+    for dt in (torch.float32, torch.bfloat16):
+        run_case(pf, FWD_T, T, d_in, d_out, dt)
+    x, w, dy = make_inputs(T, d_in, d_out, 0)
+    a, sa, bw, sb = device_operands(pf, FWD, x, w, dy)
+    _, _, bt, _ = device_operands(pf, FWD_T, x, w, dy)
+    for dt in (torch.float32, torch.bfloat16):
+        c1 = pf.gemm_blockscaled(FWD, a, sa, bw, sb, out_dtype=dt)
+        c2 = pf.gemm_blockscaled(FWD_T, a, sa, bt, sb, out_dtype=dt)
+        assert torch.equal(c1, c2)
+
+
+@pytest.mark.parametrize("mode", [FWD, DGRAD, WGRAD, DGRAD_W, FWD_T])
 def test_split_k_paths(pf, mode):
     """Few output tiles and a long K: the K range is split across work-groups
     and reduced in a second kernel (FP32 and bf16 outputs, accumulate)."""
     T, d_in, d_out = (2048, 256, 256) if mode != WGRAD else (4096, 256, 256)
-    if mode == FWD:
+    if mode in (FWD, FWD_T):
         T, d_in, d_out = 256, 2048, 256
     elif mode in (DGRAD, DGRAD_W):
         T, d_in, d_out = 256, 256, 2048
     M = T if mode != WGRAD else d_out
-    N = d_out if mode == FWD else d_in
-    K = d_in if mode == FWD else (d_out if mode in (DGRAD, DGRAD_W) else T)
+    N = d_out if mode in (FWD, FWD_T) else d_in
+    K = d_in if mode in (FWD, FWD_T) else (d_out if mode in (DGRAD, DGRAD_W) else T)
     assert pf.puro_fp8_gemm_workspace_bytes(mode, M, N, K) > 0
     run_case(pf, mode, T, d_in, d_out, torch.float32)
     run_case(pf, mode, T, d_in, d_out, torch.bfloat16)
@@ -260,7 +281,7 @@ def test_gemm_deterministic(pf):
 # ---- full transformer-shaped sizes, sampled outputs ----------------------------
 
 def _sampled_check(mode, c_dev, out_dtype, oa, osa, ob, osb, n_samples, seed, literal=True):
-    mode = DGRAD if mode == DGRAD_W else mode        # the same products
+    mode = ORACLE_MODE[mode]                         # the same products
     M, N = c_dev.shape
     rng = np.random.default_rng(seed)
     ii = rng.integers(0, M, n_samples)
@@ -278,7 +299,7 @@ def _unquantized_at(mode, t, ii, jj, chunk=512):
     """The product of the unquantized bf16 operands at (ii[s], jj[s]), in
     double: the error of the whole FP8 path against a plain matmul is
     reported, not gated (the pages give no bound for it)."""
-    if mode == FWD:                    # Y[i,j] = x[i,:] . w[j,:]
+    if mode in (FWD, FWD_T):           # Y[i,j] = x[i,:] . w[j,:]
         L, R = t["x"].float().numpy(), t["w"].float().numpy()
     elif mode in (DGRAD, DGRAD_W):     # dX[i,j] = dy[i,:] . w[:,j]
         L, R = t["dy"].float().numpy(), t["w"].float().numpy().T
@@ -339,6 +360,7 @@ def test_block_stack_wgrad_split_sampled(pf):
 
 @pytest.mark.parametrize("linear,mode,out_dtype", [
     (0, FWD, torch.bfloat16),       # QKV forward, M = 32768 tokens
+    (0, FWD_T, torch.bfloat16),     # the same from the transposed weight codes
     (2, DGRAD, torch.bfloat16),     # up/gate dgrad, dX [32768 x 2048], K = 16384
     (2, DGRAD_W, torch.bfloat16),   # the same from the weight's own codes
     (2, WGRAD, torch.float32),      # up/gate wgrad, dW [16384 x 2048], K = 32768 tokens
@@ -348,7 +370,8 @@ def test_block_stack_headline_sampled(pf, linear, mode, out_dtype):
     and multiplied in the launch configuration the benchmark step uses;
     20,000 random elements plus whole rows and a column against the oracle."""
     spec = synth.workload("block_stack").linears[linear]
-    need = {FWD: ("x", "w"), DGRAD: ("w", "dy"), DGRAD_W: ("w", "dy"), WGRAD: ("x", "dy")}[mode]
+    need = {FWD: ("x", "w"), FWD_T: ("x", "w"), DGRAD: ("w", "dy"), DGRAD_W: ("w", "dy"),
+            WGRAD: ("x", "dy")}[mode]
     t = synth.linear_inputs(spec, seed=0, need=need)
     say("block_stack", spec.name, MODE_NAMES[mode], f"T={spec.tokens} in={spec.d_in} out={spec.d_out}")
     a, sa, b, sb = device_operands(pf, mode, t.get("x"), t.get("w"), t.get("dy"))
@@ -357,7 +380,8 @@ def test_block_stack_headline_sampled(pf, linear, mode, out_dtype):
     assert np.array_equal(host(sa).view(np.uint32), osa.view(np.uint32))
     assert np.array_equal(host(sb).view(np.uint32), osb.view(np.uint32))
     # block inputs have outlier channels: FWD is the named exemption of parity.py
-    g = _sampled_check(mode, c, out_dtype, oa, osa, ob, osb, 20000, 3, literal=mode != FWD)
+    g = _sampled_check(mode, c, out_dtype, oa, osa, ob, osb, 20000, 3,
+                       literal=ORACLE_MODE[mode] != FWD)
     say("   sampled " + fmt(g))
     assert g["ok"], g
 
@@ -469,16 +493,18 @@ def test_persistent_multi_unit(pf, mode, M, N, K, out_dtype, accumulate):
     (40000, 2048, 128, torch.float32),      # one K-block per unit
     (3000, 384, 8192, torch.float32),       # split-K
 ])
-def test_dgrad_w_equals_dgrad_on_random_codes(pf, M, N, K, out_dtype):
-    """Codes over the whole E4M3 range: DGRAD_W on b^T [K][N] gives DGRAD's
-    result on b [N][K] bit for bit, through the persistent multi-unit walk,
-    half-empty last column tiles and the split-K path."""
+@pytest.mark.parametrize("mode", [DGRAD, FWD])
+def test_kn_modes_equal_on_random_codes(pf, M, N, K, out_dtype, mode):
+    """Codes over the whole E4M3 range: DGRAD_W / FWD_T on b^T [K][N] give
+    DGRAD's / FWD's result on b [N][K] bit for bit, through the persistent
+    multi-unit walk, half-empty last column tiles and the split-K path."""
     rng = np.random.default_rng(M + N + K)
-    a, sa, b, sb = _operands_codes(rng, M, N, K, DGRAD)
-    say("dgrad_w vs dgrad, random codes", M, N, K, out_dtype)
+    a, sa, b, sb = _operands_codes(rng, M, N, K, mode)
+    kn = DGRAD_W if mode == DGRAD else FWD_T
+    say(MODE_NAMES[kn], "vs", MODE_NAMES[mode], "random codes", M, N, K, out_dtype)
     ad, sad, sbd = dev(torch.from_numpy(a)), dev(torch.from_numpy(sa)), dev(torch.from_numpy(sb))
-    c1 = pf.gemm_blockscaled(DGRAD, ad, sad, dev(torch.from_numpy(b)), sbd, out_dtype=out_dtype)
-    c2 = pf.gemm_blockscaled(DGRAD_W, ad, sad, dev(torch.from_numpy(np.ascontiguousarray(b.T))),
+    c1 = pf.gemm_blockscaled(mode, ad, sad, dev(torch.from_numpy(b)), sbd, out_dtype=out_dtype)
+    c2 = pf.gemm_blockscaled(kn, ad, sad, dev(torch.from_numpy(np.ascontiguousarray(b.T))),
                              sbd, out_dtype=out_dtype)
     torch.cuda.synchronize()
     assert torch.equal(c1, c2)

@@ -206,3 +206,7 @@ def test_quant_weight(pf, n, k):
     assert np.array_equal(host(out["s"]).view(np.uint32), s.view(np.uint32))
     out2 = pf.quant_weight(dev(w), transpose=False)
     assert np.array_equal(host(out2["q"]), q) and "qt" not in out2
+    out3 = pf.quant_weight(dev(w), transpose=True, codes=False)     # transposed copy only
+    assert "q" not in out3
+    assert np.array_equal(host(out3["qt"]), qt)
+    assert np.array_equal(host(out3["s"]).view(np.uint32), s.view(np.uint32))
