@@ -99,6 +99,10 @@ def _load():
         lib.orc_swiglu_fwd.argtypes = [P, I64, I64, ctypes.c_double, P, P, P]
         lib.orc_swiglu_bwd.restype = ctypes.c_int
         lib.orc_swiglu_bwd.argtypes = [P, P, I64, I64, ctypes.c_double, P, P, P]
+        lib.orc_rmsnorm_bwd.restype = ctypes.c_int
+        lib.orc_rmsnorm_bwd.argtypes = [P, P, P, P, P, I64, I64, ctypes.c_double, P, P, P]
+        lib.orc_residual_add.restype = ctypes.c_int
+        lib.orc_residual_add.argtypes = [P, P, I64, P]
         lib.orc_rmsnorm_fwd.restype = ctypes.c_int
         lib.orc_rmsnorm_fwd.argtypes = [P, P, I64, I64, ctypes.c_double, ctypes.c_double, P, P, P,
                                         P]
@@ -366,6 +370,39 @@ def rmsnorm_fwd(x_bits: np.ndarray, gamma_bits: np.ndarray, eps: float, tol: flo
     _check(_load().orc_rmsnorm_fwd(_ptr(x), _ptr(gamma), rows, cols, float(eps), float(tol),
                                    _ptr(y), _ptr(lo), _ptr(hi), _ptr(rstd)), "rmsnorm_fwd")
     return y, lo, hi, rstd
+
+
+def rmsnorm_bwd(dy_bits: np.ndarray, x_bits: np.ndarray, gamma_bits: np.ndarray,
+                rstd: np.ndarray, gin_bits, tol: float):
+    """RMSNorm backward + residual add: dy, x, gin (or None) uint16 [rows,
+    cols], gamma uint16 [cols], rstd float32 [rows] (the forward's) ->
+    (y, lo, hi) uint16 [rows, cols]."""
+    dy = _c(dy_bits, np.uint16)
+    x = _c(x_bits, np.uint16)
+    gamma = _c(gamma_bits, np.uint16)
+    rs = _c(rstd, np.float32)
+    rows, cols = x.shape
+    if dy.shape != (rows, cols) or gamma.shape != (cols,) or rs.shape != (rows,):
+        raise ValueError("rmsnorm_bwd: shapes")
+    gin = None if gin_bits is None else _c(gin_bits, np.uint16)
+    if gin is not None and gin.shape != (rows, cols):
+        raise ValueError("rmsnorm_bwd: gin shape")
+    y, lo, hi = _three((rows, cols))
+    _check(_load().orc_rmsnorm_bwd(_ptr(dy), _ptr(x), _ptr(gamma), _ptr(rs),
+                                   None if gin is None else _ptr(gin), rows, cols, float(tol),
+                                   _ptr(y), _ptr(lo), _ptr(hi)), "rmsnorm_bwd")
+    return y, lo, hi
+
+
+def residual_add(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
+    """h = a + b of two bf16 arrays (uint16 bits), rounded once to bf16."""
+    a = _c(a_bits, np.uint16)
+    b = _c(b_bits, np.uint16)
+    if a.shape != b.shape:
+        raise ValueError("residual_add: shapes")
+    h = np.empty(a.shape, np.uint16)
+    _check(_load().orc_residual_add(_ptr(a), _ptr(b), a.size, _ptr(h)), "residual_add")
+    return h
 
 
 def set_threads(n: int) -> None:

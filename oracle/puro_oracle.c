@@ -673,6 +673,75 @@ static void rmsnorm_fwd_rows(void* p, int64_t r0, int64_t r1)
     }
 }
 
+/* RMSNorm backward fused with the residual add.  The forward is
+ * y_j = x_j * rstd * gamma_j with rstd = (mean over i of x_i^2 + eps)^(-1/2),
+ * so d rstd / d x_i = -rstd^3 x_i / cols and the gradient reaching x through
+ * the norm is
+ *   rstd * gamma_j * dy_j - x_j * rstd^3 * c,   c = (1/cols) sum_i gamma_i dy_i x_i.
+ * The residual-stream gradient gin (the branch's skip path; NULL = 0) adds to
+ * it: out_j = gin_j + that.  rstd is the forward's FP32 value, taken as
+ * given.  M_j = |gin_j| + |rstd gamma_j dy_j| + |x_j| rstd^3 (1/cols)
+ * sum_i |gamma_i dy_i x_i| (the terms can cancel, and an error in c enters
+ * multiplied by x_j rstd^3). */
+typedef struct {
+    const uint16_t *dy, *x, *gamma, *gin;
+    const float* rstd;
+    int64_t cols;
+    double tol;
+    uint16_t *y, *lo, *hi;
+} nbb_ctx;
+
+static void rmsnorm_bwd_rows(void* p, int64_t r0, int64_t r1)
+{
+    nbb_ctx* a = (nbb_ctx*)p;
+    const int64_t n = a->cols;
+    for (int64_t r = r0; r < r1; ++r) {
+        const double rs = (double)a->rstd[r];
+        double c = 0.0, cabs = 0.0;
+        for (int64_t i = 0; i < n; ++i) {
+            const double t = bf16_to_f64(a->gamma[i]) * bf16_to_f64(a->dy[r * n + i]) *
+                             bf16_to_f64(a->x[r * n + i]);
+            c += t;
+            cabs += fabs(t);
+        }
+        c /= (double)n;
+        cabs /= (double)n;
+        const double rs3 = rs * rs * rs;
+        for (int64_t j = 0; j < n; ++j) {
+            const int64_t e = r * n + j;
+            const double gin = a->gin ? bf16_to_f64(a->gin[e]) : 0.0;
+            const double xj = bf16_to_f64(a->x[e]);
+            const double t1 = rs * bf16_to_f64(a->gamma[j]) * bf16_to_f64(a->dy[e]);
+            const double t2 = xj * rs3 * c;
+            const double v = gin + t1 - t2;
+            const double m = fabs(gin) + fabs(t1) + fabs(xj) * rs3 * cabs;
+            round_band(v, a->tol * m, &a->y[e], &a->lo[e], &a->hi[e]);
+        }
+    }
+}
+
+int orc_rmsnorm_bwd(const uint16_t* dy, const uint16_t* x, const uint16_t* gamma,
+                    const float* rstd, const uint16_t* gin, int64_t rows, int64_t cols,
+                    double tol, uint16_t* y, uint16_t* lo, uint16_t* hi)
+{
+    if (rows < 0 || cols <= 0 || !dy || !x || !gamma || !rstd || !y || !lo || !hi ||
+        !(tol >= 0.0))
+        return -1;
+    nbb_ctx c = {.dy = dy, .x = x, .gamma = gamma, .gin = gin, .rstd = rstd, .cols = cols,
+                 .tol = tol, .y = y, .lo = lo, .hi = hi};
+    parallel_for(rows, rmsnorm_bwd_rows, &c);
+    return 0;
+}
+
+int orc_residual_add(const uint16_t* a, const uint16_t* b, int64_t n, uint16_t* h)
+{
+    if (n < 0 || !a || !b || !h)
+        return -1;
+    for (int64_t i = 0; i < n; ++i)
+        h[i] = orc_f64_to_bf16(bf16_to_f64(a[i]) + bf16_to_f64(b[i]));
+    return 0;
+}
+
 int orc_swiglu_fwd(const uint16_t* gu, int64_t rows, int64_t f, double tol, uint16_t* y,
                    uint16_t* lo, uint16_t* hi)
 {

@@ -136,6 +136,22 @@ int orc_swiglu_bwd(const uint16_t* dh, const uint16_t* gu, int64_t rows, int64_t
 int orc_rmsnorm_fwd(const uint16_t* x, const uint16_t* gamma, int64_t rows, int64_t cols,
                     double eps, double tol, uint16_t* y, uint16_t* lo, uint16_t* hi,
                     double* rstd);
+/* RMSNorm backward fused with the residual add (the output gradient of the
+ * projection that writes the residual stream: out-proj, down): with the
+ * forward's FP32 rstd taken as given,
+ *   out[r][j] = gin[r][j] + rstd[r] * gamma[j] * dy[r][j]
+ *               - x[r][j] * rstd[r]^3 * (1/cols) sum_i gamma[i] dy[r][i] x[r][i]
+ * in double, rounded once to bf16 with its band (gin NULL = 0).  The
+ * derivative of y = x * rstd * gamma (rstd = (mean x^2 + eps)^(-1/2)) by the
+ * chain rule, plus the skip path. */
+int orc_rmsnorm_bwd(const uint16_t* dy, const uint16_t* x, const uint16_t* gamma,
+                    const float* rstd, const uint16_t* gin, int64_t rows, int64_t cols,
+                    double tol, uint16_t* y, uint16_t* lo, uint16_t* hi);
+/* The residual add that forms an RMSNorm's input: h[i] = a[i] + b[i], the
+ * exact sum of the two bf16 values rounded once to bf16 (nearest even).  The
+ * norm's statistic of h is orc_rmsnorm_fwd's rstd.  Return 0, or -1 on a bad
+ * argument. */
+int orc_residual_add(const uint16_t* a, const uint16_t* b, int64_t n, uint16_t* h);
 /* The SwiGLU arithmetic above at one point, unrounded: out4 = {h, d gate,
  * d up, M of d gate} for gate g, up u and upstream gradient dh. */
 void orc_swiglu_point(double g, double u, double dh, double* out4);

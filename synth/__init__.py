@@ -29,7 +29,7 @@ import torch
 
 __all__ = ["normal", "student_t3", "with_outliers", "bits", "from_bits",
            "LinearSpec", "WORKLOADS", "workload", "linear_inputs", "swiglu_inputs",
-           "rmsnorm_inputs"]
+           "rmsnorm_inputs", "rmsnorm_bwd_inputs", "residual_inputs"]
 
 
 def _gen(seed: int, stream: str) -> torch.Generator:
@@ -177,7 +177,10 @@ def linear_inputs(spec: LinearSpec, seed: int = 0, need=("x", "w", "dy")) -> dic
 # N(0, 1) with 1% of its columns x4 (|gate| stays below ~20); the gradient of
 # the SwiGLU output as N(0, 1e-3) like the other output gradients; the
 # residual stream entering RMSNorm as N(0, 1) with 1% of channels x20 like the
-# linear inputs; the learned RMSNorm gain as 1 + N(0, 0.1).
+# linear inputs; the learned RMSNorm gain as 1 + N(0, 0.1); the gradients
+# reaching the norm's backward (from the next projection's DGRAD, and along
+# the skip path) as N(0, 1e-3) like the other output gradients; the
+# projection output added to the residual stream as N(0, 1).
 
 def swiglu_inputs(rows: int, f: int, seed: int = 0, need=("gu", "dh")) -> dict:
     """bf16 CPU tensors gu [rows, 2f] (gate | up) and dh [rows, f]."""
@@ -200,3 +203,21 @@ def rmsnorm_inputs(rows: int, cols: int, seed: int = 0) -> dict:
     with_outliers(x, _pct_channels(cols), 20.0, seed, base + "/x")
     gamma = 1.0 + normal((cols,), 0.1, seed, base + "/gamma")
     return {"x": x.to(torch.bfloat16), "gamma": gamma.to(torch.bfloat16)}
+
+
+def rmsnorm_bwd_inputs(rows: int, cols: int, seed: int = 0) -> dict:
+    """bf16 CPU tensors x [rows, cols], gamma [cols] (as rmsnorm_inputs), the
+    gradient dy of the norm's output and gin of the skip path [rows, cols]."""
+    out = rmsnorm_inputs(rows, cols, seed)
+    base = f"rmsnorm_bwd/{rows}x{cols}"
+    out["dy"] = normal((rows, cols), 1e-3, seed, base + "/dy").to(torch.bfloat16)
+    out["gin"] = normal((rows, cols), 1e-3, seed, base + "/gin").to(torch.bfloat16)
+    return out
+
+
+def residual_inputs(rows: int, cols: int, seed: int = 0) -> dict:
+    """bf16 CPU tensors a (the residual stream, as rmsnorm_inputs' x) and b
+    (a projection's output) [rows, cols], and gamma [cols]."""
+    d = rmsnorm_inputs(rows, cols, seed)
+    b = normal((rows, cols), 1.0, seed, f"residual/{rows}x{cols}/b").to(torch.bfloat16)
+    return {"a": d["x"], "b": b, "gamma": d["gamma"]}

@@ -207,3 +207,134 @@ def test_rmsnorm_eps(orc):
     y, _, _, rstd = orc.rmsnorm_fwd(x, gamma, eps=2.0**-20, tol=2.0**-18)
     assert rstd[0] == 1024.0
     assert y[0, 0] == 0x0000 and y[0, 1] == 0x8000
+
+
+# ---- RMSNorm backward plus the skip path ----------------------------------------
+
+def _f(bits):
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _rstd32(xb, eps):
+    x = _f(xb)
+    return (1.0 / np.sqrt(np.mean(x * x, axis=1) + eps)).astype(np.float32)
+
+
+def test_rmsnorm_bwd_golden(orc):
+    rows = _golden("rmsnorm_bwd")
+    assert len(rows) == 3
+    for x0, x1, g0, g1, d0, d1, i0, i1, o0, o1 in rows:
+        x = np.array([[x0, x1]], np.uint16)
+        rstd = np.array([math.sqrt(2.0) / 5.0], np.float32)
+        gin = np.array([[i0, i1]], np.uint16)
+        y, lo, hi = orc.rmsnorm_bwd(np.array([[d0, d1]], np.uint16), x,
+                                    np.array([g0, g1], np.uint16), rstd,
+                                    gin if (i0 or i1) else None, 2.0**-18)
+        assert y.tolist() == [[o0, o1]], [hex(v) for v in y.ravel()]
+        assert np.array_equal(lo, y) and np.array_equal(hi, y)
+
+
+@pytest.mark.parametrize("eps", [0.0, 1e-2])
+def test_rmsnorm_bwd_is_the_derivative_of_the_forward(orc, eps):
+    """Central differences of the forward y = x gamma / sqrt(mean x^2 + eps),
+    written here in double, give gin + J^T dy; the oracle's bf16 result is
+    that value rounded (within half a bf16 ulp plus the FP32 rstd's effect)."""
+    rng = np.random.default_rng(11)
+    rows, cols = 3, 24
+    xb = _to_bf16_torch(rng.standard_normal((rows, cols)) * np.array([[1.0], [0.05], [7.0]]))
+    gb = _to_bf16_torch(rng.standard_normal(cols))
+    dyb = _to_bf16_torch(rng.standard_normal((rows, cols)))
+    ginb = _to_bf16_torch(rng.standard_normal((rows, cols)) * 0.1)
+    rstd = _rstd32(xb, eps)
+    y, lo, hi = orc.rmsnorm_bwd(dyb, xb, gb, rstd, ginb, 2.0**-18)
+    x, g, dy, gin = _f(xb), _f(gb), _f(dyb), _f(ginb)
+
+    def loss(xr, dyr):
+        return float(np.sum(dyr * xr * g / math.sqrt(np.mean(xr * xr) + eps)))
+
+    got = _f(y)
+    for r in range(rows):
+        h = 1e-4 * float(np.max(np.abs(x[r])))
+        for i in range(cols):
+            xp, xm = x[r].copy(), x[r].copy()
+            xp[i] += h
+            xm[i] -= h
+            fd = gin[r, i] + (loss(xp, dy[r]) - loss(xm, dy[r])) / (2.0 * h)
+            rs = 1.0 / math.sqrt(np.mean(x[r] ** 2) + eps)
+            m = abs(gin[r, i]) + abs(rs * g[i] * dy[r, i]) + \
+                abs(x[r, i]) * rs ** 3 * float(np.mean(np.abs(g * dy[r] * x[r])))
+            assert abs(got[r, i] - fd) <= 2.0**-8 * abs(fd) + 1e-6 * m, (r, i, got[r, i], fd)
+    assert np.all(_f(lo) <= got) and np.all(got <= _f(hi))
+
+
+def test_rmsnorm_bwd_orthogonal_to_x(orc):
+    """eps = 0 makes y invariant under x -> a x, so J x = 0 and sum_i x_i out_i
+    = 0 without the skip path (up to the bf16 rounding of out)."""
+    rng = np.random.default_rng(12)
+    rows, cols = 5, 256
+    xb = _to_bf16_torch(rng.standard_normal((rows, cols)))
+    gb = _to_bf16_torch(1.0 + 0.3 * rng.standard_normal(cols))
+    # dy partly along x, so the two terms are large and must cancel
+    dyb = _to_bf16_torch(0.7 * _f(xb) + 0.7 * rng.standard_normal((rows, cols)))
+    y, _, _ = orc.rmsnorm_bwd(dyb, xb, gb, _rstd32(xb, 0.0), None, 0.0)
+    p = _f(xb) * _f(y)
+    assert np.all(np.abs(p.sum(axis=1)) <= 2.0**-8 * np.abs(p).sum(axis=1))
+    # the pieces do not cancel on their own: without the second term the sum
+    # is O(1) of its magnitude
+    direct = _f(xb) * _rstd32(xb, 0.0)[:, None] * _f(gb) * _f(dyb)
+    assert np.all(np.abs(direct.sum(axis=1)) > 0.25 * np.abs(direct).sum(axis=1))
+
+
+def test_rmsnorm_bwd_scaling(orc):
+    """eps = 0: x -> 2x (rstd -> rstd/2, exact) halves out; dy -> 2 dy doubles
+    it; (gamma, dy) -> (2 gamma, dy/2) leaves it unchanged -- all bit-exact
+    exponent shifts of every nonzero bf16 result."""
+    rng = np.random.default_rng(13)
+    rows, cols = 4, 384
+    xf = rng.standard_normal((rows, cols))
+    xb, x2b = _to_bf16_torch(xf), _to_bf16_torch(2.0 * xf)
+    gf = rng.standard_normal(cols)
+    gb, g2b = _to_bf16_torch(gf), _to_bf16_torch(2.0 * gf)
+    dyf = rng.standard_normal((rows, cols))
+    dyb, dy2b, dyhb = (_to_bf16_torch(dyf), _to_bf16_torch(2.0 * dyf),
+                       _to_bf16_torch(0.5 * dyf))
+    rs = _rstd32(xb, 0.0)
+    y, _, _ = orc.rmsnorm_bwd(dyb, xb, gb, rs, None, 0.0)
+    yx2, _, _ = orc.rmsnorm_bwd(dyb, x2b, gb, rs / np.float32(2.0), None, 0.0)
+    ydy2, _, _ = orc.rmsnorm_bwd(dy2b, xb, gb, rs, None, 0.0)
+    yg2, _, _ = orc.rmsnorm_bwd(dyhb, xb, g2b, rs, None, 0.0)
+    nz = (y & 0x7FFF) != 0
+    assert nz.mean() > 0.99
+    assert np.array_equal(yx2[nz], y[nz] - 0x80)
+    assert np.array_equal(ydy2[nz], y[nz] + 0x80)
+    assert np.array_equal(yg2, y)
+
+
+def test_rmsnorm_bwd_skip_path_alone(orc):
+    """dy = 0: out is gin, bit for bit, with a one-value band."""
+    rng = np.random.default_rng(14)
+    rows, cols = 3, 128
+    xb = _to_bf16_torch(rng.standard_normal((rows, cols)))
+    ginb = _to_bf16_torch(rng.standard_normal((rows, cols)))
+    y, lo, hi = orc.rmsnorm_bwd(np.zeros((rows, cols), np.uint16), xb,
+                                _to_bf16_torch(rng.standard_normal(cols)), _rstd32(xb, 0.0),
+                                ginb, 2.0**-18)
+    assert np.array_equal(y, ginb) and np.array_equal(lo, ginb) and np.array_equal(hi, ginb)
+
+
+def test_residual_add_matches_torch(orc):
+    """h = a + b rounded once to bf16, against PyTorch's bf16 addition, over a
+    spread of binades (the FP32 sum of two bf16 values rounds to the same
+    bf16 as the exact sum), plus signed zeros and cancellation."""
+    import torch
+    rng = np.random.default_rng(15)
+    n = 1 << 16
+    a = _to_bf16_torch(rng.standard_normal(n) * np.exp2(rng.integers(-30, 30, n)))
+    b = _to_bf16_torch(rng.standard_normal(n) * np.exp2(rng.integers(-30, 30, n)))
+    a[:4] = [0x0000, 0x8000, 0x3F80, 0x4049]
+    b[:4] = [0x8000, 0x8000, 0xBF80, 0xC049]
+    want = (torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+            + torch.from_numpy(b.view(np.int16)).view(torch.bfloat16)).view(torch.int16).numpy()
+    h = orc.residual_add(a, b)
+    assert np.array_equal(h, want.view(np.uint16))
+    assert h[:4].tolist() == [0x0000, 0x8000, 0x0000, 0x0000]
