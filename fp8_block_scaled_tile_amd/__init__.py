@@ -34,6 +34,8 @@ __all__ = [
     "puro_bf16_gemm_nt", "puro_bf16_gemm_nt_workspace_bytes", "gemm_bf16_nt",
     "puro_fp8_swiglu_quant", "puro_fp8_swiglu_bwd_quant", "puro_fp8_rmsnorm_quant",
     "swiglu_quant", "swiglu_bwd_quant", "rmsnorm_quant", "library_path",
+    "puro_fp8_rmsnorm_quant_rstd", "puro_fp8_rmsnorm_bwd_quant", "puro_bf16_residual_add_rstd",
+    "rmsnorm_quant_rstd", "rmsnorm_bwd_quant", "residual_add_rstd",
 ]
 
 GEMM_FWD, GEMM_DGRAD, GEMM_WGRAD, GEMM_DGRAD_W, GEMM_FWD_T = 0, 1, 2, 3, 4
@@ -117,6 +119,21 @@ def puro_fp8_swiglu_bwd_quant(dh, gu, rows, f, q, s, qt, st, y, stream) -> int:
 def puro_fp8_rmsnorm_quant(x, gamma, rows, cols, eps, rstd, q, s, qt, st, y, stream) -> int:
     return _lib.get().puro_fp8_rmsnorm_quant(x, gamma, rows, cols, eps, rstd, q, s, qt, st, y,
                                              stream)
+
+
+def puro_fp8_rmsnorm_quant_rstd(x, gamma, rstd, rows, cols, q, s, qt, st, y, stream) -> int:
+    return _lib.get().puro_fp8_rmsnorm_quant_rstd(x, gamma, rstd, rows, cols, q, s, qt, st, y,
+                                                  stream)
+
+
+def puro_fp8_rmsnorm_bwd_quant(dy, x, gamma, rstd, gin, rows, cols, coef, q, s, qt, st, y,
+                               stream) -> int:
+    return _lib.get().puro_fp8_rmsnorm_bwd_quant(dy, x, gamma, rstd, gin, rows, cols, coef, q, s,
+                                                 qt, st, y, stream)
+
+
+def puro_bf16_residual_add_rstd(a, b, rows, cols, eps, h, rstd, stream) -> int:
+    return _lib.get().puro_bf16_residual_add_rstd(a, b, rows, cols, eps, h, rstd, stream)
 
 
 # ---- torch-facing wrappers --------------------------------------------------
@@ -256,6 +273,81 @@ def rmsnorm_quant(x, gamma, eps: float = 1e-6, row: bool = True, col: bool = Tru
                                   _ptr(out.get("q")), _ptr(out.get("s")), _ptr(out.get("qt")),
                                   _ptr(out.get("st")), _ptr(out.get("y")), _stream(stream)))
     return out
+
+
+def _gamma(gamma, cols, *others):
+    torch = _torch()
+    if gamma.dtype != torch.bfloat16 or tuple(gamma.shape) != (cols,):
+        raise TypeError("gamma: expected a bfloat16 tensor of shape [cols]")
+    _same_device(gamma, *others)
+    return gamma.contiguous()
+
+
+def _rstd(rstd, rows, dev):
+    torch = _torch()
+    if rstd.dtype != torch.float32 or tuple(rstd.shape) != (rows,):
+        raise TypeError("rstd: expected a float32 tensor of shape [rows]")
+    if rstd.device != dev:
+        raise ValueError("rstd: on a different device")
+    return rstd.contiguous()
+
+
+def rmsnorm_quant_rstd(x, gamma, rstd, row: bool = True, col: bool = True,
+                       bf16_out: bool = False, stream=None):
+    """As rmsnorm_quant with the row statistic rstd f32 [rows] given (as
+    residual_add_rstd returns it): one pass over x."""
+    x = _bf16_2d(x, "x")
+    rows, cols = x.shape
+    gamma = _gamma(gamma, cols, x)
+    rstd = _rstd(rstd, rows, x.device)
+    out = _produce_outputs(rows, cols, x.device, row, col, bf16_out)
+    _check(puro_fp8_rmsnorm_quant_rstd(_ptr(x), _ptr(gamma), _ptr(rstd), rows, cols,
+                                       _ptr(out.get("q")), _ptr(out.get("s")), _ptr(out.get("qt")),
+                                       _ptr(out.get("st")), _ptr(out.get("y")), _stream(stream)))
+    return out
+
+
+def rmsnorm_bwd_quant(dy, x, gamma, rstd, gin=None, row: bool = True, col: bool = True,
+                      bf16_out: bool = False, stream=None):
+    """RMSNorm backward plus the skip-path gradient gin (None = 0) as FP8
+    operands: gin + rstd*gamma*dy - x*rstd^3*mean(gamma*dy*x).  Also returns
+    ``coef`` f32 [rows] (the per-row second term's factor)."""
+    torch = _torch()
+    dy = _bf16_2d(dy, "dy")
+    x = _bf16_2d(x, "x")
+    rows, cols = x.shape
+    if tuple(dy.shape) != (rows, cols):
+        raise TypeError("dy: expected the shape of x")
+    gamma = _gamma(gamma, cols, x, dy)
+    rstd = _rstd(rstd, rows, x.device)
+    if gin is not None:
+        gin = _bf16_2d(gin, "gin")
+        if tuple(gin.shape) != (rows, cols):
+            raise TypeError("gin: expected the shape of x")
+        _same_device(x, gin)
+    out = _produce_outputs(rows, cols, x.device, row, col, bf16_out)
+    out["coef"] = torch.empty(rows, dtype=torch.float32, device=x.device)
+    _check(puro_fp8_rmsnorm_bwd_quant(_ptr(dy), _ptr(x), _ptr(gamma), _ptr(rstd), _ptr(gin), rows,
+                                      cols, _ptr(out["coef"]), _ptr(out.get("q")),
+                                      _ptr(out.get("s")), _ptr(out.get("qt")), _ptr(out.get("st")),
+                                      _ptr(out.get("y")), _stream(stream)))
+    return out
+
+
+def residual_add_rstd(a, b, eps: float = 1e-6, stream=None):
+    """h = a + b (bf16) and the RMSNorm statistic of h, rstd f32 [rows]."""
+    torch = _torch()
+    a = _bf16_2d(a, "a")
+    b = _bf16_2d(b, "b")
+    if a.shape != b.shape:
+        raise TypeError("residual_add_rstd: a and b differ in shape")
+    _same_device(a, b)
+    rows, cols = a.shape
+    h = torch.empty_like(a)
+    rstd = torch.empty(rows, dtype=torch.float32, device=a.device)
+    _check(puro_bf16_residual_add_rstd(_ptr(a), _ptr(b), rows, cols, float(eps), _ptr(h), _ptr(rstd),
+                                  _stream(stream)))
+    return {"h": h, "rstd": rstd}
 
 
 def quant_weight(w, transpose: bool = True, codes: bool = True, stream=None):

@@ -17,6 +17,7 @@ EXPORTS = (
     "puro_fp8_probe_encode", "puro_bf16_gemm_nt", "puro_bf16_gemm_nt_workspace_bytes",
     "puro_fp8_swiglu_quant", "puro_fp8_swiglu_bwd_quant", "puro_fp8_rmsnorm_quant",
     "puro_fp8_probe_sigmoid", "puro_fp8_probe_mfma", "puro_fp8_gemm_blockscaled_noalloc",
+    "puro_fp8_rmsnorm_quant_rstd", "puro_fp8_rmsnorm_bwd_quant", "puro_bf16_residual_add_rstd",
 )
 
 
@@ -68,5 +69,11 @@ def get():
         lib.puro_fp8_rmsnorm_quant.restype = I
         lib.puro_fp8_rmsnorm_quant.argtypes = [P, P, I64, I64, ctypes.c_float, P, P, P, P, P, P,
                                                P]
+        lib.puro_fp8_rmsnorm_quant_rstd.restype = I
+        lib.puro_fp8_rmsnorm_quant_rstd.argtypes = [P, P, P, I64, I64, P, P, P, P, P, P]
+        lib.puro_fp8_rmsnorm_bwd_quant.restype = I
+        lib.puro_fp8_rmsnorm_bwd_quant.argtypes = [P, P, P, P, P, I64, I64, P, P, P, P, P, P, P]
+        lib.puro_bf16_residual_add_rstd.restype = I
+        lib.puro_bf16_residual_add_rstd.argtypes = [P, P, I64, I64, ctypes.c_float, P, P, P]
         _handle = lib
         return lib

@@ -297,6 +297,63 @@ puro_status_t puro_bf16_gemm_nt(int64_t M, int64_t N, int64_t K, const void* a, 
     });
 }
 
+puro_status_t puro_fp8_rmsnorm_quant_rstd(const void* x, const void* gamma, const float* rstd,
+                                          int64_t rows, int64_t cols, uint8_t* q, float* s,
+                                          uint8_t* qt, float* st, void* y, void* stream)
+{
+    return guarded([&]() -> puro_status_t {
+        const puro_status_t rc = check_produce(x && gamma && rstd,
+                                               aligned16(x) && aligned16(gamma) && aligned16(rstd),
+                                               rows, cols, q, s, qt, st, y);
+        if (rc != PURO_OK || rows == 0)
+            return rc;
+        return from_hip(puro::launch_rmsnorm_quant_rstd(x, gamma, rstd, rows, cols, q, s, qt, st,
+                                                        y, static_cast<hipStream_t>(stream)));
+    });
+}
+
+puro_status_t puro_fp8_rmsnorm_bwd_quant(const void* dy, const void* x, const void* gamma,
+                                         const float* rstd, const void* gin, int64_t rows,
+                                         int64_t cols, float* coef, uint8_t* q, float* s,
+                                         uint8_t* qt, float* st, void* y, void* stream)
+{
+    return guarded([&]() -> puro_status_t {
+        const puro_status_t rc =
+            check_produce(dy && x && gamma && rstd && coef,
+                          aligned16(dy) && aligned16(x) && aligned16(gamma) && aligned16(rstd) &&
+                              aligned16(coef) && (!gin || aligned16(gin)),
+                          rows, cols, q, s, qt, st, y);
+        if (rc != PURO_OK)
+            return rc;
+        if ((rows + 3) / 4 > kMaxDim)        // the statistics pass runs 4 rows per work-group
+            return PURO_ERR_BAD_SHAPE;
+        if (rows == 0)
+            return PURO_OK;
+        return from_hip(puro::launch_rmsnorm_bwd_quant(dy, x, gamma, rstd, gin, rows, cols, coef,
+                                                       q, s, qt, st, y,
+                                                       static_cast<hipStream_t>(stream)));
+    });
+}
+
+puro_status_t puro_bf16_residual_add_rstd(const void* a, const void* b, int64_t rows, int64_t cols,
+                                     float eps, void* h, float* rstd, void* stream)
+{
+    return guarded([&]() -> puro_status_t {
+        if (rows < 0 || cols <= 0 || cols % 128 != 0 || cols > kMaxDim || (rows + 3) / 4 > kMaxDim)
+            return PURO_ERR_BAD_SHAPE;
+        if (rows == 0)
+            return PURO_OK;
+        if (!a || !b || !h || !rstd)
+            return PURO_ERR_NULL_POINTER;
+        if (!aligned16(a) || !aligned16(b) || !aligned16(h) || !aligned16(rstd))
+            return PURO_ERR_MISALIGNED;
+        if (!(eps >= 0.0f) || eps > std::numeric_limits<float>::max())
+            return PURO_ERR_BAD_VALUE;
+        return from_hip(puro::launch_residual_rstd(a, b, rows, cols, eps, h, rstd,
+                                                   static_cast<hipStream_t>(stream)));
+    });
+}
+
 puro_status_t puro_fp8_probe_encode(uint32_t first_bits, int64_t n, uint8_t* out, void* stream)
 {
     return guarded([&]() -> puro_status_t {

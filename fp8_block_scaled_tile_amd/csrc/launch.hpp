@@ -45,6 +45,15 @@ hipError_t launch_swiglu_bwd_quant(const void* dh, const void* gu, int64_t rows,
 hipError_t launch_rmsnorm_quant(const void* x, const void* gamma, int64_t rows, int64_t cols,
                                 float eps, float* rstd, uint8_t* q, float* s, uint8_t* qt,
                                 float* st, void* y, hipStream_t stream);
+hipError_t launch_rmsnorm_quant_rstd(const void* x, const void* gamma, const float* rstd,
+                                     int64_t rows, int64_t cols, uint8_t* q, float* s,
+                                     uint8_t* qt, float* st, void* y, hipStream_t stream);
+hipError_t launch_rmsnorm_bwd_quant(const void* dy, const void* x, const void* gamma,
+                                    const float* rstd, const void* gin, int64_t rows, int64_t cols,
+                                    float* coef, uint8_t* q, float* s, uint8_t* qt, float* st,
+                                    void* y, hipStream_t stream);
+hipError_t launch_residual_rstd(const void* a, const void* b, int64_t rows, int64_t cols, float eps,
+                                void* h, float* rstd, hipStream_t stream);
 hipError_t launch_probe_encode(uint32_t first, int64_t n, uint8_t* out, hipStream_t stream);
 hipError_t launch_probe_sigmoid(uint32_t first, int64_t n, float* out, hipStream_t stream);
 hipError_t launch_probe_mfma(int form, const uint8_t* a, const uint8_t* b, int scale_a,

@@ -272,6 +272,138 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(
                                                  lds);
 }
 
+// ---- RMSNorm backward fused with the residual add --------------------------
+// The output gradient of the projection that writes the residual stream
+// (out-proj, down): out = gin + rstd * gamma * dy - x * rstd^3 * c with
+// c = (1/cols) sum_i gamma_i dy_i x_i per row (the norm's derivative by the
+// chain rule, plus the skip path gin).  Two kernels, as for the forward: the
+// per-row coefficient k = rstd^3 * c (one wave per row), then the fused
+// elementwise pass that quantizes the bf16 result block by block.
+
+__global__ __launch_bounds__(256) void rmsnorm_bwd_coef_kernel(
+    const uint16_t* __restrict__ dy, const uint16_t* __restrict__ x,
+    const uint16_t* __restrict__ gamma, const float* __restrict__ rstd, int64_t rows,
+    int64_t cols, float* __restrict__ coef)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= rows)
+        return;
+    float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t c = 8 * lane; c < cols; c += 512) {
+        const uint4 dv = load16(dy + r * cols + c);
+        const uint4 xv = load16(x + r * cols + c);
+        const uint4 gv = load16(gamma + c);
+        const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w};
+        const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+        const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[2 * i] = __builtin_fmaf(bf16_lo(gw[i]) * bf16_lo(dw[i]), bf16_lo(xw[i]), acc[2 * i]);
+            acc[2 * i + 1] =
+                __builtin_fmaf(bf16_hi(gw[i]) * bf16_hi(dw[i]), bf16_hi(xw[i]), acc[2 * i + 1]);
+        }
+    }
+    float sum = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        sum += __shfl_xor(sum, off, 64);
+    if (lane == 0) {
+        const float rs = rstd[r];
+        coef[r] = ((rs * rs) * rs) * (sum / (float)cols);
+    }
+}
+
+template <bool ROW, bool COL, bool STORE_Y>
+__global__ __launch_bounds__(256) void rmsnorm_bwd_quant_kernel(
+    const uint16_t* __restrict__ dy, const uint16_t* __restrict__ x,
+    const uint16_t* __restrict__ gamma, const float* __restrict__ rstd,
+    const float* __restrict__ coef, const uint16_t* __restrict__ gin, int64_t rows, int64_t cols,
+    int64_t ld_t, uint8_t* __restrict__ q, float* __restrict__ s, uint8_t* __restrict__ qt,
+    float* __restrict__ st, uint16_t* __restrict__ y, int group_rows)
+{
+    __shared__ QuantLds<ROW, COL, false, false> lds;
+    const int t = threadIdx.x;
+    const BlockRC b = block_of(blockIdx.x, ld_t / 128, cols / 128, group_rows);
+    const int64_t row0 = b.rb * 128 + 8 * (t >> 4);
+    const int64_t col0 = b.cb * 128 + 8 * (t & 15);
+
+    uint4 dv[8], xv[8], iv[8];
+    float rs[8], kc[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const int64_t r = row0 + p;
+        const bool in = r < rows;
+        dv[p] = in ? load16(dy + r * cols + col0) : kZero4;
+        xv[p] = in ? load16(x + r * cols + col0) : kZero4;
+        iv[p] = (in && gin) ? load16(gin + r * cols + col0) : kZero4;
+        rs[p] = in ? rstd[r] : 0.0f;
+        kc[p] = in ? coef[r] : 0.0f;
+    }
+    const uint4 gv = load16(gamma + col0);
+    const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+    uint4 v[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const uint32_t dw[4] = {dv[p].x, dv[p].y, dv[p].z, dv[p].w};
+        const uint32_t xw[4] = {xv[p].x, xv[p].y, xv[p].z, xv[p].w};
+        const uint32_t iw[4] = {iv[p].x, iv[p].y, iv[p].z, iv[p].w};
+        // out = gin + (rstd * gamma) * dy - x * k, two FMAs
+        auto f = [&](float d, float xe, float ie, float g) __attribute__((always_inline)) {
+            return __builtin_fmaf(-xe, kc[p], __builtin_fmaf(rs[p] * g, d, ie));
+        };
+        uint32_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            o[i] = pack_bf16(f(bf16_lo(dw[i]), bf16_lo(xw[i]), bf16_lo(iw[i]), bf16_lo(gw[i])),
+                             f(bf16_hi(dw[i]), bf16_hi(xw[i]), bf16_hi(iw[i]), bf16_hi(gw[i])));
+        v[p] = row0 + p < rows ? make_uint4(o[0], o[1], o[2], o[3]) : kZero4;
+        if (STORE_Y && row0 + p < rows)
+            store16(y + (row0 + p) * cols + col0, v[p]);
+    }
+    if constexpr (ROW || COL)
+        quant_block_body<ROW, COL, false, false>(v, rows, cols, ld_t, b.rb, b.cb, q, s, qt, st,
+                                                 lds);
+}
+
+// ---- the residual add that produces a norm's input, with its statistic -----
+// h = a + b (FP32 sum of the two bf16 values, rounded to bf16) and
+// rstd = 1 / sqrt(mean over the row of h^2 + eps), so the RMSNorm that reads h
+// needs one pass (puro_fp8_rmsnorm_quant_rstd).  One wave per row.
+__global__ __launch_bounds__(256) void residual_rstd_kernel(const uint16_t* __restrict__ a,
+                                                            const uint16_t* __restrict__ bb,
+                                                            int64_t rows, int64_t cols, float eps,
+                                                            uint16_t* __restrict__ h,
+                                                            float* __restrict__ rstd)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= rows)
+        return;
+    float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t c = 8 * lane; c < cols; c += 512) {
+        const uint4 av = load16(a + r * cols + c);
+        const uint4 bv = load16(bb + r * cols + c);
+        const uint32_t aw[4] = {av.x, av.y, av.z, av.w};
+        const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            o[i] = pack_bf16(bf16_lo(aw[i]) + bf16_lo(bw[i]), bf16_hi(aw[i]) + bf16_hi(bw[i]));
+            const float lo = bf16_lo(o[i]), hi = bf16_hi(o[i]);
+            acc[2 * i] = __builtin_fmaf(lo, lo, acc[2 * i]);
+            acc[2 * i + 1] = __builtin_fmaf(hi, hi, acc[2 * i + 1]);
+        }
+        store16(h + r * cols + c, make_uint4(o[0], o[1], o[2], o[3]));
+    }
+    float sum = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        sum += __shfl_xor(sum, off, 64);
+    if (lane == 0)
+        rstd[r] = 1.0f / sqrtf(sum / (float)cols + eps);
+}
+
 // ---- launchers --------------------------------------------------------------
 
 // Launches KERNEL<ROW, COL, STORE_Y> for the requested outputs (q, qt and
@@ -339,6 +471,50 @@ hipError_t launch_rmsnorm_quant(const void* x, const void* gamma, int64_t rows, 
     const int gr = quant_group_rows(false, cols);
     return PURO_DISPATCH_OUTPUTS(rmsnorm_quant_kernel, grid,
                                  (xb, gb, rstd, rows, cols, rows_pad, q, s, qt, st, y, gr));
+}
+
+hipError_t launch_rmsnorm_quant_rstd(const void* x, const void* gamma, const float* rstd,
+                                     int64_t rows, int64_t cols, uint8_t* q, float* s,
+                                     uint8_t* qt, float* st, void* yout, hipStream_t stream)
+{
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    const uint16_t* gb = static_cast<const uint16_t*>(gamma);
+    uint16_t* y = static_cast<uint16_t*>(yout);
+    const int64_t rows_pad = (rows + 127) / 128 * 128;
+    const dim3 grid((unsigned)((rows_pad / 128) * (cols / 128)));
+    const int gr = quant_group_rows(false, cols);
+    return PURO_DISPATCH_OUTPUTS(rmsnorm_quant_kernel, grid,
+                                 (xb, gb, rstd, rows, cols, rows_pad, q, s, qt, st, y, gr));
+}
+
+hipError_t launch_rmsnorm_bwd_quant(const void* dy, const void* x, const void* gamma,
+                                    const float* rstd, const void* gin, int64_t rows, int64_t cols,
+                                    float* coef, uint8_t* q, float* s, uint8_t* qt, float* st,
+                                    void* yout, hipStream_t stream)
+{
+    const uint16_t* db = static_cast<const uint16_t*>(dy);
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    const uint16_t* gb = static_cast<const uint16_t*>(gamma);
+    const uint16_t* ib = static_cast<const uint16_t*>(gin);
+    uint16_t* y = static_cast<uint16_t*>(yout);
+    const hipError_t e = launch_kernel(rmsnorm_bwd_coef_kernel, dim3((unsigned)((rows + 3) / 4)),
+                                       dim3(256), stream, db, xb, gb, rstd, rows, cols, coef);
+    if (e != hipSuccess)
+        return e;
+    const int64_t rows_pad = (rows + 127) / 128 * 128;
+    const dim3 grid((unsigned)((rows_pad / 128) * (cols / 128)));
+    const int gr = quant_group_rows(false, cols);
+    return PURO_DISPATCH_OUTPUTS(rmsnorm_bwd_quant_kernel, grid,
+                                 (db, xb, gb, rstd, coef, ib, rows, cols, rows_pad, q, s, qt, st,
+                                  y, gr));
+}
+
+hipError_t launch_residual_rstd(const void* a, const void* b, int64_t rows, int64_t cols, float eps,
+                                void* h, float* rstd, hipStream_t stream)
+{
+    return launch_kernel(residual_rstd_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), stream,
+                         static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b), rows,
+                         cols, eps, static_cast<uint16_t*>(h), rstd);
 }
 
 hipError_t launch_probe_sigmoid(uint32_t first, int64_t n, float* out, hipStream_t stream)

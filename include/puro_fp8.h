@@ -307,6 +307,53 @@ puro_status_t puro_fp8_rmsnorm_quant(const void* x, const void* gamma, int64_t r
                                      void* stream);
 
 /*
+ * RMSNorm forward with the row statistic handed over: as
+ * puro_fp8_rmsnorm_quant, but rstd f32 [rows] is an INPUT (as
+ * puro_bf16_residual_add_rstd writes it for the norm's input), so the call is one
+ * pass over x: the normalize-and-quantize kernel alone.
+ */
+puro_status_t puro_fp8_rmsnorm_quant_rstd(const void* x, const void* gamma, const float* rstd,
+                                          int64_t rows, int64_t cols, uint8_t* q, float* s,
+                                          uint8_t* qt, float* st, void* y, void* stream);
+
+/*
+ * RMSNorm backward fused with the residual add: the output gradient dY of the
+ * projection that writes the residual stream (the out-projection, and the
+ * previous block's down projection), as FP8 operands.
+ *   dy   bf16 [rows][cols]  gradient of the norm's output y (the next
+ *                           projection's DGRAD result)
+ *   x    bf16 [rows][cols]  the norm's input (the residual stream)
+ *   gamma bf16 [cols], rstd f32 [rows] as the forward used them
+ *   gin  bf16 [rows][cols]  gradient arriving along the skip path (NULL = 0)
+ *   coef f32 [rows]         written: rstd^3 * (1/cols) sum_i gamma_i dy_i x_i
+ * out (out_cols = cols) = gin + rstd * gamma * dy - x * coef, the derivative
+ * of y = x * rstd * gamma by the chain rule plus the skip path; the bf16
+ * result y (optional) is the gradient that continues down the residual
+ * stream.  Two kernels: the per-row coefficient, then the fused pass.  The
+ * FP32 error before the bf16 rounding is below (cols/512 + 18) * 2^-24 of
+ * M = |gin| + |rstd gamma dy| + |x| rstd^3 (1/cols) sum_i |gamma_i dy_i x_i|
+ * (under 2^-18 M for rows of up to 16384 columns); the bf16 value is one of
+ * the two neighbours of the exact result whenever that band allows both.
+ * rows, cols and outputs as for puro_fp8_rmsnorm_quant; rstd, coef and gin
+ * 16-byte aligned.
+ */
+puro_status_t puro_fp8_rmsnorm_bwd_quant(const void* dy, const void* x, const void* gamma,
+                                         const float* rstd, const void* gin, int64_t rows,
+                                         int64_t cols, float* coef, uint8_t* q, float* s,
+                                         uint8_t* qt, float* st, void* y, void* stream);
+
+/*
+ * The residual add that produces an RMSNorm's input, with the norm's row
+ * statistic: h bf16 [rows][cols] = a + b (the FP32 sum of the two bf16
+ * values, rounded to nearest even) and rstd f32 [rows] =
+ * 1 / sqrt(mean over the row of h^2 + eps), for puro_fp8_rmsnorm_quant_rstd.
+ * a, b, h bf16 [rows][cols]; cols a positive multiple of 128; eps finite and
+ * >= 0 (PURO_ERR_BAD_VALUE otherwise).
+ */
+puro_status_t puro_bf16_residual_add_rstd(const void* a, const void* b, int64_t rows, int64_t cols,
+                                     float eps, void* h, float* rstd, void* stream);
+
+/*
  * BF16 comparator (measurement only, not part of the FP8 path).
  *
  * The BF16 linear-layer GEMM the FP8 path replaces, on this library's own

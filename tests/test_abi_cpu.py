@@ -42,7 +42,8 @@ def test_header_declares_the_entry_points():
               "puro_fp8_abi_version", "puro_fp8_probe_encode", "puro_fp8_swiglu_quant",
               "puro_fp8_swiglu_bwd_quant", "puro_fp8_rmsnorm_quant", "puro_bf16_gemm_nt",
               "puro_fp8_probe_sigmoid", "puro_fp8_probe_mfma",
-              "puro_fp8_gemm_blockscaled_noalloc"):
+              "puro_fp8_gemm_blockscaled_noalloc", "puro_fp8_rmsnorm_quant_rstd",
+              "puro_fp8_rmsnorm_bwd_quant", "puro_bf16_residual_add_rstd"):
         assert n in names
 
 
@@ -243,3 +244,46 @@ def test_rmsnorm_quant_validation(lib):
     assert call(4, float("nan")) == VALUE
     assert call(4, float("inf")) == VALUE
     assert f(P16, P16, 0, 256, 1e-6, P16, P16, P16, None, None, None, None) == OK
+
+
+def test_rmsnorm_quant_rstd_validation(lib):
+    f = lib.puro_fp8_rmsnorm_quant_rstd
+    ok = (P16, P16, P16, 16, 256, P16, P16, None, None, None, None)
+    call = lambda i, v: f(*(ok[:i] + (v,) + ok[i + 1:]))
+    assert call(4, 200) == SHAPE
+    assert call(3, -1) == SHAPE
+    assert call(2, None) == NULLP                                          # rstd is an input
+    assert call(0, None) == NULLP
+    assert call(2, P_ODD) == ALIGN
+    assert call(5, None) == NULLP                                          # no output at all
+    assert call(3, 0) == OK
+
+
+def test_rmsnorm_bwd_quant_validation(lib):
+    f = lib.puro_fp8_rmsnorm_bwd_quant
+    # dy, x, gamma, rstd, gin, rows, cols, coef, q, s, qt, st, y, stream
+    ok = (P16, P16, P16, P16, None, 16, 256, P16, P16, P16, None, None, None, None)
+    call = lambda i, v: f(*(ok[:i] + (v,) + ok[i + 1:]))
+    assert call(6, 100) == SHAPE
+    assert call(5, -2) == SHAPE
+    for i in (0, 1, 2, 3, 7):                                              # gin alone may be NULL
+        assert call(i, None) == NULLP, i
+    for i in (0, 1, 2, 3, 4, 7):
+        assert call(i, P_ODD) == ALIGN, i
+    assert call(8, None) == NULLP                                          # q without s / no output
+    assert call(5, 0) == OK
+
+
+def test_residual_add_rstd_validation(lib):
+    f = lib.puro_bf16_residual_add_rstd
+    ok = (P16, P16, 16, 256, 1e-6, P16, P16, None)
+    call = lambda i, v: f(*(ok[:i] + (v,) + ok[i + 1:]))
+    assert call(3, 200) == SHAPE
+    assert call(3, 0) == SHAPE
+    assert call(2, -1) == SHAPE
+    for i in (0, 1, 5, 6):
+        assert call(i, None) == NULLP, i
+        assert call(i, P_ODD) == ALIGN, i
+    assert call(4, -1.0) == VALUE
+    assert call(4, float("nan")) == VALUE
+    assert call(2, 0) == OK

@@ -250,3 +250,90 @@ def test_probe_sigmoid_within_its_bound(pf):
             worst = max(worst, float(err.max()))
     say(f"   max relative error {worst / 2.0 ** -24:.3f} x 2^-24")
     assert worst <= 5 * 2.0 ** -24
+
+
+# ---- RMSNorm backward plus the skip path; residual add with rstd -----------------
+
+def _tol_bwd(cols):
+    """The FP32 error bound the C header states for the backward, as a
+    fraction of its magnitude M: (cols/512 + 18) * 2^-24."""
+    return (cols / 512 + 18) * 2.0 ** -24
+
+
+@pytest.mark.parametrize("rows,cols,skip", [(77, 128, True), (256, 2048, True),
+                                            (130, 8192, False), (1000, 384, True)])
+def test_rmsnorm_bwd_parity(pf, rows, cols, skip):
+    say("rmsnorm_bwd_quant", rows, cols, skip)
+    d = synth.rmsnorm_bwd_inputs(rows, cols, seed=rows + cols)
+    rstd = torch.from_numpy(oracle.rmsnorm_fwd(synth.bits(d["x"]), synth.bits(d["gamma"]),
+                                               1e-6, TOL)[3].astype(np.float32))
+    gin = d["gin"] if skip else None
+    out = pf.rmsnorm_bwd_quant(dev(d["dy"]), dev(d["x"]), dev(d["gamma"]), dev(rstd),
+                               None if gin is None else dev(gin), row=True, col=True,
+                               bf16_out=True)
+    y, lo, hi = oracle.rmsnorm_bwd(synth.bits(d["dy"]), synth.bits(d["x"]),
+                                   synth.bits(d["gamma"]), rstd.numpy(),
+                                   None if gin is None else synth.bits(gin), _tol_bwd(cols))
+    _assert_ok(pc.check_outputs(_host_outputs(out), y, lo, hi, rows),
+               f"rmsnorm_bwd {rows}x{cols}")
+
+
+def test_rmsnorm_bwd_output_subsets(pf):
+    """Each subset of outputs equals the same outputs of the all-output call,
+    and the codes are those of the plain quantizer on the bf16 result."""
+    rows, cols = 300, 512
+    d = synth.rmsnorm_bwd_inputs(rows, cols, seed=6)
+    rstd = dev(torch.rand(rows, dtype=torch.float32) + 0.5)
+    args = [dev(d[k]) for k in ("dy", "x", "gamma")] + [rstd, dev(d["gin"])]
+    say("rmsnorm_bwd_quant subsets", rows, cols)
+    full = pf.rmsnorm_bwd_quant(*args, row=True, col=True, bf16_out=True)
+    for row, col, yb in [(True, False, False), (False, True, False), (False, False, True),
+                         (True, True, False), (True, False, True), (False, True, True)]:
+        part = pf.rmsnorm_bwd_quant(*args, row=row, col=col, bf16_out=yb)
+        for k, v in part.items():
+            assert _same(v, full[k]), (k, row, col, yb)
+    ref = pf.quant_act(full["y"], row=True, col=True)
+    for k in ("q", "s", "qt", "st"):
+        assert _same(full[k], ref[k]), k
+
+
+def test_rmsnorm_bwd_block_stack_sampled(pf):
+    rows, cols = 32768, 2048
+    say("rmsnorm_bwd_quant block_stack", rows, cols)
+    d = synth.rmsnorm_bwd_inputs(rows, cols, seed=0)
+    x = dev(d["x"])
+    fwd = pf.rmsnorm_quant(x, dev(d["gamma"]), eps=1e-6, row=True, col=False)
+    out = pf.rmsnorm_bwd_quant(dev(d["dy"]), x, dev(d["gamma"]), fwd["rstd"], dev(d["gin"]),
+                               row=True, col=True)
+    sel = _sample_rows()
+    h = _host_outputs(out, row_sel=sel.to("cuda:0"), rb_sel=SAMPLE_RBS)
+    rstd = host(fwd["rstd"][sel.to("cuda:0")])
+    y, lo, hi = oracle.rmsnorm_bwd(synth.bits(d["dy"][sel]), synth.bits(d["x"][sel]),
+                                   synth.bits(d["gamma"]), rstd, synth.bits(d["gin"][sel]),
+                                   _tol_bwd(cols))
+    _assert_ok(pc.check_outputs(h, y, lo, hi, sel.numel()), "rmsnorm_bwd block_stack")
+
+
+@pytest.mark.parametrize("rows,cols", [(77, 128), (1000, 2048), (130, 8192)])
+def test_residual_add_rstd_then_one_pass_norm(pf, rows, cols):
+    """h = a + b bit for bit against the oracle, rstd within TOL of the
+    oracle's statistic of h, and the one-pass norm from that rstd equals the
+    two-pass puro_fp8_rmsnorm_quant on h wherever the two rstd agree."""
+    say("residual_add_rstd", rows, cols)
+    d = synth.residual_inputs(rows, cols, seed=rows + cols)
+    r = pf.residual_add_rstd(dev(d["a"]), dev(d["b"]), eps=1e-6)
+    h_ref = oracle.residual_add(synth.bits(d["a"]), synth.bits(d["b"]))
+    assert np.array_equal(bf16_host_bits(r["h"]), h_ref)
+    _, _, _, rstd_ref = oracle.rmsnorm_fwd(h_ref, synth.bits(d["gamma"]), float(np.float32(1e-6)),
+                                           TOL)
+    got_rstd = host(r["rstd"]).astype(np.float64)
+    assert np.max(np.abs(got_rstd - rstd_ref) / rstd_ref) <= TOL
+    one = pf.rmsnorm_quant_rstd(r["h"], dev(d["gamma"]), r["rstd"], row=True, col=True,
+                                bf16_out=True)
+    two = pf.rmsnorm_quant(r["h"], dev(d["gamma"]), eps=1e-6, row=True, col=True,
+                           bf16_out=True)
+    assert torch.equal(two["rstd"], r["rstd"])      # same statistic, same summation order
+    for k in ("q", "s", "qt", "st", "y"):
+        assert _same(one[k], two[k]), k
+    y, lo, hi, _ = oracle.rmsnorm_fwd(h_ref, synth.bits(d["gamma"]), float(np.float32(1e-6)), TOL)
+    _assert_ok(pc.check_outputs(_host_outputs(one), y, lo, hi, rows), f"one-pass {rows}x{cols}")
