@@ -31,10 +31,13 @@ a tuned FP8 GEMM without block scales, as a yardstick for the block-scaled
 GEMMs (not the same method).
 
 Quantize-on-produce ("produce"): the BF16 neighbour ops of one block at the
-same token count (RMSNorm x2 before QKV and up/gate, SwiGLU forward before
-down, SwiGLU backward after down's DGRAD), each writing FP8 operands straight
-from the op, timed against the unfused pair (the op writing bf16, then
-quant_act on it).  Not part of the step above, whose inputs are bf16 tensors.
+same token count, each writing FP8 operands straight from the op, timed
+against the unfused pair (the op writing bf16, then quant_act on it): the
+residual add + RMSNorm x2 (before QKV and up/gate; fused: the add hands the
+norm its row statistic, so the norm is one pass), SwiGLU forward before down,
+SwiGLU backward after down's DGRAD, and RMSNorm backward + the skip-path
+gradient x2 (the dY of out-proj and of the previous block's down).  Not part
+of the step above, whose inputs are bf16 tensors.
 
 After the timed region every launch of one step is also run on its own, 50
 times, each right after a 512 MiB write that evicts the L2s and the MALL
@@ -45,7 +48,15 @@ The CPU baseline times the plain CPU oracle (quantize + block-scaled GEMM in
 all three modes) on a bounded slice of the same workload: the first
 `--cpu-tokens` tokens of every linear layer, all host cores.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+The smaller workloads run one linear layer each, with only the GEMMs they
+name (--config c1..c4: the tiny forward, the QKV forward and the SwiGLU
+up+gate forward, each quantizing X row-wise and W once; the down-projection
+backward, quantizing dY both ways and X column-wise): the same line, with
+every GEMM launch bracketed.  Every run also reports each GEMM's error
+against the unquantized FP32 matmul of its bf16 inputs ("error_vs_fp32", on
+sampled output rows).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c1..c5]
 """
 from __future__ import annotations
 
@@ -70,6 +81,11 @@ _CSRC = os.path.join(ROOT, "fp8_block_scaled_tile_amd", "csrc")
 GEMM_SOURCES = [os.path.join(_CSRC, n) for n in ("gemm.hip", "device_common.hpp")]
 QUANT_SOURCES = [os.path.join(_CSRC, n) for n in ("quant.hip", "quant_block.hpp", "device_common.hpp")]
 
+# the workloads by number: the tiny forward, QKV forward, up+gate forward,
+# down-projection backward, and the linear stack of one block (the headline)
+CONFIGS = {"c1": "tiny_fwd", "c2": "qkv_fwd", "c3": "upgate_fwd", "c4": "down_bwd",
+           "c5": "block_stack"}
+
 # the GEMM classes whose launches carry events inside the timed region: the
 # dominant kernel is the one of these with the most time per step (the
 # WGRAD classes run fewer FLOP per step)
@@ -78,12 +94,15 @@ ROOFLINE_CLASSES = ("gemm_fwd_bf16", "gemm_fwd_t_bf16", "gemm_dgrad_bf16", "gemm
 # kernel symbol of each launch class (for matching rocprofv3 summaries)
 KERNEL_SYMBOLS = {
     "gemm_fwd_bf16": "void puro::gemm_bs_kernel<0, 0>",
+    "gemm_fwd_fp32": "void puro::gemm_bs_kernel<0, 1>",
     "gemm_fwd_t_bf16": "void puro::gemm_bs_kernel<5, 0>",
     "gemm_dgrad_bf16": "void puro::gemm_bs_kernel<1, 0>",
     "gemm_dgrad_w_bf16": "void puro::gemm_bs_kernel<4, 0>",
     "gemm_wgrad_fp32": "void puro::gemm_bs_kernel<2, 1>",
     "gemm_wgrad_splitk": "void puro::gemm_bs_kernel<2, 3> + splitk_reduce_kernel<1>",
     "quant_act_dual": "void puro::quant_block_kernel<true, true, false, false>",
+    "quant_act_row": "void puro::quant_block_kernel<true, false, false, false>",
+    "quant_act_col": "void puro::quant_block_kernel<false, true, false, false>",
     "quant_weight_t": "void puro::quant_block_kernel<false, false, true, true>",
     "quant_weight": "void puro::quant_block_kernel<false, false, true, false>",
 }
@@ -105,7 +124,12 @@ def parse_args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="block_stack")
+    p.add_argument("--workload", default="block_stack",
+                   help="a workload by name: " + ", ".join(f"{k} ({v})" for k, v in CONFIGS.items()))
+    p.add_argument("--config", choices=sorted(CONFIGS),
+                   help="a workload by its number (overrides --workload)")
+    p.add_argument("--no-fp32-error", action="store_true",
+                   help="skip the error against the unquantized FP32 matmul")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--layout", choices=sorted(LAYOUTS), default="w",
                    help="operand layout of each layer's FWD / DGRAD GEMMs (w: both on the "
@@ -153,9 +177,15 @@ def sha(paths) -> str:
 
 # ---- per-launch algorithmic work -------------------------------------------
 
+def act_bytes(rows, cols, row=True, col=True):
+    # read bf16; write 1x128 codes and / or 128x1 transposed codes, one FP32
+    # scale per 128 elements for each
+    n = int(row) + int(col)
+    return rows * cols * (2 + n) + n * (rows * cols // 128) * 4
+
+
 def act_dual_bytes(rows, cols):
-    # read bf16, write 1x128 codes + 128x1 transposed codes, two scale sets
-    return rows * cols * (2 + 1 + 1) + 2 * (rows * cols // 128) * 4
+    return act_bytes(rows, cols, True, True)
 
 
 def weight_bytes(n, k, copies):
@@ -164,55 +194,75 @@ def weight_bytes(n, k, copies):
 
 
 class Linear:
-    """Device buffers of one linear layer's FP8 path (allocated once)."""
+    """Device buffers of one linear layer's FP8 path (allocated once): the
+    GEMMs the layer's spec asks for (FWD, DGRAD, WGRAD) and the operands they
+    read."""
 
     def __init__(self, torch, pf, spec, tensors, layout):
         T, din, dout = spec.tokens, spec.d_in, spec.d_out
         fwd, dgrad = layout.get(spec.name, ("fwd", "dgrad"))
         self.fwd_mode = pf.GEMM_FWD_T if fwd == "fwd_t" else pf.GEMM_FWD
         self.dgrad_mode = pf.GEMM_DGRAD_W if dgrad == "dgrad_w" else pf.GEMM_DGRAD
-        self.layout = (fwd, dgrad)
-        # which weight code copies the two GEMMs read
-        self.need_q = self.fwd_mode == pf.GEMM_FWD or self.dgrad_mode == pf.GEMM_DGRAD_W
-        self.need_qt = self.fwd_mode == pf.GEMM_FWD_T or self.dgrad_mode == pf.GEMM_DGRAD
+        self.layout = (fwd if spec.fwd else None, dgrad if spec.dgrad else None)
+        # which weight code copies the GEMMs read
+        self.need_q = ((spec.fwd and self.fwd_mode == pf.GEMM_FWD)
+                       or (spec.dgrad and self.dgrad_mode == pf.GEMM_DGRAD_W))
+        self.need_qt = ((spec.fwd and self.fwd_mode == pf.GEMM_FWD_T)
+                        or (spec.dgrad and self.dgrad_mode == pf.GEMM_DGRAD))
+        # which activation codes: 1x128 rows for FWD (X) / DGRAD (dY), 128x1
+        # transposed for WGRAD (both)
+        self.x_row, self.x_col = spec.fwd, spec.wgrad
+        self.dy_row, self.dy_col = spec.dgrad, spec.wgrad
         Tp = (T + 127) // 128 * 128
         d = "cuda:0"
         u8, f32, bf16 = torch.uint8, torch.float32, torch.bfloat16
+        E = lambda shape, dt, need: torch.empty(shape, dtype=dt, device=d) if need else None
         self.spec = spec
         self.T, self.Tp, self.din, self.dout = T, Tp, din, dout
-        self.x = tensors["x"].to(d)
-        self.w = tensors["w"].to(d)
-        self.dy = tensors["dy"].to(d)
-        self.qx = torch.empty((T, din), dtype=u8, device=d)
-        self.sx = torch.empty((din // 128, T), dtype=f32, device=d)
-        self.qtx = torch.empty((din, Tp), dtype=u8, device=d)
-        self.stx = torch.empty((Tp // 128, din), dtype=f32, device=d)
-        self.qw = torch.empty((dout, din), dtype=u8, device=d)
-        self.qtw = torch.empty((din, dout), dtype=u8, device=d)
-        self.sw = torch.empty((dout // 128, din // 128), dtype=f32, device=d)
-        self.y = torch.empty((T, dout), dtype=bf16, device=d)
-        self.qdy = torch.empty((T, dout), dtype=u8, device=d)
-        self.sdy = torch.empty((dout // 128, T), dtype=f32, device=d)
-        self.qtdy = torch.empty((dout, Tp), dtype=u8, device=d)
-        self.stdy = torch.empty((Tp // 128, dout), dtype=f32, device=d)
-        self.dx = torch.empty((T, din), dtype=bf16, device=d)
-        self.dw = torch.empty((dout, din), dtype=f32, device=d)
+        need_x = spec.fwd or spec.wgrad
+        need_dy = spec.dgrad or spec.wgrad
+        self.x = tensors["x"].to(d) if need_x else None
+        self.w = tensors["w"].to(d) if (spec.fwd or spec.dgrad) else None
+        self.dy = tensors["dy"].to(d) if need_dy else None
+        self.qx = E((T, din), u8, self.x_row)
+        self.sx = E((din // 128, T), f32, self.x_row)
+        self.qtx = E((din, Tp), u8, self.x_col)
+        self.stx = E((Tp // 128, din), f32, self.x_col)
+        self.qw = E((dout, din), u8, self.need_q)
+        self.qtw = E((din, dout), u8, self.need_qt)
+        self.sw = E((dout // 128, din // 128), f32, self.need_q or self.need_qt)
+        self.fwd_fp32 = spec.fwd_out == "fp32"
+        self.y = E((T, dout), f32 if self.fwd_fp32 else bf16, spec.fwd)
+        self.qdy = E((T, dout), u8, self.dy_row)
+        self.sdy = E((dout // 128, T), f32, self.dy_row)
+        self.qtdy = E((dout, Tp), u8, self.dy_col)
+        self.stdy = E((Tp // 128, dout), f32, self.dy_col)
+        self.dx = E((T, din), bf16, spec.dgrad)
+        self.dw = E((dout, din), f32, spec.wgrad)
         self.fwd_b = self.qw if self.fwd_mode == pf.GEMM_FWD else self.qtw
         self.dgrad_b = self.qtw if self.dgrad_mode == pf.GEMM_DGRAD else self.qw
-        self.gemms = [  # (class, mode, M, N, K)
-            ("gemm_fwd_t_bf16" if fwd == "fwd_t" else "gemm_fwd_bf16", self.fwd_mode, T, dout, din),
-            ("gemm_dgrad_w_bf16" if dgrad == "dgrad_w" else "gemm_dgrad_bf16", self.dgrad_mode,
-             T, din, dout),
-            (None, pf.GEMM_WGRAD, dout, din, Tp),
-        ]
-        ws_need = max(pf.puro_fp8_gemm_workspace_bytes(m, M, N, K) for _, m, M, N, K in self.gemms)
-        self.ws = torch.empty(max(ws_need, 16), dtype=u8, device=d)
-        self.wgrad_split = pf.puro_fp8_gemm_workspace_bytes(pf.GEMM_WGRAD, dout, din, Tp) > 0
-        self.gemms[2] = ("gemm_wgrad_splitk" if self.wgrad_split else "gemm_wgrad_fp32",
-                         pf.GEMM_WGRAD, dout, din, Tp)
+        out_tag = "fp32" if self.fwd_fp32 else "bf16"
+        self.gemms = []  # (kind, class, mode, M, N, K)
+        if spec.fwd:
+            self.gemms.append(("fwd", ("gemm_fwd_t_" if fwd == "fwd_t" else "gemm_fwd_") + out_tag,
+                               self.fwd_mode, T, dout, din))
+        if spec.dgrad:
+            self.gemms.append(("dgrad", "gemm_dgrad_w_bf16" if dgrad == "dgrad_w" else
+                               "gemm_dgrad_bf16", self.dgrad_mode, T, din, dout))
+        self.wgrad_split = False
+        if spec.wgrad:
+            self.wgrad_split = pf.puro_fp8_gemm_workspace_bytes(pf.GEMM_WGRAD, dout, din, Tp) > 0
+            self.gemms.append(("wgrad", "gemm_wgrad_splitk" if self.wgrad_split else
+                               "gemm_wgrad_fp32", pf.GEMM_WGRAD, dout, din, Tp))
+        ws_need = max([pf.puro_fp8_gemm_workspace_bytes(m, M, N, K)
+                       for _, _, m, M, N, K in self.gemms] + [16])
+        self.ws = torch.empty(ws_need, dtype=u8, device=d)
+
+    def gemm(self, kind):
+        return next(g for g in self.gemms if g[0] == kind)
 
     def flops(self):
-        return sum(2.0 * M * N * K for _, _, M, N, K in self.gemms)
+        return sum(2.0 * M * N * K for _, _, _, M, N, K in self.gemms)
 
 
 def spec0_tokens(specs):
@@ -224,32 +274,49 @@ def check(pf, rc, what):
         raise RuntimeError(f"{what}: {pf.puro_fp8_status_string(rc)}")
 
 
+def _act_class(row, col):
+    return "quant_act_dual" if row and col else ("quant_act_row" if row else "quant_act_col")
+
+
 def step_calls(pf, layers, stream):
     """The launches of one step in order: (layer, class, work, fn), where work
     is the launch's algorithmic bytes (quantizers) or FLOP (GEMMs)."""
-    P = lambda t: t.data_ptr()
+    P = lambda t: None if t is None else t.data_ptr()
 
     def layer_calls(L):     # a scope per layer: each lambda binds its own L
-        return [
-            ("quant_act_dual", act_dual_bytes(L.T, L.din), lambda: pf.puro_fp8_quant_act(
-                P(L.x), L.T, L.din, P(L.qx), P(L.sx), P(L.qtx), P(L.stx), stream)),
-            ("quant_weight_t" if L.need_qt else "quant_weight",
-             weight_bytes(L.dout, L.din, int(L.need_q) + int(L.need_qt)),
-             lambda: pf.puro_fp8_quant_weight(
-                P(L.w), L.dout, L.din, P(L.qw) if L.need_q else None,
-                P(L.qtw) if L.need_qt else None, P(L.sw), stream)),
-            (L.gemms[0][0], 2.0 * L.T * L.dout * L.din, lambda: pf.puro_fp8_gemm_blockscaled(
-                L.fwd_mode, L.T, L.dout, L.din, P(L.qx), P(L.sx), P(L.fwd_b), P(L.sw), P(L.y),
-                pf.OUT_BF16, 0, P(L.ws), L.ws.numel(), stream)),
-            ("quant_act_dual", act_dual_bytes(L.T, L.dout), lambda: pf.puro_fp8_quant_act(
-                P(L.dy), L.T, L.dout, P(L.qdy), P(L.sdy), P(L.qtdy), P(L.stdy), stream)),
-            (L.gemms[1][0], 2.0 * L.T * L.din * L.dout, lambda: pf.puro_fp8_gemm_blockscaled(
-                L.dgrad_mode, L.T, L.din, L.dout, P(L.qdy), P(L.sdy), P(L.dgrad_b), P(L.sw),
-                P(L.dx), pf.OUT_BF16, 0, P(L.ws), L.ws.numel(), stream)),
-            (L.gemms[2][0], 2.0 * L.dout * L.din * L.Tp, lambda: pf.puro_fp8_gemm_blockscaled(
-                pf.GEMM_WGRAD, L.dout, L.din, L.Tp, P(L.qtdy), P(L.stdy), P(L.qtx), P(L.stx),
-                P(L.dw), pf.OUT_FP32, 0, P(L.ws), L.ws.numel(), stream)),
-        ]
+        sp = L.spec
+        calls = []
+        if L.x_row or L.x_col:
+            calls.append((_act_class(L.x_row, L.x_col), act_bytes(L.T, L.din, L.x_row, L.x_col),
+                          lambda: pf.puro_fp8_quant_act(P(L.x), L.T, L.din, P(L.qx), P(L.sx),
+                                                        P(L.qtx), P(L.stx), stream)))
+        if L.need_q or L.need_qt:
+            calls.append(("quant_weight_t" if L.need_qt else "quant_weight",
+                          weight_bytes(L.dout, L.din, int(L.need_q) + int(L.need_qt)),
+                          lambda: pf.puro_fp8_quant_weight(P(L.w), L.dout, L.din, P(L.qw),
+                                                           P(L.qtw), P(L.sw), stream)))
+        if sp.fwd:
+            out = pf.OUT_FP32 if L.fwd_fp32 else pf.OUT_BF16
+            calls.append((L.gemm("fwd")[1], 2.0 * L.T * L.dout * L.din,
+                          lambda: pf.puro_fp8_gemm_blockscaled(
+                              L.fwd_mode, L.T, L.dout, L.din, P(L.qx), P(L.sx), P(L.fwd_b),
+                              P(L.sw), P(L.y), out, 0, P(L.ws), L.ws.numel(), stream)))
+        if L.dy_row or L.dy_col:
+            calls.append((_act_class(L.dy_row, L.dy_col),
+                          act_bytes(L.T, L.dout, L.dy_row, L.dy_col),
+                          lambda: pf.puro_fp8_quant_act(P(L.dy), L.T, L.dout, P(L.qdy), P(L.sdy),
+                                                        P(L.qtdy), P(L.stdy), stream)))
+        if sp.dgrad:
+            calls.append((L.gemm("dgrad")[1], 2.0 * L.T * L.din * L.dout,
+                          lambda: pf.puro_fp8_gemm_blockscaled(
+                              L.dgrad_mode, L.T, L.din, L.dout, P(L.qdy), P(L.sdy), P(L.dgrad_b),
+                              P(L.sw), P(L.dx), pf.OUT_BF16, 0, P(L.ws), L.ws.numel(), stream)))
+        if sp.wgrad:
+            calls.append((L.gemm("wgrad")[1], 2.0 * L.dout * L.din * L.Tp,
+                          lambda: pf.puro_fp8_gemm_blockscaled(
+                              pf.GEMM_WGRAD, L.dout, L.din, L.Tp, P(L.qtdy), P(L.stdy), P(L.qtx),
+                              P(L.stx), P(L.dw), pf.OUT_FP32, 0, P(L.ws), L.ws.numel(), stream)))
+        return calls
 
     return [(L.spec.name, name, work, fn) for L in layers for name, work, fn in layer_calls(L)]
 
@@ -389,6 +456,57 @@ def produce_bench(torch, pf, tokens, hidden, ffn, stream, iters, seed):
             tokens * hidden * (2.0 + dual) + 4.0 * tokens,
             tokens * hidden * (2.0 + 2.0 + 2.0 + dual) + 4.0 * tokens, 2)
     del b, x, gamma, rstd
+    ops[-1]["per_block"] = 0
+    ops[-1]["note"] = "x given; the block's two norms run as residual_rmsnorm"
+    # the residual add that forms each norm's input, then the norm: fused =
+    # the add writing h and rstd, then the one-pass norm writing FP8 codes;
+    # unfused = the add, the two-pass norm writing bf16, then quant_act
+    d = synth.residual_inputs(tokens, hidden, seed=seed)
+    a, bb, gamma = d["a"].to("cuda"), d["b"].to("cuda"), d["gamma"].to("cuda")
+    del d
+    h = torch.empty_like(a)
+    rstd = torch.empty(tokens, dtype=torch.float32, device="cuda")
+    rstd2 = torch.empty(tokens, dtype=torch.float32, device="cuda")
+    b = bufs(tokens, hidden)
+    add = lambda: check(pf, pf.puro_bf16_residual_add_rstd(P(a), P(bb), tokens, hidden, 1e-6, P(h),
+                                                           P(rstd), stream), "residual_add_rstd")
+
+    def fused_res():
+        add()
+        check(pf, pf.puro_fp8_rmsnorm_quant_rstd(P(h), P(gamma), P(rstd), tokens, hidden, P(b["q"]),
+                                                 P(b["s"]), P(b["qt"]), P(b["st"]), None, stream),
+              "rmsnorm_quant_rstd")
+
+    def op_res():
+        add()
+        check(pf, pf.puro_fp8_rmsnorm_quant(P(h), P(gamma), tokens, hidden, 1e-6, P(rstd2), None,
+                                            None, None, None, P(b["y"]), stream), "rmsnorm")
+
+    measure("residual_rmsnorm", tokens, hidden, fused_res, op_res, qa(b, tokens, hidden),
+            tokens * hidden * (4.0 + 2.0 + 2.0 + dual) + 8.0 * tokens,
+            tokens * hidden * (4.0 + 2.0 + 2.0 + 2.0 + 2.0 + 2.0 + dual) + 8.0 * tokens, 2)
+    del b, a, bb, h, rstd, rstd2
+    # RMSNorm backward plus the skip path -> the FP8 dY of out-proj and of the
+    # previous block's down (twice per block); the bf16 result continues down
+    # the residual stream, so both variants write it
+    d = synth.rmsnorm_bwd_inputs(tokens, hidden, seed=seed)
+    dy, x, gin = d["dy"].to("cuda"), d["x"].to("cuda"), d["gin"].to("cuda")
+    del d
+    rstd = torch.rand(tokens, dtype=torch.float32, device="cuda") + 0.5
+    coef = torch.empty(tokens, dtype=torch.float32, device="cuda")
+    b = bufs(tokens, hidden)
+    measure("rmsnorm_bwd", tokens, hidden,
+            lambda: check(pf, pf.puro_fp8_rmsnorm_bwd_quant(P(dy), P(x), P(gamma), P(rstd), P(gin), tokens,
+                                                            hidden, P(coef), P(b["q"]), P(b["s"]),
+                                                            P(b["qt"]), P(b["st"]), P(b["y"]), stream),
+                          "rmsnorm_bwd_quant"),
+            lambda: check(pf, pf.puro_fp8_rmsnorm_bwd_quant(P(dy), P(x), P(gamma), P(rstd), P(gin), tokens,
+                                                            hidden, P(coef), None, None, None, None,
+                                                            P(b["y"]), stream), "rmsnorm_bwd"),
+            qa(b, tokens, hidden),
+            tokens * hidden * (6.0 + 2.0 + dual) + 8.0 * tokens,
+            tokens * hidden * (6.0 + 2.0 + 2.0 + dual) + 8.0 * tokens, 2)
+    del b, dy, x, gin, gamma, rstd, coef
     fused = sum(o["fused_ms"] * o["per_block"] for o in ops)
     unfused = sum(o["unfused_ms"] * o["per_block"] for o in ops)
     return {"ops": ops, "fused_ms_per_block": round(fused, 4),
@@ -530,25 +648,43 @@ def traffic_for(symbol_prefix):
     return v["hbm_bytes_per_dispatch"] if v else None
 
 
+# ---- error against the unquantized matmul ---------------------------------------
+
+def error_vs_fp32(torch, layers, rows=256):
+    """Each GEMM's FP8 result (from the last step) against the unquantized
+    FP32 matmul of the same bf16 inputs (torch, FP32 on the GPU), on the first
+    and last `rows` output rows: relative Frobenius error and the largest
+    |error| over the largest |reference|.  This is the quantization's error,
+    not a parity gate (parity is against the oracle on the same codes)."""
+    out = {}
+    for L in layers:
+        for kind, *_ in L.gemms:
+            if kind == "fwd":
+                M, got = L.T, L.y
+                ref_rows = lambda r: L.x[r].float() @ L.w.float().t()
+            elif kind == "dgrad":
+                M, got = L.T, L.dx
+                ref_rows = lambda r: L.dy[r].float() @ L.w.float()
+            else:
+                M, got = L.dout, L.dw
+                ref_rows = lambda r: L.dy[:, r].float().t() @ L.x.float()
+            sel = (torch.arange(M, device="cuda:0") if M <= 2 * rows else
+                   torch.cat([torch.arange(rows), torch.arange(M - rows, M)]).to("cuda:0"))
+            ref = ref_rows(sel).double()
+            g = got[sel].double()
+            err = g - ref
+            out[f"{L.spec.name}.{kind}"] = {
+                "rel_fro": float(err.norm() / ref.norm()),
+                "max_abs_err_over_max_ref": float(err.abs().max() / ref.abs().max()),
+                "rows_sampled": int(sel.numel())}
+            del ref, g, err
+    torch.cuda.synchronize()
+    return out
+
+
 # ---- BF16 comparator ------------------------------------------------------------
 
-def bf16_reference(torch, layers, steps):
-    """The same 12 products as plain BF16 GEMMs of the vendor library
-    (torch.matmul -> hipBLASLt / rocBLAS), bf16 outputs, with the transposed
-    operands materialized beforehand (outside the timing).  This is the
-    unquantized linear layer the FP8 path replaces; it is context for the
-    FP8/BF16 speedup, not part of the measured step."""
-    bufs = []
-    for L in layers:
-        bufs.append((L.x, L.w.t().contiguous(), L.dy, L.w, L.dy.t().contiguous(),
-                     torch.empty_like(L.y), torch.empty_like(L.dx),
-                     torch.empty((L.dout, L.din), dtype=torch.bfloat16, device="cuda:0")))
-
-    def step():
-        for x, wt, dy, w, dyt, y, dx, dw in bufs:
-            torch.matmul(x, wt, out=y)          # Y  = X . W^T
-            torch.matmul(dy, w, out=dx)         # dX = dY . W
-            torch.matmul(dyt, x, out=dw)        # dW = dY^T . X
+def _time_steps(torch, step, steps):
     for _ in range(3):
         step()
     torch.cuda.synchronize()
@@ -558,14 +694,39 @@ def bf16_reference(torch, layers, steps):
         step()
     e1.record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    flops = sum(2.0 * L.T * L.din * L.dout * 3 for L in layers)
-    del bufs
+    return e0.elapsed_time(e1) / steps
+
+
+def bf16_reference(torch, layers, steps):
+    """The step's products (FWD, DGRAD, WGRAD as each layer has them) as plain
+    BF16 GEMMs of the vendor library (torch.matmul -> hipBLASLt / rocBLAS),
+    bf16 outputs, with the transposed operands materialized beforehand
+    (outside the timing).  This is the unquantized linear layer the FP8 path
+    replaces; it is context for the FP8/BF16 speedup, not part of the
+    measured step."""
+    calls = []
+    for L in layers:
+        for kind, *_ in L.gemms:
+            if kind == "fwd":                  # Y  = X . W^T
+                calls.append((L.x, L.w.t().contiguous(),
+                              torch.empty((L.T, L.dout), dtype=torch.bfloat16, device="cuda:0")))
+            elif kind == "dgrad":              # dX = dY . W
+                calls.append((L.dy, L.w, torch.empty_like(L.dx)))
+            else:                              # dW = dY^T . X
+                calls.append((L.dy.t().contiguous(), L.x,
+                              torch.empty((L.dout, L.din), dtype=torch.bfloat16, device="cuda:0")))
+
+    def step():
+        for a, b, c in calls:
+            torch.matmul(a, b, out=c)
+    ms = _time_steps(torch, step, steps)
+    flops = sum(2.0 * a.shape[0] * a.shape[1] * b.shape[1] for a, b, _ in calls)
+    del calls
     return ms, flops / (ms * 1e-3) / 1e12
 
 
 def bf16_tiled(torch, pf, layers, steps, stream):
-    """The same 12 products through this library's BF16 comparator GEMM
+    """The step's products through this library's BF16 comparator GEMM
     (puro_bf16_gemm_nt: the FP8 path's own tiling on the bf16 matrix cores,
     no block scales), bf16 outputs, with the transposed operands materialized
     beforehand (outside the timing).  Kernel-for-kernel context for the FP8
@@ -573,39 +734,36 @@ def bf16_tiled(torch, pf, layers, steps, stream):
     P = lambda t: t.data_ptr()
     calls = []
     keep = []
+    bf16 = torch.bfloat16
     for L in layers:
-        wt, dyt, xt = L.w.t().contiguous(), L.dy.t().contiguous(), L.x.t().contiguous()
-        y, dx = torch.empty_like(L.y), torch.empty_like(L.dx)
-        dw = torch.empty((L.dout, L.din), dtype=torch.bfloat16, device="cuda:0")
-        shapes = [(L.T, L.dout, L.din, L.x, L.w, y),      # Y  = X . W^T
-                  (L.T, L.din, L.dout, L.dy, wt, dx),     # dX = dY . W   (B = W^T)
-                  (L.dout, L.din, L.T, dyt, xt, dw)]      # dW = dY^T . X (A = dY^T, B = X^T)
+        shapes = []
+        for kind, *_ in L.gemms:
+            if kind == "fwd":                  # Y  = X . W^T
+                shapes.append((L.T, L.dout, L.din, L.x, L.w,
+                               torch.empty((L.T, L.dout), dtype=bf16, device="cuda:0")))
+            elif kind == "dgrad":              # dX = dY . W   (B = W^T)
+                shapes.append((L.T, L.din, L.dout, L.dy, L.w.t().contiguous(),
+                               torch.empty_like(L.dx)))
+            else:                              # dW = dY^T . X (A = dY^T, B = X^T)
+                shapes.append((L.dout, L.din, L.T, L.dy.t().contiguous(), L.x.t().contiguous(),
+                               torch.empty((L.dout, L.din), dtype=bf16, device="cuda:0")))
         need = max(pf.puro_bf16_gemm_nt_workspace_bytes(M, N, K) for M, N, K, *_ in shapes)
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda:0")
-        keep += [wt, dyt, xt, y, dx, dw, ws]
+        keep += [t for sh in shapes for t in sh[3:]] + [ws]
         for M, N, K, a, b, c in shapes:
             calls.append((M, N, K, P(a), P(b), P(c), P(ws), ws.numel()))
 
     def step():
         for M, N, K, a, b, c, w, wb in calls:
             check(pf, pf.puro_bf16_gemm_nt(M, N, K, a, b, c, w, wb, stream), "bf16 comparator")
-    for _ in range(3):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ms = _time_steps(torch, step, steps)
     flops = sum(2.0 * M * N * K for M, N, K, *_ in calls)
     del keep
     return ms, flops / (ms * 1e-3) / 1e12
 
 
 def fp8_tensorwise_reference(torch, pf, layers, steps):
-    """The same 12 products through the vendor library's FP8 GEMM
+    """The step's products through the vendor library's FP8 GEMM
     (torch._scaled_mm -> hipBLASLt) on the codes the step's quantizers wrote,
     with ONE scale per tensor: no per-block scales and no fold, so it is not
     the block-scaled method.  It shows what a tuned FP8 GEMM without block
@@ -619,18 +777,31 @@ def fp8_tensorwise_reference(torch, pf, layers, steps):
     one = torch.ones((), dtype=torch.float32, device="cuda:0")
     calls = []
     wgrad_dtype = torch.float32
-    for L in layers:       # both weight code copies (the step may write only one)
-        rc = pf.puro_fp8_quant_weight(L.w.data_ptr(), L.dout, L.din, L.qw.data_ptr(),
-                                      L.qtw.data_ptr(), L.sw.data_ptr(),
-                                      torch.cuda.current_stream().cuda_stream)
-        check(pf, rc, "quant_weight")
-    for L in layers:
-        calls.append((L.qx.view(f8), L.qw.view(f8), torch.bfloat16))      # Y  = X . W^T
-        calls.append((L.qdy.view(f8), L.qtw.view(f8), torch.bfloat16))    # dX = dY . W
-        calls.append((L.qtdy.view(f8), L.qtx.view(f8), None))             # dW = dY^T . X
+    keep = []
+    for L in layers:       # the weight code copy each product reads (the step may write the other)
+        kinds = [g[0] for g in L.gemms]
+        qw = qtw = None
+        if "fwd" in kinds or "dgrad" in kinds:
+            qw = torch.empty((L.dout, L.din), dtype=torch.uint8, device="cuda:0")
+            qtw = torch.empty((L.din, L.dout), dtype=torch.uint8, device="cuda:0")
+            sw = torch.empty((L.dout // 128, L.din // 128), dtype=torch.float32, device="cuda:0")
+            keep += [qw, qtw, sw]
+            rc = pf.puro_fp8_quant_weight(L.w.data_ptr(), L.dout, L.din, qw.data_ptr(),
+                                          qtw.data_ptr(), sw.data_ptr(),
+                                          torch.cuda.current_stream().cuda_stream)
+            check(pf, rc, "quant_weight")
+        for kind in kinds:
+            if kind == "fwd":
+                calls.append((L.qx.view(f8), qw.view(f8), torch.bfloat16))      # Y  = X . W^T
+            elif kind == "dgrad":
+                calls.append((L.qdy.view(f8), qtw.view(f8), torch.bfloat16))    # dX = dY . W
+            else:
+                calls.append((L.qtdy.view(f8), L.qtx.view(f8), None))           # dW = dY^T . X
+    wg = [c for c in calls if c[2] is None]
     try:
-        a, b, _ = calls[2]
-        torch._scaled_mm(a, b.t(), scale_a=one, scale_b=one, out_dtype=torch.float32)
+        if wg:
+            a, b, _ = wg[0]
+            torch._scaled_mm(a, b.t(), scale_a=one, scale_b=one, out_dtype=torch.float32)
     except (RuntimeError, TypeError, ValueError, NotImplementedError):
         wgrad_dtype = torch.bfloat16
     try:
@@ -667,26 +838,33 @@ def _cpu_model() -> str:
 
 
 def _oracle_slice(specs, host_tensors, tokens):
-    """The oracle (quantize + block-scaled GEMM, all three modes) on the first
-    `tokens` tokens of every linear layer: (GEMM FLOP, seconds)."""
+    """The oracle (quantize + the block-scaled GEMMs each layer has) on the
+    first `tokens` tokens of every linear layer: (GEMM FLOP, seconds)."""
     import oracle
     import synth
     flops = 0.0
     t0 = time.perf_counter()
     for spec, t in zip(specs, host_tensors):
-        x = synth.bits(t["x"][:tokens])
-        w = synth.bits(t["w"])
-        dy = synth.bits(t["dy"][:tokens])
-        qx, sx = oracle.quant_rowwise(x)
-        qtx, stx = oracle.quant_colwise(x)
-        qw, qtw, sw = oracle.quant_weight(w)
-        qdy, sdy = oracle.quant_rowwise(dy)
-        qtdy, stdy = oracle.quant_colwise(dy)
-        oracle.gemm_blockscaled(oracle.MODE_FWD, qx, sx, qw, sw)
-        oracle.gemm_blockscaled(oracle.MODE_DGRAD, qdy, sdy, qtw, sw)
-        oracle.gemm_blockscaled(oracle.MODE_WGRAD, qtdy, stdy, qtx, stx)
-        tp = qtx.shape[1]
-        flops += 2.0 * tokens * spec.d_out * spec.d_in * 2 + 2.0 * spec.d_out * spec.d_in * tp
+        tk = min(tokens, spec.tokens)
+        if spec.fwd or spec.wgrad:
+            x = synth.bits(t["x"][:tk])
+        if spec.fwd or spec.dgrad:
+            qw, qtw, sw = oracle.quant_weight(synth.bits(t["w"]), transpose=spec.dgrad)
+        if spec.dgrad or spec.wgrad:
+            dy = synth.bits(t["dy"][:tk])
+        if spec.fwd:
+            qx, sx = oracle.quant_rowwise(x)
+            oracle.gemm_blockscaled(oracle.MODE_FWD, qx, sx, qw, sw)
+            flops += 2.0 * tk * spec.d_out * spec.d_in
+        if spec.dgrad:
+            qdy, sdy = oracle.quant_rowwise(dy)
+            oracle.gemm_blockscaled(oracle.MODE_DGRAD, qdy, sdy, qtw, sw)
+            flops += 2.0 * tk * spec.d_out * spec.d_in
+        if spec.wgrad:
+            qtx, stx = oracle.quant_colwise(x)
+            qtdy, stdy = oracle.quant_colwise(dy)
+            oracle.gemm_blockscaled(oracle.MODE_WGRAD, qtdy, stdy, qtx, stx)
+            flops += 2.0 * spec.d_out * spec.d_in * qtx.shape[1]
     return flops, time.perf_counter() - t0
 
 
@@ -717,8 +895,13 @@ def cpu_baseline(specs, host_tensors, tokens, single_tokens=256):
             "threads_from": "OMP_NUM_THREADS" if env else "os.cpu_count()",
             "single_thread": single,
             "sample": (f"first {tokens} tokens of each of the {len(specs)} linear layers: "
-                       f"quantize X, dY (1x128 and 128x1), W (128x128) and the FWD, DGRAD and "
-                       f"WGRAD GEMMs of that slice ({flops / 1e9:.1f} GFLOP), on {used} threads")}
+                       f"quantize the operands each GEMM reads (1x128, 128x1, 128x128) and run "
+                       f"the layer's {'/'.join(_kinds(specs))} GEMMs on that slice "
+                       f"({flops / 1e9:.1f} GFLOP), on {used} threads")}
+
+
+def _kinds(specs):
+    return [k.upper() for k in ("fwd", "dgrad", "wgrad") if any(getattr(s, k) for s in specs)]
 
 
 # ---- main --------------------------------------------------------------------------
@@ -757,7 +940,8 @@ def main():
     import fp8_block_scaled_tile_amd as pf
     import synth
 
-    wl = synth.workload(args.workload)
+    wl = synth.workload(CONFIGS[args.config] if args.config else args.workload)
+    headline = wl.name == "block_stack"
     specs = list(wl.linears)
     t_gen = time.perf_counter()
     host_tensors = [synth.linear_inputs(s, seed=args.seed) for s in specs]
@@ -788,7 +972,10 @@ def main():
         return rec
 
     timed_events = []
-    rec = recorder(timed_events, ROOFLINE_CLASSES)
+    # the headline step brackets FWD and DGRAD only; a single-layer workload
+    # (one to three GEMM launches per step) brackets every GEMM launch
+    classes = ROOFLINE_CLASSES if headline else {g[1] for L in layers for g in L.gemms}
+    rec = recorder(timed_events, classes)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -875,8 +1062,10 @@ def main():
                                   f"outputs, {wdt} WGRAD output; context, not timed above",
                           "block_scaled_gemm_ratio": round(vms / gemm_ms, 3) if gemm_ms else None}
 
+    fp32_err = None if args.no_fp32_error else error_vs_fp32(torch, layers)
+
     produce = None
-    if not args.no_produce:
+    if not args.no_produce and headline:
         produce = produce_bench(torch, pf, spec0_tokens(specs), 2048, 8192, stream, args.produce_iters,
                                 args.seed)
 
@@ -904,11 +1093,14 @@ def main():
         "vs_baseline": None,
         "dtype": "fp8_e4m3",
         "data": "synthetic",
-        "config": {"workload": wl.name, "tokens": spec0.tokens, "hidden": 2048, "heads": 16,
-                   "ffn": 8192, "linears": {s.name: [s.d_in, s.d_out] for s in specs},
-                   "gemm_tflop_per_step": round(step_flops / 1e12, 4),
-                   "operand_layout": {L.spec.name: list(L.layout) for L in layers},
-                   "parallelism": "single GPU"},
+        "config": dict({"workload": wl.name, "description": wl.description,
+                        "tokens": spec0.tokens},
+                       **({"hidden": 2048, "heads": 16, "ffn": 8192} if headline else {}),
+                       linears={s.name: [s.d_in, s.d_out] for s in specs},
+                       gemms={L.spec.name: [g[0] for g in L.gemms] for L in layers},
+                       gemm_tflop_per_step=round(step_flops / 1e12, 4),
+                       operand_layout={L.spec.name: list(L.layout) for L in layers},
+                       parallelism="single GPU"),
         "pct_of_fp8_peak": round(100.0 * value / FP8_PEAK_TFLOPS, 2),
         "gemm_only_tflops": round(step_flops / (gemm_ms * 1e-3) / 1e12, 1) if gemm_ms else None,
         "ms_per_step_all_events": round(ms_all_events, 4),
@@ -920,6 +1112,7 @@ def main():
         "bf16_reference": bf16,
         "bf16_tiled": bf16_own,
         "fp8_tensorwise_reference": fp8_vendor,
+        "error_vs_fp32": fp32_err,
         "produce": produce,
         "kernels_cold": cold,
         "hbm_copy_reference": copy_ref,

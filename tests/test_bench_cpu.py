@@ -24,20 +24,39 @@ class _Ptr(_Buf):
         return self.v
 
 
-def _layer(name, T, din, dout, fwd_mode=0, dgrad_mode=1):
-    L = types.SimpleNamespace(spec=types.SimpleNamespace(name=name), T=T, Tp=T, din=din, dout=dout)
-    for a in ("x", "qx", "sx", "qtx", "stx", "w", "sw", "y", "dy", "qdy", "sdy",
-              "qtdy", "stdy", "dx", "dw", "ws"):
+def _layer(name, T, din, dout, fwd_mode=0, dgrad_mode=1, fwd=True, dgrad=True, wgrad=True):
+    spec = types.SimpleNamespace(name=name, fwd=fwd, dgrad=dgrad, wgrad=wgrad)
+    L = types.SimpleNamespace(spec=spec, T=T, Tp=T, din=din, dout=dout)
+    for a in ("x", "w", "sw", "y", "dy", "dx", "dw", "ws"):
         setattr(L, a, _Buf())
-    L.qw, L.qtw = _Ptr(16), _Ptr(32)         # tell the two weight code copies apart
+    L.x_row, L.x_col, L.dy_row, L.dy_col = fwd, wgrad, dgrad, wgrad
+    L.qx, L.sx = (_Buf(), _Buf()) if fwd else (None, None)
+    L.qtx, L.stx = (_Buf(), _Buf()) if wgrad else (None, None)
+    L.qdy, L.sdy = (_Buf(), _Buf()) if dgrad else (None, None)
+    L.qtdy, L.stdy = (_Buf(), _Buf()) if wgrad else (None, None)
     L.fwd_mode, L.dgrad_mode = fwd_mode, dgrad_mode
-    L.need_q = fwd_mode == 0 or dgrad_mode == 3
-    L.need_qt = fwd_mode == 4 or dgrad_mode == 1
+    L.need_q = (fwd and fwd_mode == 0) or (dgrad and dgrad_mode == 3)
+    L.need_qt = (fwd and fwd_mode == 4) or (dgrad and dgrad_mode == 1)
+    L.qw = _Ptr(16) if L.need_q else None          # tell the two weight code copies apart
+    L.qtw = _Ptr(32) if L.need_qt else None
     L.fwd_b = L.qw if fwd_mode == 0 else L.qtw
     L.dgrad_b = L.qtw if dgrad_mode == 1 else L.qw
-    L.gemms = [("gemm_fwd_bf16", fwd_mode, T, dout, din), ("gemm_dgrad_bf16", dgrad_mode, T, din, dout),
-               ("gemm_wgrad_fp32", 2, dout, din, T)]
+    L.fwd_fp32 = False
+    L.gemms = ([("fwd", "gemm_fwd_bf16", fwd_mode, T, dout, din)] * fwd
+               + [("dgrad", "gemm_dgrad_bf16", dgrad_mode, T, din, dout)] * dgrad
+               + [("wgrad", "gemm_wgrad_fp32", 2, dout, din, T)] * wgrad)
+    L.gemm = lambda kind: next(g for g in L.gemms if g[0] == kind)
     return L
+
+
+def _pf(seen):
+    return types.SimpleNamespace(
+        GEMM_FWD=0, GEMM_DGRAD=1, GEMM_WGRAD=2, GEMM_DGRAD_W=3, GEMM_FWD_T=4, OUT_BF16=0,
+        OUT_FP32=1,
+        puro_fp8_quant_act=lambda x, r, c, q, s, qt, st, stream:
+            seen.append(("act", r, c, q is not None, qt is not None)) or 0,
+        puro_fp8_quant_weight=lambda w, n, k, q, qt, s, st: seen.append(("weight", n, k, q, qt)) or 0,
+        puro_fp8_gemm_blockscaled=lambda m, M, N, K, a, sa, b, *r: seen.append(("gemm", m, M, N, K, b)) or 0)
 
 
 def test_step_calls_bind_each_layer():
@@ -45,25 +64,51 @@ def test_step_calls_bind_each_layer():
     weight code copies: layer a runs FWD + DGRAD (reads q and q^T), layer b
     FWD_T + DGRAD (reads q^T only, so the weight quantizer skips q)."""
     seen = []
-    pf = types.SimpleNamespace(
-        GEMM_FWD=0, GEMM_DGRAD=1, GEMM_WGRAD=2, GEMM_DGRAD_W=3, GEMM_FWD_T=4, OUT_BF16=0,
-        OUT_FP32=1,
-        puro_fp8_quant_act=lambda x, r, c, *a: seen.append(("act", r, c)) or 0,
-        puro_fp8_quant_weight=lambda w, n, k, q, qt, s, st: seen.append(("weight", n, k, q, qt)) or 0,
-        puro_fp8_gemm_blockscaled=lambda m, M, N, K, a, sa, b, *r: seen.append(("gemm", m, M, N, K, b)) or 0)
+    pf = _pf(seen)
     layers = [_layer("a", 256, 128, 384), _layer("b", 512, 256, 128, fwd_mode=4, dgrad_mode=1)]
     calls = bench.step_calls(pf, layers, None)
     assert [c[0] for c in calls] == ["a"] * 6 + ["b"] * 6
     for _, _, _, fn in calls:
         assert fn() == 0
-    expect = [("act", 256, 128), ("weight", 384, 128, 16, 32), ("gemm", 0, 256, 384, 128, 16),
-              ("act", 256, 384), ("gemm", 1, 256, 128, 384, 32), ("gemm", 2, 384, 128, 256, 0),
-              ("act", 512, 256), ("weight", 128, 256, None, 32), ("gemm", 4, 512, 128, 256, 32),
-              ("act", 512, 128), ("gemm", 1, 512, 256, 128, 32), ("gemm", 2, 128, 256, 512, 0)]
+    A = lambda r, c: ("act", r, c, True, True)
+    expect = [A(256, 128), ("weight", 384, 128, 16, 32), ("gemm", 0, 256, 384, 128, 16),
+              A(256, 384), ("gemm", 1, 256, 128, 384, 32), ("gemm", 2, 384, 128, 256, 0),
+              A(512, 256), ("weight", 128, 256, None, 32), ("gemm", 4, 512, 128, 256, 32),
+              A(512, 128), ("gemm", 1, 512, 256, 128, 32), ("gemm", 2, 128, 256, 512, 0)]
     assert seen == expect
     works = [c[2] for c in calls]
     assert works[2] == 2.0 * 256 * 384 * 128 and works[8] == 2.0 * 512 * 128 * 256
     assert works[1] == bench.weight_bytes(384, 128, 2) and works[7] == bench.weight_bytes(128, 256, 1)
+
+
+def test_step_calls_follow_the_layer_gemm_set():
+    """A forward-only layer quantizes X row-wise only and W without the
+    transposed copy; a backward-only layer (DGRAD from the weight's codes +
+    WGRAD) quantizes dY both ways, X column-wise only, W once."""
+    seen = []
+    pf = _pf(seen)
+    fwd_only = _layer("qkv", 16384, 2048, 6144, dgrad=False, wgrad=False)
+    bwd_only = _layer("down", 16384, 8192, 2048, dgrad_mode=3, fwd=False)
+    calls = bench.step_calls(pf, [fwd_only, bwd_only], None)
+    for _, _, _, fn in calls:
+        assert fn() == 0
+    assert [c[1] for c in calls] == ["quant_act_row", "quant_weight", "gemm_fwd_bf16",
+                                     "quant_act_col", "quant_weight", "quant_act_dual",
+                                     "gemm_dgrad_bf16", "gemm_wgrad_fp32"]
+    assert seen == [("act", 16384, 2048, True, False), ("weight", 6144, 2048, 16, None),
+                    ("gemm", 0, 16384, 6144, 2048, 16),
+                    ("act", 16384, 8192, False, True), ("weight", 2048, 8192, 16, None),
+                    ("act", 16384, 2048, True, True), ("gemm", 3, 16384, 8192, 2048, 16),
+                    ("gemm", 2, 2048, 8192, 16384, 0)]
+    assert calls[0][2] == bench.act_bytes(16384, 2048, True, False) == 16384 * 2048 * 3 + 16384 * 16 * 4
+    assert calls[5][2] == bench.act_dual_bytes(16384, 2048)
+
+
+def test_configs_name_the_workloads():
+    import synth
+    assert bench.CONFIGS["c5"] == "block_stack"
+    for name in bench.CONFIGS.values():
+        synth.workload(name)
 
 
 def test_ingest_mfma_weights_by_duration_and_gates_on_code(tmp_path, monkeypatch):
