@@ -561,6 +561,10 @@ void orc_f32_to_bf16_array(const float* v, int64_t n, uint16_t* out)
  * between the roundings of the two ends (lo, hi), both included.  lo == hi
  * (== y) marks an element with one correct result. */
 
+/* A positive band is widened by 2^-149: below the normal range an FP32
+ * result carries an absolute rounding error of up to half of 2^-149 (the
+ * subnormal spacing) whatever its relative bound, so a device result there
+ * is correct up to that much more. */
 static void round_band(double v, double band, uint16_t* y, uint16_t* lo, uint16_t* hi)
 {
     *y = orc_f64_to_bf16(v);
@@ -569,6 +573,7 @@ static void round_band(double v, double band, uint16_t* y, uint16_t* lo, uint16_
         *hi = *y;
         return;
     }
+    band += 0x1p-149;
     *lo = orc_f64_to_bf16(v - band);
     *hi = orc_f64_to_bf16(v + band);
 }

@@ -122,7 +122,9 @@ void     orc_f32_to_bf16_array(const float* v, int64_t n, uint16_t* out);
  * that evaluates the op in FP32 with an error of at most tol * M (M: the op's
  * magnitude at that element, stated per op in the source) returns a bf16
  * value between lo and hi, both included: the roundings of the two ends of
- * that band.  lo == hi (== y) where only one result is correct.  Return 0, or
+ * that band, widened by 2^-149 (an FP32 result below the normal range is
+ * rounded to that spacing whatever its relative bound; tol = 0 keeps the band
+ * empty).  lo == hi (== y) where only one result is correct.  Return 0, or
  * -1 on a bad argument.
  *   swiglu_fwd: gu [rows][2f] -> [rows][f],  h = silu(gate) * up
  *   swiglu_bwd: dh [rows][f], gu [rows][2f] -> [rows][2f] = (d gate | d up)
@@ -156,7 +158,7 @@ int orc_residual_add(const uint16_t* a, const uint16_t* b, int64_t n, uint16_t* 
  * d up, M of d gate} for gate g, up u and upstream gradient dh. */
 void orc_swiglu_point(double g, double u, double dh, double* out4);
 /* The rounding above for one value: out3 = {y, lo, hi} of v with band
- * half-width `band`. */
+ * half-width `band` (+ 2^-149 when band > 0). */
 void orc_bf16_band(double v, double band, uint16_t* out3);
 
 /* Worker threads used by the array functions (default: all online cores). */

@@ -91,6 +91,11 @@ def test_band_ends(orc):
     assert orc.bf16_band(1.0, 2.0**-6) == (0x3F80, 0x3F7C, 0x3F82)  # several steps wide
     assert orc.bf16_band(1e-45, 1e-44) == (0x0000, 0x8000, 0x0000)  # straddles zero
     assert orc.bf16_band(-0.0, 0.0) == (0x8000, 0x8000, 0x8000)    # exact: keeps the sign
+    # below the normal range the band also holds the FP32 subnormal spacing:
+    # 2^-134 is the midpoint of bf16's 0 and 2^-133 (ties to the even 0), and
+    # a device result of 2^-134 +- 2^-150 may round either way
+    assert orc.bf16_band(2.0**-134, 2.0**-160) == (0x0000, 0x0000, 0x0001)
+    assert orc.bf16_band(2.0**-134, 0.0) == (0x0000, 0x0000, 0x0000)
 
 
 # ---- SwiGLU ------------------------------------------------------------------
