@@ -41,26 +41,62 @@ namespace puro {
 // 3.3 * 2^-24 of e^t.  It costs 6 instructions where the math library's
 // expf costs about 13; the bare 2^(t * log2 e) would cost 2, but rounding
 // t * log2 e carries |t| * 2^-24 into the exponent.
-__device__ __forceinline__ float exp_f32(float t)
+//
+// The function computes e^t * 2^k: k is added to y_hi before the hardware
+// 2^x (k = 0 gives e^t).
+// For y_hi <= -k (t <= -k ln 2) and k a power of two up to 64 the sum is
+// exact (its ulp is no coarser than y_hi's), so the result is e^t scaled by
+// exactly 2^k, with e^t's relative error, and it stays a normal FP32 number
+// where e^t itself would be subnormal -- which the hardware 2^x flushes to
+// zero.
+__device__ __forceinline__ float exp_f32_shifted(float t, float k)
 {
     constexpr float kLog2eHi = 0x1.715476p+0f;      // RN32(log2 e)
     constexpr float kLog2eLo = 0x1.4ae0cp-26f;      // RN32(log2 e - kLog2eHi)
     constexpr float kLn2 = 0x1.62e430p-1f;          // RN32(ln 2)
     const float y_hi = t * kLog2eHi;
     const float y_lo = fmaf(t, kLog2eLo, fmaf(t, kLog2eHi, -y_hi));
-    const float r = __builtin_amdgcn_exp2f(y_hi);
+    const float r = __builtin_amdgcn_exp2f(y_hi + k);
     return r * (1.0f + y_lo * kLn2);
 }
 
-// sigmoid(g) = 1 / (1 + e^-g) in FP32: exp_f32, then the hardware
-// reciprocal (within 1 ulp).  A relative error of e^-g reaches sigmoid damped
-// by e^-g / (1 + e^-g), so sigmoid stays within about 5 units of 2^-24 for
-// every g (measured over every FP32 g in [-88, 88] with a normal result:
-// 4.1 * 2^-24); for g below about -88.7 the exponential overflows and the
-// result is 0.
+// sigmoid(g) and 1 - sigmoid(g) in FP32 from one exponential that never
+// overflows: with e = e^-|g| in (0, 1] and s = 1 / (1 + e) (the hardware
+// reciprocal, within 1 ulp), sigmoid is s for g >= 0 and e * s for g < 0, and
+// 1 - sigmoid the other one.  For g >= 0 a relative error of e reaches s
+// damped by e / (1 + e); for g < 0 it reaches e * s in full, so the bound is
+// exp_f32's plus the add, the reciprocal and the product: about 5 units of
+// 2^-24 (measured 4.5 over [-87, 0), 2.2 over [0, 104]).
+//
+// Below g = -64 sigmoid is e^g to FP32 precision and heads for the
+// subnormal range (from g = -87.3), where the hardware 2^x returns zero.
+// There the pair is returned scaled: p = sigmoid(g) * 2^64 (from
+// exp_f32_shifted, a normal number down to g = -131), and the caller
+// multiplies its result by `scale` = 2^-64 as the last step, so only that
+// one rounding can be subnormal.  Above -64 scale = 1 and the arithmetic is
+// the plain one.  (Products by 2^64 and 2^-64 are exact on normal numbers,
+// so wherever the result is normal both orders give the same bits.)
+struct Sig {
+    float p;        // sigmoid(g), times 1 / scale
+    float q;        // 1 - sigmoid(g)
+    float scale;    // 1, or 2^-64 below g = -64
+};
+
+__device__ __forceinline__ Sig sigmoid_pair(float g)
+{
+    const bool deep = g < -64.0f;
+    const float e = exp_f32_shifted(-__builtin_fabsf(g), deep ? 64.0f : 0.0f);
+    const float s = __builtin_amdgcn_rcpf(1.0f + (deep ? 0.0f : e));   // e < 2^-92 when deep
+    const float es = e * s;
+    if (g >= 0.0f)
+        return Sig{s, es, 1.0f};
+    return Sig{es, s, deep ? 0x1p-64f : 1.0f};
+}
+
 __device__ __forceinline__ float sigmoid_f32(float g)
 {
-    return __builtin_amdgcn_rcpf(1.0f + exp_f32(-g));
+    const Sig sg = sigmoid_pair(g);
+    return sg.p * sg.scale;
 }
 
 // The sigmoid on consecutive FP32 bit patterns (puro_fp8_probe_sigmoid).
@@ -101,7 +137,8 @@ __device__ __forceinline__ uint4 map8(const uint4& a, const uint4& b, const uint
 struct SwigluH {
     __device__ float operator()(float g, float u, float) const
     {
-        return (g * sigmoid_f32(g)) * u;
+        const Sig sg = sigmoid_pair(g);
+        return ((g * sg.p) * u) * sg.scale;
     }
 };
 
@@ -109,8 +146,8 @@ struct SwigluH {
 struct SwigluDGate {
     __device__ float operator()(float g, float u, float dh) const
     {
-        const float sg = sigmoid_f32(g);
-        return ((dh * u) * sg) * __builtin_fmaf(g, 1.0f - sg, 1.0f);
+        const Sig sg = sigmoid_pair(g);
+        return (((dh * u) * sg.p) * __builtin_fmaf(g, sg.q, 1.0f)) * sg.scale;
     }
 };
 
@@ -118,7 +155,8 @@ struct SwigluDGate {
 struct SwigluDUp {
     __device__ float operator()(float g, float, float dh) const
     {
-        return dh * (g * sigmoid_f32(g));
+        const Sig sg = sigmoid_pair(g);
+        return (dh * (g * sg.p)) * sg.scale;
     }
 };
 

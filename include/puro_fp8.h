@@ -122,6 +122,32 @@ puro_status_t puro_fp8_quant_weight(const void* w, int64_t n, int64_t k,
                                     void* stream);
 
 /*
+ * Several weights quantized in ONE launch (one block's QKV, out-proj,
+ * up/gate and down): each descriptor is exactly the arguments of one
+ * puro_fp8_quant_weight call, with the same layouts, requirements and
+ * results bit for bit.  The small weights of a block do not fill the 256
+ * compute units one at a time (a 2048x2048 weight is 256 blocks of 128x128);
+ * together they do, and one launch replaces four.
+ *   descs  HOST array of `count` descriptors, read during the call only
+ *   count  0 .. PURO_FP8_MAX_GROUPED_WEIGHTS (0 enqueues nothing)
+ * A descriptor that fails puro_fp8_quant_weight's checks fails the call with
+ * that status, and nothing is enqueued.  The outputs of different
+ * descriptors must not overlap.
+ * Defined by: the same passages as puro_fp8_quant_act.
+ */
+#define PURO_FP8_MAX_GROUPED_WEIGHTS 16
+typedef struct puro_fp8_weight_desc {
+    const void* w;    /* bf16 [n][k] */
+    int64_t n, k;
+    uint8_t* q;       /* u8 [n][k] or NULL */
+    uint8_t* qt;      /* u8 [k][n] or NULL */
+    float* s;         /* f32 [n/128][k/128] */
+} puro_fp8_weight_desc;
+
+puro_status_t puro_fp8_quant_weight_grouped(const puro_fp8_weight_desc* descs, int count,
+                                            void* stream);
+
+/*
  * Block-scaled FP8 GEMM.
  *
  *   C[m][n] (+)= sum over kb < K/128 of
@@ -216,7 +242,8 @@ puro_status_t puro_fp8_probe_encode(uint32_t first_bits, int64_t n, uint8_t* out
 
 /*
  * Diagnostic: the FP32 sigmoid 1 / (1 + e^-g) that the SwiGLU producers
- * evaluate (puro_fp8_swiglu_quant, puro_fp8_swiglu_bwd_quant), applied to the
+ * evaluate (puro_fp8_swiglu_quant, puro_fp8_swiglu_bwd_quant; below g = -64
+ * they keep it scaled by 2^64, and the probe returns it scaled back), applied to the
  * binary32 values whose bit patterns are first_bits, first_bits + 1, ...,
  * first_bits + n - 1 (wrapping modulo 2^32).  out: f32 [n] device buffer,
  * 4-byte aligned.  Lets a test hold the device evaluation to its error bound
@@ -267,8 +294,11 @@ puro_status_t puro_fp8_probe_mfma(int form, const uint8_t* a, const uint8_t* b, 
  * the op where the exact value lies within the FP32 evaluation error of a
  * bf16 rounding boundary; it is then the other neighbour.  That error stays
  * below 2^-18 of the op's magnitude (|result|; for d gate,
- * |dh * up * sigmoid(gate)| * (1 + |gate|)) for |gate| <= 80 and, for
- * RMSNorm, rows up to 2^15 columns.
+ * |dh * up * sigmoid(gate)| * (1 + |gate|)) plus 2^-150 (half the FP32
+ * subnormal spacing, for results below the normal range), for every gate
+ * value (deep negative gates, where sigmoid heads for the subnormal range,
+ * are evaluated with the exponential scaled by 2^64 and the result scaled
+ * back in one last rounding) and, for RMSNorm, rows up to 2^15 columns.
  */
 
 /*

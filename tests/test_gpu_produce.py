@@ -8,6 +8,9 @@ TOL * M, of the exact one (the bound the C header states).  produce_check
 compares every tile bit for bit where it has one correct result, and checks
 the others against every correct (scale, codes).
 
+The band holds, besides TOL * M, the FP32 subnormal spacing 2^-149 (a
+result below the normal range is rounded to it whatever its relative bound).
+
 Sizes: small cases span several tiles and a ragged last row block; the
 block-stack sizes (32768 tokens, FFN 8192, hidden 2048) run in the launch
 configuration the benchmark uses and are checked on sampled row blocks
@@ -95,11 +98,14 @@ def test_swiglu_fwd_output_subsets(pf):
 
 
 def _wide_gate(rows, f, seed):
-    """gate | up with the gate spread over [-80, 80] (the range the C header
-    states the error bound for) and up ~ N(0, 1)."""
+    """gate | up with the gate spread over [-80, 80] and, in every fifth row,
+    over [-104, -64] (where sigmoid(gate) is below 2^-92 and the results head
+    for the subnormal range), up ~ N(0, 1)."""
     d = synth.swiglu_inputs(rows, f, seed=seed)
     gu = d["gu"].float()
     gu[:, :f] = (gu[:, :f] * 8.0).clamp(-80.0, 80.0)
+    deep = torch.linspace(-104.0, -64.0, f)
+    gu[::5, :f] = deep[torch.randperm(f, generator=torch.Generator().manual_seed(seed))]
     return gu.to(torch.bfloat16), d["dh"]
 
 
@@ -228,28 +234,43 @@ def test_rmsnorm_block_stack_sampled(pf):
 def test_probe_sigmoid_within_its_bound(pf):
     """The FP32 sigmoid the SwiGLU producers evaluate, through
     puro_fp8_probe_sigmoid, against 1 / (1 + e^-g) in double precision on
-    2 x 64 runs of 2^18 consecutive FP32 inputs spread over [-88, 88]
-    (33.5 M values, both signs): relative error at most 5 * 2^-24, the budget
-    the producers' tolerance assumes, wherever the result is normal."""
+    3 x 64 runs of 2^18 consecutive FP32 inputs (50 M values) spread over
+    [0, 104] in both signs and packed into [-104, -80]: relative error at
+    most 5 * 2^-24 (the budget the producers' tolerance assumes) wherever the
+    result is normal, and below that (g < -87.3, a subnormal result) within
+    5 * 2^-24 of it plus half the subnormal spacing 2^-149, never flushed to
+    zero while the exact value is at least 2^-149."""
     import struct
-    lim = struct.unpack("<I", struct.pack("<f", 88.0))[0]
+    bits = lambda v: struct.unpack("<I", struct.pack("<f", v))[0]
     run = 1 << 18
     buf = torch.empty(run, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
     worst = 0.0
-    for sign in (0, 0x80000000):
-        say("probe_sigmoid", "negative" if sign else "positive", "64 runs of", run)
+    worst_sub = 0.0
+    n_sub = 0
+    for sign, lo, hi in ((0, 0.0, 104.0), (0x80000000, 0.0, 104.0), (0x80000000, 80.0, 104.0)):
+        say("probe_sigmoid", "-" if sign else "+", lo, hi, "64 runs of", run)
+        b0, b1 = bits(lo), bits(hi)
         for k in range(64):
-            first = (k * (lim - run)) // 63 | sign
+            first = (b0 + (k * (b1 - b0 - run)) // 63) | sign
             assert pf.puro_fp8_probe_sigmoid(first, run, buf.data_ptr(), stream) == 0
             got = host(buf).astype(np.float64)
             g = np.arange(first, first + run, dtype=np.uint64).astype(np.uint32).view(np.float32)
             ref = 1.0 / (1.0 + np.exp(-g.astype(np.float64)))
             normal = ref >= 2.0 ** -126
-            err = np.abs(got[normal] - ref[normal]) / ref[normal]
-            worst = max(worst, float(err.max()))
-    say(f"   max relative error {worst / 2.0 ** -24:.3f} x 2^-24")
+            if normal.any():
+                err = np.abs(got[normal] - ref[normal]) / ref[normal]
+                worst = max(worst, float(err.max()))
+            sub = ~normal & (ref >= 2.0 ** -149)
+            if sub.any():
+                n_sub += int(sub.sum())
+                excess = np.abs(got[sub] - ref[sub]) - 5 * 2.0 ** -24 * ref[sub]
+                worst_sub = max(worst_sub, float(excess.max()))
+                assert np.all(got[sub] > 0.0)
+    say(f"   max relative error {worst / 2.0 ** -24:.3f} x 2^-24; {n_sub} subnormal results, "
+        f"worst excess {worst_sub / 2.0 ** -149:.3f} x 2^-149")
     assert worst <= 5 * 2.0 ** -24
+    assert n_sub > 0 and worst_sub <= 2.0 ** -150
 
 
 # ---- RMSNorm backward plus the skip path; residual add with rstd -----------------
