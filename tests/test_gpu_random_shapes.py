@@ -1,9 +1,10 @@
 """Seeded sweep over random ragged shapes, through the C ABI: quantizer codes
 and scales bit-exact against the oracle, GEMM outputs within the gates of
-tests/parity.py, in every mode, and the quantize-on-produce kernels (SwiGLU
-forward and backward, RMSNorm) against the oracle's band.  Complements the hand-picked shapes of the
-other GPU tests with shapes nobody chose (token counts from 1 to a few
-thousand, every multiple of 128 for the feature dimensions in range)."""
+tests/parity.py, in every mode -- including shapes that take the split-K path
+(K >= 2048 with fewer than 256 output tiles) and the persistent multi-unit
+walk (more than 256 tiles) -- and the quantize-on-produce kernels (SwiGLU
+forward and backward, RMSNorm) against the oracle's band.  Complements the
+hand-picked shapes of the other GPU tests with shapes nobody chose."""
 from __future__ import annotations
 
 import numpy as np
@@ -11,7 +12,9 @@ import pytest
 import torch
 
 from parity import random_bf16, say
-from test_gpu_gemm import DGRAD, FWD, WGRAD, run_case
+from test_gpu_gemm import (B_KN, DGRAD, DGRAD_W, FWD, FWD_T, MODE_NAMES, ORACLE_MODE, WGRAD,
+                           device_operands, device_values, make_inputs, oracle_operands,
+                           run_case)
 from test_gpu_quant import _check_act
 
 pytestmark = pytest.mark.gpu
@@ -30,6 +33,38 @@ for mode in (FWD, DGRAD, WGRAD):
         else:
             out, acc = ("fp32", "bf16")[int(_RNG.integers(0, 2))], False
         GEMM_CASES.append((mode, T, d_in, d_out, out, acc))
+
+
+# split-K (K >= 16 K-blocks, fewer than 256 output tiles) in every mode, and
+# the persistent multi-unit walk (more than 256 output tiles)
+SPLITK_CASES = []
+for mode in (FWD, DGRAD, WGRAD, DGRAD_W, FWD_T):
+    if mode == WGRAD:
+        T = int(_RNG.integers(2048, 4200))
+        d_in, d_out = 128 * int(_RNG.integers(1, 9)), 128 * int(_RNG.integers(1, 9))
+    else:
+        T = int(_RNG.integers(1, 1500))
+        k_dim, n_dim = 128 * int(_RNG.integers(16, 41)), 128 * int(_RNG.integers(1, 9))
+        d_in, d_out = (k_dim, n_dim) if mode in (FWD, FWD_T) else (n_dim, k_dim)
+    SPLITK_CASES.append((mode, T, d_in, d_out, ("fp32", "bf16")[int(_RNG.integers(0, 2))]))
+MULTI_CASES = []
+for mode in (FWD, DGRAD, WGRAD, DGRAD_W, FWD_T):
+    if mode == WGRAD:     # M = d_out, N = d_in: > 256 tiles; K = T
+        T = int(_RNG.integers(1, 700))
+        d_in, d_out = 128 * int(_RNG.integers(34, 48)), 128 * int(_RNG.integers(34, 48))
+    else:                 # M = T, N = d_out (FWD) or d_in (DGRAD)
+        T = int(_RNG.integers(8300, 12000))
+        n_dim, k_dim = 128 * int(_RNG.integers(17, 40)), 128 * int(_RNG.integers(1, 9))
+        d_in, d_out = (k_dim, n_dim) if mode in (FWD, FWD_T) else (n_dim, k_dim)
+    MULTI_CASES.append((mode, T, d_in, d_out, ("fp32", "bf16")[int(_RNG.integers(0, 2))]))
+
+
+def _mnk(mode, T, d_in, d_out):
+    if mode in (FWD, FWD_T):
+        return T, d_out, d_in
+    if mode in (DGRAD, DGRAD_W):
+        return T, d_in, d_out
+    return d_out, d_in, (T + 127) // 128 * 128
 
 
 @pytest.fixture(scope="module")
@@ -63,6 +98,48 @@ def test_quant_weight_random(pf, n, k):
 def test_gemm_random(pf, mode, T, d_in, d_out, out, acc):
     run_case(pf, mode, T, d_in, d_out, torch.float32 if out == "fp32" else torch.bfloat16,
              seed=T + d_in + d_out, accumulate=acc)
+
+
+@pytest.mark.parametrize("mode,T,d_in,d_out,out", SPLITK_CASES)
+def test_gemm_random_split_k(pf, mode, T, d_in, d_out, out):
+    M, N, K = _mnk(mode, T, d_in, d_out)
+    assert (M + 255) // 256 * ((N + 255) // 256) < 256 and K >= 2048
+    assert pf.puro_fp8_gemm_workspace_bytes(mode, M, N, K) > 0      # the split-K path
+    run_case(pf, mode, T, d_in, d_out, torch.float32 if out == "fp32" else torch.bfloat16,
+             seed=T + d_in + d_out)
+
+
+@pytest.mark.parametrize("mode,T,d_in,d_out,out", MULTI_CASES)
+def test_gemm_random_multi_unit(pf, mode, T, d_in, d_out, out):
+    """More output tiles than compute units, through the linear-layer path:
+    device codes bit-exact, outputs on sampled elements plus whole first and
+    last rows and the last column."""
+    import hw_accum
+    import oracle
+    from parity import fmt, gemm_gates, host
+    M, N, K = _mnk(mode, T, d_in, d_out)
+    assert (M + 255) // 256 * ((N + 255) // 256) > 256
+    assert pf.puro_fp8_gemm_workspace_bytes(mode, M, N, K) == 0
+    x, w, dy = make_inputs(T, d_in, d_out, T + d_in + d_out)
+    say("gemm multi-unit", MODE_NAMES[mode], f"T={T} in={d_in} out={d_out}", out)
+    a, sa, b, sb = device_operands(pf, mode, x, w, dy)
+    out_dtype = torch.float32 if out == "fp32" else torch.bfloat16
+    c = pf.gemm_blockscaled(mode, a, sa, b, sb, out_dtype=out_dtype)
+    oa, osa, ob, osb = oracle_operands(mode, x, w, dy)
+    assert np.array_equal(host(a), oa)
+    assert np.array_equal(host(b).T if mode in B_KN else host(b), ob)
+    rng = np.random.default_rng(M + N)
+    ii = np.concatenate([rng.integers(0, M, 6000), np.zeros(N, np.int64), np.full(N, M - 1),
+                         np.arange(M)])
+    jj = np.concatenate([rng.integers(0, N, 6000), np.arange(N), np.arange(N),
+                         np.full(M, N - 1)])
+    omode = ORACLE_MODE[mode]
+    ref = oracle.gemm_blockscaled_at(omode, oa, osa, ob, osb, ii, jj)
+    bound = hw_accum.bounds(omode, oa, osa, ob, osb, ii, jj, ref)
+    g = gemm_gates(device_values(c)[ii, jj], ref, bound, out_dtype == torch.bfloat16,
+                   literal=omode != FWD)
+    say("   " + fmt(g))
+    assert g["ok"], g
 
 
 # ---- quantize-on-produce: random ragged shapes --------------------------------
