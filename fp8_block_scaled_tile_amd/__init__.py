@@ -36,11 +36,15 @@ __all__ = [
     "swiglu_quant", "swiglu_bwd_quant", "rmsnorm_quant", "library_path",
     "puro_fp8_rmsnorm_quant_rstd", "puro_fp8_rmsnorm_bwd_quant", "puro_bf16_residual_add_rstd",
     "rmsnorm_quant_rstd", "rmsnorm_bwd_quant", "residual_add_rstd",
+    "puro_fp8_quant_weight_grouped", "quant_weight_grouped", "WeightDesc",
+    "PURO_FP8_MAX_GROUPED_WEIGHTS",
 ]
 
 GEMM_FWD, GEMM_DGRAD, GEMM_WGRAD, GEMM_DGRAD_W, GEMM_FWD_T = 0, 1, 2, 3, 4
 OUT_BF16, OUT_FP32 = 0, 1
 PURO_FP8_NOALLOC_SCRATCH_BYTES = 64 << 20
+PURO_FP8_MAX_GROUPED_WEIGHTS = 16
+WeightDesc = _lib.WeightDesc
 PURO_OK = 0
 
 
@@ -62,6 +66,11 @@ def puro_fp8_quant_act(x, rows, cols, q, s, qt, st, stream) -> int:
 
 def puro_fp8_quant_weight(w, n, k, q, qt, s, stream) -> int:
     return _lib.get().puro_fp8_quant_weight(w, n, k, q, qt, s, stream)
+
+
+def puro_fp8_quant_weight_grouped(descs, count, stream) -> int:
+    """descs: a ctypes array of WeightDesc (or a pointer to its first element)."""
+    return _lib.get().puro_fp8_quant_weight_grouped(descs, count, stream)
 
 
 def puro_fp8_gemm_blockscaled(mode, M, N, K, a, sa, b, sb, c, c_dtype, accumulate, workspace,
@@ -368,6 +377,32 @@ def quant_weight(w, transpose: bool = True, codes: bool = True, stream=None):
     _check(puro_fp8_quant_weight(_ptr(w), n, k, _ptr(out.get("q")), _ptr(out.get("qt")),
                                  _ptr(out["s"]), _stream(stream)))
     return out
+
+
+def quant_weight_grouped(ws, transpose: bool = True, codes: bool = True, stream=None):
+    """Several bf16 [n, k] CUDA weights quantized 128x128 in one launch: a list
+    of dicts as quant_weight returns them, bit for bit."""
+    torch = _torch()
+    ws = [_bf16_2d(w, f"w[{i}]") for i, w in enumerate(ws)]
+    if len(ws) > PURO_FP8_MAX_GROUPED_WEIGHTS:
+        raise ValueError(f"quant_weight_grouped: at most {PURO_FP8_MAX_GROUPED_WEIGHTS} weights")
+    if not codes and not transpose:
+        raise ValueError("quant_weight_grouped: nothing to write (codes=False, transpose=False)")
+    if ws:
+        _same_device(ws[0], *ws[1:])
+    outs = []
+    descs = (WeightDesc * max(1, len(ws)))()
+    for i, w in enumerate(ws):
+        n, k = w.shape
+        o = {"s": torch.empty((n // 128, k // 128), dtype=torch.float32, device=w.device)}
+        if codes:
+            o["q"] = torch.empty((n, k), dtype=torch.uint8, device=w.device)
+        if transpose:
+            o["qt"] = torch.empty((k, n), dtype=torch.uint8, device=w.device)
+        descs[i] = WeightDesc(_ptr(w), n, k, _ptr(o.get("q")), _ptr(o.get("qt")), _ptr(o["s"]))
+        outs.append(o)
+    _check(puro_fp8_quant_weight_grouped(descs, len(ws), _stream(stream)))
+    return outs
 
 
 def gemm_blockscaled(mode: int, a, sa, b, sb, out_dtype=None, out=None, accumulate=False,

@@ -18,7 +18,14 @@ EXPORTS = (
     "puro_fp8_swiglu_quant", "puro_fp8_swiglu_bwd_quant", "puro_fp8_rmsnorm_quant",
     "puro_fp8_probe_sigmoid", "puro_fp8_probe_mfma", "puro_fp8_gemm_blockscaled_noalloc",
     "puro_fp8_rmsnorm_quant_rstd", "puro_fp8_rmsnorm_bwd_quant", "puro_bf16_residual_add_rstd",
+    "puro_fp8_quant_weight_grouped",
 )
+
+
+class WeightDesc(ctypes.Structure):
+    """puro_fp8_weight_desc: the arguments of one puro_fp8_quant_weight call."""
+    _fields_ = [("w", ctypes.c_void_p), ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("q", ctypes.c_void_p), ("qt", ctypes.c_void_p), ("s", ctypes.c_void_p)]
 
 
 def path() -> str:
@@ -75,5 +82,7 @@ def get():
         lib.puro_fp8_rmsnorm_bwd_quant.argtypes = [P, P, P, P, P, I64, I64, P, P, P, P, P, P, P]
         lib.puro_bf16_residual_add_rstd.restype = I
         lib.puro_bf16_residual_add_rstd.argtypes = [P, P, I64, I64, ctypes.c_float, P, P, P]
+        lib.puro_fp8_quant_weight_grouped.restype = I
+        lib.puro_fp8_quant_weight_grouped.argtypes = [ctypes.POINTER(WeightDesc), I, P]
         _handle = lib
         return lib

@@ -145,6 +145,34 @@ puro_status_t puro_fp8_quant_weight(const void* w, int64_t n, int64_t k, uint8_t
     });
 }
 
+puro_status_t puro_fp8_quant_weight_grouped(const puro_fp8_weight_desc* descs, int count,
+                                            void* stream)
+{
+    return guarded([&]() -> puro_status_t {
+        static_assert(PURO_FP8_MAX_GROUPED_WEIGHTS == puro::kMaxGroupedWeights, "group size");
+        if (count < 0 || count > PURO_FP8_MAX_GROUPED_WEIGHTS)
+            return PURO_ERR_BAD_SHAPE;
+        if (count == 0)
+            return PURO_OK;
+        if (!descs)
+            return PURO_ERR_NULL_POINTER;
+        puro::WeightJob jobs[puro::kMaxGroupedWeights];
+        int64_t blocks = 0;
+        for (int i = 0; i < count; ++i) {
+            const puro_fp8_weight_desc& d = descs[i];
+            const puro_status_t rc = check_weight(d.w, d.n, d.k, d.q, d.qt, d.s);
+            if (rc != PURO_OK)
+                return rc;
+            blocks += (d.n / 128) * (d.k / 128);
+            jobs[i] = puro::WeightJob{static_cast<const uint16_t*>(d.w), d.n, d.k, d.q, d.qt, d.s};
+        }
+        if (blocks > kMaxDim)       // one work-group per block, a 1-D grid
+            return PURO_ERR_BAD_SHAPE;
+        return from_hip(puro::launch_quant_weight_grouped(jobs, count,
+                                                          static_cast<hipStream_t>(stream)));
+    });
+}
+
 puro_status_t puro_fp8_swiglu_quant(const void* gu, int64_t rows, int64_t f, uint8_t* q,
                                     float* s, uint8_t* qt, float* st, void* y, void* stream)
 {

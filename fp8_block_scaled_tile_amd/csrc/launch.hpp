@@ -37,6 +37,17 @@ hipError_t launch_quant_act(const void* x, int64_t rows, int64_t cols, uint8_t* 
                             uint8_t* qt, float* st, hipStream_t stream);
 hipError_t launch_quant_weight(const void* w, int64_t n, int64_t k, uint8_t* q, uint8_t* qt,
                                float* s, hipStream_t stream);
+// One launch over several weights: d[i] = (w, n, k, q, qt, s) of one
+// puro_fp8_quant_weight call each, count <= kMaxGroupedWeights.
+constexpr int kMaxGroupedWeights = 16;
+struct WeightJob {
+    const uint16_t* w;
+    int64_t n, k;
+    uint8_t* q;
+    uint8_t* qt;
+    float* s;
+};
+hipError_t launch_quant_weight_grouped(const WeightJob* jobs, int count, hipStream_t stream);
 hipError_t launch_swiglu_quant(const void* gu, int64_t rows, int64_t f, uint8_t* q, float* s,
                                uint8_t* qt, float* st, void* h, hipStream_t stream);
 hipError_t launch_swiglu_bwd_quant(const void* dh, const void* gu, int64_t rows, int64_t f,

@@ -33,6 +33,39 @@ __global__ __launch_bounds__(256) void quant_block_kernel(
     quant_block_body<ROW, COL, WEIGHT, WT>(v, rows, cols, ld_t, b.rb, b.cb, q, s, qt, st, lds);
 }
 
+// Several weights in one launch: work-group b takes block b - first[i] of
+// weight i, first[i] <= b < first[i + 1] (a uniform scalar search over at
+// most 16 entries), and quantizes it exactly as quant_block_kernel does for
+// that weight alone (same block walk inside the weight, same body).  With WT,
+// a weight whose qt is NULL skips the transposed copy.
+struct WeightJobs {
+    WeightJob j[kMaxGroupedWeights];
+    int64_t first[kMaxGroupedWeights + 1];
+    int count;
+    int group_rows;
+};
+
+template <bool WT>
+__global__ __launch_bounds__(256) void quant_weight_grouped_kernel(const WeightJobs jobs)
+{
+    __shared__ QuantLds<false, false, true, WT> lds;
+    const int t = threadIdx.x;
+    const int64_t bid = blockIdx.x;
+    int i = 0;
+    while (i + 1 < jobs.count && bid >= jobs.first[i + 1])
+        ++i;
+    const WeightJob J = jobs.j[i];
+    const BlockRC b = block_of(bid - jobs.first[i], J.n / 128, J.k / 128, jobs.group_rows);
+    const int64_t row0 = b.rb * 128 + 8 * (t >> 4);
+    const int64_t col0 = b.cb * 128 + 8 * (t & 15);
+    uint4 v[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p)
+        v[p] = *reinterpret_cast<const uint4*>(J.w + (row0 + p) * J.k + col0);
+    quant_block_body<false, false, true, WT>(v, J.n, J.k, J.n, b.rb, b.cb, J.q, J.s, J.qt, nullptr,
+                                            lds);
+}
+
 // Diagnostic: E4M3 code of every binary32 bit pattern first + i, i < n.
 __global__ __launch_bounds__(256) void probe_encode_kernel(uint32_t first, int64_t n,
                                                            uint8_t* __restrict__ out)
@@ -83,6 +116,28 @@ hipError_t launch_quant_weight(const void* w, int64_t n, int64_t k, uint8_t* q, 
                              wb, n, k, n, q, s, qt, nullptr, gr);
     return launch_kernel(quant_block_kernel<false, false, true, false>, grid, dim3(256), stream,
                          wb, n, k, n, q, s, nullptr, nullptr, gr);
+}
+
+hipError_t launch_quant_weight_grouped(const WeightJob* jobs, int count, hipStream_t stream)
+{
+    WeightJobs g{};
+    bool any_t = false;
+    int64_t total = 0;
+    for (int i = 0; i < count; ++i) {
+        g.j[i] = jobs[i];
+        g.first[i] = total;
+        total += (jobs[i].n / 128) * (jobs[i].k / 128);
+        any_t = any_t || jobs[i].qt != nullptr;
+    }
+    g.first[count] = total;
+    g.count = count;
+    g.group_rows = quant_group_rows(true, 0);
+    if (count == 0 || total == 0)
+        return hipSuccess;
+    const dim3 grid((unsigned)total);
+    if (any_t)
+        return launch_kernel(quant_weight_grouped_kernel<true>, grid, dim3(256), stream, g);
+    return launch_kernel(quant_weight_grouped_kernel<false>, grid, dim3(256), stream, g);
 }
 
 hipError_t launch_probe_encode(uint32_t first, int64_t n, uint8_t* out, hipStream_t stream)

@@ -152,7 +152,10 @@ __device__ __forceinline__ void quant_block_body(const uint4 (&v)[8], int64_t ro
     }
 
     // ---- transposed codes (128x1 tiles, or the weight block transposed) -
+    // (a weight of a grouped launch may pass qt = NULL: uniform per block)
     if constexpr (TRANS) {
+        if (WEIGHT && qt == nullptr)
+            return;
         if constexpr (COL) {
             int cm[8];
 #pragma unroll

@@ -43,7 +43,8 @@ def test_header_declares_the_entry_points():
               "puro_fp8_swiglu_bwd_quant", "puro_fp8_rmsnorm_quant", "puro_bf16_gemm_nt",
               "puro_fp8_probe_sigmoid", "puro_fp8_probe_mfma",
               "puro_fp8_gemm_blockscaled_noalloc", "puro_fp8_rmsnorm_quant_rstd",
-              "puro_fp8_rmsnorm_bwd_quant", "puro_bf16_residual_add_rstd"):
+              "puro_fp8_rmsnorm_bwd_quant", "puro_bf16_residual_add_rstd",
+              "puro_fp8_quant_weight_grouped"):
         assert n in names
 
 
@@ -226,6 +227,22 @@ def test_swiglu_bwd_quant_validation(lib):
     assert f(P16, P_ODD, 16, 128, P16, P16, None, None, None, None) == ALIGN
     assert f(P16, P16, 16, 128, None, None, P16, P_ODD, None, None) == ALIGN
     assert f(P16, P16, 0, 128, P16, P16, None, None, None, None) == OK
+
+
+def test_quant_weight_grouped_validation(lib):
+    f = lib.puro_fp8_quant_weight_grouped
+    D = lib.WeightDesc
+    good = lambda: D(P16, 256, 384, P16, None, P16)
+    arr = lambda *ds: (D * len(ds))(*ds)
+    assert f(None, 0, None) == OK                                          # nothing to do
+    assert f(None, 1, None) == NULLP
+    assert f(arr(good()), -1, None) == SHAPE
+    assert f(arr(*[good() for _ in range(17)]), 17, None) == SHAPE         # more than 16
+    assert f(arr(good(), D(P16, 200, 384, P16, None, P16)), 2, None) == SHAPE
+    assert f(arr(good(), D(P16, 256, 384, None, None, P16)), 2, None) == NULLP   # no codes at all
+    assert f(arr(good(), D(P16, 256, 384, P16, P16, None)), 2, None) == NULLP    # no scales
+    assert f(arr(D(P_ODD, 256, 384, P16, None, P16)), 1, None) == ALIGN
+    assert f(arr(good(), D(P16, 256, 384, P16, P_ODD, P16)), 2, None) == ALIGN
 
 
 def test_rmsnorm_quant_validation(lib):

@@ -210,3 +210,46 @@ def test_quant_weight(pf, n, k):
     assert "q" not in out3
     assert np.array_equal(host(out3["qt"]), qt)
     assert np.array_equal(host(out3["s"]).view(np.uint32), s.view(np.uint32))
+
+
+def test_quant_weight_grouped_equals_separate_launches(pf):
+    """One launch over a block's four weights (with each combination of code
+    copies) gives each weight's codes and scales bit for bit as its own
+    puro_fp8_quant_weight launch, and as the oracle."""
+    import oracle
+    shapes = [(768, 256), (256, 256), (2048, 256), (256, 1024)]        # qkv, out, up/gate, down
+    ws = [synth.normal(sh, 0.02, 7, f"grouped/{sh[0]}x{sh[1]}").to(torch.bfloat16) for sh in shapes]
+    dws = [dev(w) for w in ws]
+    for transpose, codes in ((True, True), (False, True), (True, False)):
+        say("quant_weight_grouped", len(ws), "transpose" if transpose else "", "codes" if codes else "")
+        got = pf.quant_weight_grouped(dws, transpose=transpose, codes=codes)
+        for w, dw, g in zip(ws, dws, got):
+            one = pf.quant_weight(dw, transpose=transpose, codes=codes)
+            for k in one:
+                assert torch.equal(g[k], one[k]), k
+            q, qt, s = oracle.quant_weight(synth.bits(w), transpose=True)
+            assert np.array_equal(host(g["s"]).view(np.uint32), s.view(np.uint32))
+            if codes:
+                assert np.array_equal(host(g["q"]), q)
+            if transpose:
+                assert np.array_equal(host(g["qt"]), qt)
+
+
+def test_quant_weight_grouped_mixed_copies(pf):
+    """Descriptors of one launch may ask for different code copies."""
+    ws = [dev(synth.normal((384, 512), 0.02, i, f"grouped-mixed/{i}").to(torch.bfloat16))
+          for i in range(3)]
+    outs = [{"s": torch.empty((3, 4), dtype=torch.float32, device="cuda")} for _ in ws]
+    outs[0]["q"] = torch.empty((384, 512), dtype=torch.uint8, device="cuda")
+    outs[1]["qt"] = torch.empty((512, 384), dtype=torch.uint8, device="cuda")
+    outs[2]["q"] = torch.empty((384, 512), dtype=torch.uint8, device="cuda")
+    outs[2]["qt"] = torch.empty((512, 384), dtype=torch.uint8, device="cuda")
+    P = lambda t: None if t is None else t.data_ptr()
+    descs = (pf.WeightDesc * 3)(*[pf.WeightDesc(P(w), 384, 512, P(o.get("q")), P(o.get("qt")),
+                                               P(o["s"])) for w, o in zip(ws, outs)])
+    say("quant_weight_grouped mixed copies")
+    assert pf.puro_fp8_quant_weight_grouped(descs, 3, torch.cuda.current_stream().cuda_stream) == 0
+    for w, o in zip(ws, outs):
+        ref = pf.quant_weight(w, transpose=True)
+        for k in o:
+            assert torch.equal(o[k], ref[k]), k
