@@ -105,6 +105,8 @@ KERNEL_SYMBOLS = {
     "quant_act_col": "void puro::quant_block_kernel<false, true, false, false>",
     "quant_weight_t": "void puro::quant_block_kernel<false, false, true, true>",
     "quant_weight": "void puro::quant_block_kernel<false, false, true, false>",
+    "quant_weight_grouped": "void puro::quant_weight_grouped_kernel<false>",
+    "quant_weight_grouped_t": "void puro::quant_weight_grouped_kernel<true>",
 }
 
 # Operand layout of each linear layer's FWD and DGRAD GEMMs in the step.  The
@@ -134,6 +136,8 @@ def parse_args():
     p.add_argument("--layout", choices=sorted(LAYOUTS), default="w",
                    help="operand layout of each layer's FWD / DGRAD GEMMs (w: both on the "
                         "weight's own codes, no transposed copy; nk: DGRAD on the transposed copy)")
+    p.add_argument("--weight-launch", choices=("grouped", "per-layer"), default="grouped",
+                   help="quantize every layer's weight in one launch (default) or one launch each")
     p.add_argument("--cpu-tokens", type=int, default=3072,
                    help="token slice for the CPU-oracle baseline (0 = skip)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -278,10 +282,23 @@ def _act_class(row, col):
     return "quant_act_dual" if row and col else ("quant_act_row" if row else "quant_act_col")
 
 
-def step_calls(pf, layers, stream):
+def step_calls(pf, layers, stream, grouped_weights=False):
     """The launches of one step in order: (layer, class, work, fn), where work
-    is the launch's algorithmic bytes (quantizers) or FLOP (GEMMs)."""
+    is the launch's algorithmic bytes (quantizers) or FLOP (GEMMs).  With
+    grouped_weights, every layer's weight is quantized by one launch at the
+    start of the step instead of one launch per layer."""
     P = lambda t: None if t is None else t.data_ptr()
+    wl = [L for L in layers if L.need_q or L.need_qt]
+    grouped = grouped_weights and len(wl) > 1
+    head = []
+    if grouped:
+        descs = (pf.WeightDesc * len(wl))(*[
+            pf.WeightDesc(P(L.w), L.dout, L.din, P(L.qw) if L.need_q else None,
+                          P(L.qtw) if L.need_qt else None, P(L.sw)) for L in wl])
+        any_t = any(L.need_qt for L in wl)
+        work = sum(weight_bytes(L.dout, L.din, int(L.need_q) + int(L.need_qt)) for L in wl)
+        head.append(("all", "quant_weight_grouped_t" if any_t else "quant_weight_grouped", work,
+                     lambda: pf.puro_fp8_quant_weight_grouped(descs, len(wl), stream)))
 
     def layer_calls(L):     # a scope per layer: each lambda binds its own L
         sp = L.spec
@@ -290,7 +307,7 @@ def step_calls(pf, layers, stream):
             calls.append((_act_class(L.x_row, L.x_col), act_bytes(L.T, L.din, L.x_row, L.x_col),
                           lambda: pf.puro_fp8_quant_act(P(L.x), L.T, L.din, P(L.qx), P(L.sx),
                                                         P(L.qtx), P(L.stx), stream)))
-        if L.need_q or L.need_qt:
+        if (L.need_q or L.need_qt) and not grouped:
             calls.append(("quant_weight_t" if L.need_qt else "quant_weight",
                           weight_bytes(L.dout, L.din, int(L.need_q) + int(L.need_qt)),
                           lambda: pf.puro_fp8_quant_weight(P(L.w), L.dout, L.din, P(L.qw),
@@ -318,13 +335,14 @@ def step_calls(pf, layers, stream):
                               P(L.stx), P(L.dw), pf.OUT_FP32, 0, P(L.ws), L.ws.numel(), stream)))
         return calls
 
-    return [(L.spec.name, name, work, fn) for L in layers for name, work, fn in layer_calls(L)]
+    return head + [(L.spec.name, name, work, fn) for L in layers
+                   for name, work, fn in layer_calls(L)]
 
 
-def run_step(pf, layers, stream, rec=None):
+def run_step(pf, layers, stream, rec=None, grouped_weights=False):
     """Enqueue one step.  rec(name, work) returns (start_event, end_event) to
     bracket a launch, or None to launch unbracketed."""
-    for _, name, work, fn in step_calls(pf, layers, stream):
+    for _, name, work, fn in step_calls(pf, layers, stream, grouped_weights):
         ev = rec(name, work) if rec else None
         if ev:
             ev[0].record()
@@ -333,14 +351,14 @@ def run_step(pf, layers, stream, rec=None):
             ev[1].record()
 
 
-def cold_kernel_stats(torch, pf, layers, stream, iters):
+def cold_kernel_stats(torch, pf, layers, stream, iters, grouped_weights=False):
     """Every launch of one step on its own, `iters` times, each right after a
     512 MiB write that evicts the L2s and the MALL: median, p10 and p90 of the
     event-timed duration per launch, and the rate at the median."""
     import numpy as np
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     out = []
-    for layer, name, work, fn in step_calls(pf, layers, stream):
+    for layer, name, work, fn in step_calls(pf, layers, stream, grouped_weights):
         evs = []
         for _ in range(iters):
             flush.fill_(1)
@@ -953,9 +971,10 @@ def main():
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream().cuda_stream
     step_flops = sum(L.flops() for L in layers)
+    gw = args.weight_launch == "grouped"
 
     for _ in range(args.warmup):
-        run_step(pf, layers, stream)
+        run_step(pf, layers, stream, grouped_weights=gw)
     torch.cuda.synchronize()
 
     # timed region: K steps.  Only the launches of the two largest GEMM
@@ -979,7 +998,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        run_step(pf, layers, stream, rec)
+        run_step(pf, layers, stream, rec, grouped_weights=gw)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
@@ -991,7 +1010,7 @@ def main():
     rec_all = recorder(all_events)
     t1 = time.perf_counter()
     for _ in range(args.steps):
-        run_step(pf, layers, stream, rec_all)
+        run_step(pf, layers, stream, rec_all, grouped_weights=gw)
     torch.cuda.synchronize()
     ms_all_events = (time.perf_counter() - t1) * 1e3 / args.steps
 
@@ -1072,7 +1091,7 @@ def main():
     cold = None
     copy_ref = None
     if not args.no_cold_stats:
-        cold = cold_kernel_stats(torch, pf, layers, stream, args.cold_iters)
+        cold = cold_kernel_stats(torch, pf, layers, stream, args.cold_iters, gw)
         copy_ref = hbm_copy_reference(torch)
 
     cpu = None
@@ -1100,6 +1119,7 @@ def main():
                        gemms={L.spec.name: [g[0] for g in L.gemms] for L in layers},
                        gemm_tflop_per_step=round(step_flops / 1e12, 4),
                        operand_layout={L.spec.name: list(L.layout) for L in layers},
+                       weight_launch=args.weight_launch,
                        parallelism="single GPU"),
         "pct_of_fp8_peak": round(100.0 * value / FP8_PEAK_TFLOPS, 2),
         "gemm_only_tflops": round(step_flops / (gemm_ms * 1e-3) / 1e12, 1) if gemm_ms else None,

@@ -104,6 +104,33 @@ def test_step_calls_follow_the_layer_gemm_set():
     assert calls[5][2] == bench.act_dual_bytes(16384, 2048)
 
 
+def test_step_calls_grouped_weights():
+    """With grouped weights the step starts with one launch over every
+    layer's weight (each with the code copies its GEMMs read) and the layers
+    launch no weight quantizer of their own."""
+    import ctypes
+    seen = []
+    pf = _pf(seen)
+
+    class Desc(ctypes.Structure):
+        _fields_ = [("w", ctypes.c_void_p), ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+                    ("q", ctypes.c_void_p), ("qt", ctypes.c_void_p), ("s", ctypes.c_void_p)]
+    pf.WeightDesc = Desc
+    pf.puro_fp8_quant_weight_grouped = lambda d, n, st: seen.append(
+        ("grouped", n, [(d[i].n, d[i].k, d[i].q, d[i].qt) for i in range(n)])) or 0
+    layers = [_layer("a", 256, 128, 384, dgrad_mode=3), _layer("b", 512, 256, 128, fwd_mode=4)]
+    calls = bench.step_calls(pf, layers, None, grouped_weights=True)
+    assert [c[1] for c in calls][:1] == ["quant_weight_grouped_t"]
+    assert not any(c[1].startswith("quant_weight") for c in calls[1:])
+    for _, _, _, fn in calls:
+        assert fn() == 0
+    assert seen[0] == ("grouped", 2, [(384, 128, 16, None), (128, 256, None, 32)])
+    assert calls[0][2] == bench.weight_bytes(384, 128, 1) + bench.weight_bytes(128, 256, 1)
+    # one weight only: the per-layer launch
+    one = bench.step_calls(pf, layers[:1], None, grouped_weights=True)
+    assert [c[1] for c in one][1] == "quant_weight"
+
+
 def test_configs_name_the_workloads():
     import synth
     assert bench.CONFIGS["c5"] == "block_stack"
