@@ -101,8 +101,8 @@ def puro_fp8_probe_encode(first_bits, n, out, stream) -> int:
     return _lib.get().puro_fp8_probe_encode(first_bits, n, out, stream)
 
 
-def puro_fp8_probe_sigmoid(first_bits, n, out, stream) -> int:
-    return _lib.get().puro_fp8_probe_sigmoid(first_bits, n, out, stream)
+def puro_fp8_probe_sigmoid(first_bits, n, form, out, stream) -> int:
+    return _lib.get().puro_fp8_probe_sigmoid(first_bits, n, form, out, stream)
 
 
 def puro_fp8_probe_mfma(form, a, b, scale_a, scale_b, d, stream) -> int:

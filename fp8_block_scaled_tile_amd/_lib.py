@@ -62,7 +62,7 @@ def get():
         lib.puro_fp8_probe_encode.restype = I
         lib.puro_fp8_probe_encode.argtypes = [ctypes.c_uint32, I64, P, P]
         lib.puro_fp8_probe_sigmoid.restype = I
-        lib.puro_fp8_probe_sigmoid.argtypes = [ctypes.c_uint32, I64, P, P]
+        lib.puro_fp8_probe_sigmoid.argtypes = [ctypes.c_uint32, I64, I, P, P]
         lib.puro_fp8_probe_mfma.restype = I
         lib.puro_fp8_probe_mfma.argtypes = [I, P, P, I, I, P, P]
         lib.puro_bf16_gemm_nt.restype = I

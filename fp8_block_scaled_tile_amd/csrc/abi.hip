@@ -396,9 +396,12 @@ puro_status_t puro_fp8_probe_encode(uint32_t first_bits, int64_t n, uint8_t* out
     });
 }
 
-puro_status_t puro_fp8_probe_sigmoid(uint32_t first_bits, int64_t n, float* out, void* stream)
+puro_status_t puro_fp8_probe_sigmoid(uint32_t first_bits, int64_t n, int form, float* out,
+                                     void* stream)
 {
     return guarded([&]() -> puro_status_t {
+        if (form < 0 || form > 2)
+            return PURO_ERR_BAD_ENUM;
         if (n < 0)
             return PURO_ERR_BAD_SHAPE;
         if (n == 0)
@@ -407,7 +410,7 @@ puro_status_t puro_fp8_probe_sigmoid(uint32_t first_bits, int64_t n, float* out,
             return PURO_ERR_NULL_POINTER;
         if ((reinterpret_cast<uintptr_t>(out) & 3u) != 0)
             return PURO_ERR_MISALIGNED;
-        return from_hip(puro::launch_probe_sigmoid(first_bits, n, out,
+        return from_hip(puro::launch_probe_sigmoid(first_bits, n, form, out,
                                                    static_cast<hipStream_t>(stream)));
     });
 }

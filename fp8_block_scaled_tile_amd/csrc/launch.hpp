@@ -66,7 +66,8 @@ hipError_t launch_rmsnorm_bwd_quant(const void* dy, const void* x, const void* g
 hipError_t launch_residual_rstd(const void* a, const void* b, int64_t rows, int64_t cols, float eps,
                                 void* h, float* rstd, hipStream_t stream);
 hipError_t launch_probe_encode(uint32_t first, int64_t n, uint8_t* out, hipStream_t stream);
-hipError_t launch_probe_sigmoid(uint32_t first, int64_t n, float* out, hipStream_t stream);
+hipError_t launch_probe_sigmoid(uint32_t first, int64_t n, int form, float* out,
+                                hipStream_t stream);
 hipError_t launch_probe_mfma(int form, const uint8_t* a, const uint8_t* b, int scale_a,
                              int scale_b, float* d, hipStream_t stream);
 

@@ -60,51 +60,84 @@ __device__ __forceinline__ float exp_f32_shifted(float t, float k)
     return r * (1.0f + y_lo * kLn2);
 }
 
-// sigmoid(g) and 1 - sigmoid(g) in FP32 from one exponential that never
-// overflows: with e = e^-|g| in (0, 1] and s = 1 / (1 + e) (the hardware
-// reciprocal, within 1 ulp), sigmoid is s for g >= 0 and e * s for g < 0, and
-// 1 - sigmoid the other one.  For g >= 0 a relative error of e reaches s
-// damped by e / (1 + e); for g < 0 it reaches e * s in full, so the bound is
-// exp_f32's plus the add, the reciprocal and the product: about 5 units of
-// 2^-24 (measured 4.5 over [-87, 0), 2.2 over [0, 104]).
+// Two FP32 forms of sigmoid(g) = 1 / (1 + e^-g); the SwiGLU producers pick
+// one per wave.
 //
-// Below g = -64 sigmoid is e^g to FP32 precision and heads for the
-// subnormal range (from g = -87.3), where the hardware 2^x returns zero.
-// There the pair is returned scaled: p = sigmoid(g) * 2^64 (from
-// exp_f32_shifted, a normal number down to g = -131), and the caller
-// multiplies its result by `scale` = 2^-64 as the last step, so only that
-// one rounding can be subnormal.  Above -64 scale = 1 and the arithmetic is
-// the plain one.  (Products by 2^64 and 2^-64 are exact on normal numbers,
-// so wherever the result is normal both orders give the same bits.)
+// The plain form, s = rcp(1 + e^-g) with the hardware reciprocal (within
+// 1 ulp), and 1 - sigmoid as 1 - s: a relative error of e^-g reaches s
+// damped by e^-g / (1 + e^-g), so it stays within about 5 units of 2^-24
+// (measured 4.1 over every FP32 g in [-88, 88] with a normal result).  It
+// serves every wave whose gates are all >= -64.
+//
+// The deep form, for a wave with a gate below -64: from e = e^-|g| in
+// (0, 1] and s = 1 / (1 + e), sigmoid is s for g >= 0 and e * s for g < 0
+// (1 - sigmoid the other one), so nothing overflows; below g = -64 sigmoid is
+// e^g to FP32 precision and heads for the subnormal range (from g = -87.3),
+// where the hardware 2^x returns zero.  There the pair is returned scaled:
+// p = sigmoid(g) * 2^64 (from exp_f32_shifted, a normal number down to
+// g = -131), and the caller multiplies its result by `scale` = 2^-64 as the
+// last step, so only that one rounding can be subnormal.  For g < 0 a
+// relative error of e reaches e * s in full: about 5 units of 2^-24
+// (measured 4.5).  (Products by 2^64 and 2^-64 are exact on normal numbers,
+// so wherever the result is normal the scaled order gives the same bits.)
 struct Sig {
     float p;        // sigmoid(g), times 1 / scale
     float q;        // 1 - sigmoid(g)
-    float scale;    // 1, or 2^-64 below g = -64
+    float scale;    // 1, or 2^-64 below g = -64 in the deep form
 };
 
+template <bool DEEP>
 __device__ __forceinline__ Sig sigmoid_pair(float g)
 {
-    const bool deep = g < -64.0f;
-    const float e = exp_f32_shifted(-__builtin_fabsf(g), deep ? 64.0f : 0.0f);
-    const float s = __builtin_amdgcn_rcpf(1.0f + (deep ? 0.0f : e));   // e < 2^-92 when deep
-    const float es = e * s;
-    if (g >= 0.0f)
-        return Sig{s, es, 1.0f};
-    return Sig{es, s, deep ? 0x1p-64f : 1.0f};
+    if constexpr (!DEEP) {
+        const float s = __builtin_amdgcn_rcpf(1.0f + exp_f32_shifted(-g, 0.0f));
+        return Sig{s, 1.0f - s, 1.0f};
+    } else {
+        const bool deep = g < -64.0f;
+        const float e = exp_f32_shifted(-__builtin_fabsf(g), deep ? 64.0f : 0.0f);
+        const float s = __builtin_amdgcn_rcpf(1.0f + (deep ? 0.0f : e));   // e < 2^-92 if deep
+        const float es = e * s;
+        if (g >= 0.0f)
+            return Sig{s, es, 1.0f};
+        return Sig{es, s, deep ? 0x1p-64f : 1.0f};
+    }
 }
 
-__device__ __forceinline__ float sigmoid_f32(float g)
+// Does any lane of the wave hold a gate below -64 among its eight chunks of
+// eight bf16 values?  (A negative bf16 below -64 has bits above 0xC280 as an
+// unsigned 16-bit number.)  Wave-uniform.
+__device__ __forceinline__ bool wave_has_deep_gate(const uint4 (&gv)[8])
 {
-    const Sig sg = sigmoid_pair(g);
-    return sg.p * sg.scale;
+    uint32_t m = 0;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const uint32_t w[4] = {gv[p].x, gv[p].y, gv[p].z, gv[p].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            m = max(m, max(w[i] & 0xFFFFu, w[i] >> 16));
+    }
+    return __builtin_amdgcn_ballot_w64(m > 0xC280u) != 0;
 }
 
-// The sigmoid on consecutive FP32 bit patterns (puro_fp8_probe_sigmoid).
-__global__ __launch_bounds__(256) void probe_sigmoid_kernel(uint32_t first, int64_t n, float* out)
+// The sigmoid on consecutive FP32 bit patterns (puro_fp8_probe_sigmoid):
+// form 0 picks per wave as the producers do, 1 is the plain form, 2 the deep
+// form; the deep form's scaled value is scaled back.
+__global__ __launch_bounds__(256) void probe_sigmoid_kernel(uint32_t first, int64_t n, int form,
+                                                            float* out)
 {
     const int64_t stride = (int64_t)gridDim.x * 256;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride)
-        out[i] = sigmoid_f32(__uint_as_float(first + (uint32_t)i));
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
+        const float g = __uint_as_float(first + (uint32_t)i);
+        bool deep = form == 2;
+        if (form == 0)
+            deep = __builtin_amdgcn_ballot_w64(g < -64.0f) != 0;
+        Sig sg;
+        if (deep)
+            sg = sigmoid_pair<true>(g);
+        else
+            sg = sigmoid_pair<false>(g);
+        out[i] = sg.p * sg.scale;
+    }
 }
 
 __device__ __forceinline__ uint4 load16(const uint16_t* p)
@@ -133,30 +166,37 @@ __device__ __forceinline__ uint4 map8(const uint4& a, const uint4& b, const uint
     return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-// h = silu(g) * u = (g * sigmoid(g)) * u.
+// h = silu(g) * u = (g * sigmoid(g)) * u.  (The plain form's scale is 1,
+// and the product by it is dropped at compile time.)
+template <bool DEEP>
 struct SwigluH {
     __device__ float operator()(float g, float u, float) const
     {
-        const Sig sg = sigmoid_pair(g);
-        return ((g * sg.p) * u) * sg.scale;
+        const Sig sg = sigmoid_pair<DEEP>(g);
+        const float r = (g * sg.p) * u;
+        return DEEP ? r * sg.scale : r;
     }
 };
 
 // d gate = ((dh * u) * sigmoid(g)) * (1 + g * (1 - sigmoid(g))).
+template <bool DEEP>
 struct SwigluDGate {
     __device__ float operator()(float g, float u, float dh) const
     {
-        const Sig sg = sigmoid_pair(g);
-        return (((dh * u) * sg.p) * __builtin_fmaf(g, sg.q, 1.0f)) * sg.scale;
+        const Sig sg = sigmoid_pair<DEEP>(g);
+        const float r = ((dh * u) * sg.p) * __builtin_fmaf(g, sg.q, 1.0f);
+        return DEEP ? r * sg.scale : r;
     }
 };
 
 // d up = dh * (g * sigmoid(g)).
+template <bool DEEP>
 struct SwigluDUp {
     __device__ float operator()(float g, float, float dh) const
     {
-        const Sig sg = sigmoid_pair(g);
-        return (dh * (g * sg.p)) * sg.scale;
+        const Sig sg = sigmoid_pair<DEEP>(g);
+        const float r = dh * (g * sg.p);
+        return DEEP ? r * sg.scale : r;
     }
 };
 
@@ -184,13 +224,19 @@ __global__ __launch_bounds__(256) void swiglu_quant_kernel(
         uv[p] = r < rows ? load16(gu + r * 2 * f + f + col0) : kZero4;
     }
     uint4 v[8];
+    auto produce = [&](auto fn) __attribute__((always_inline)) {
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-        // rows past the end hold zeros (silu(0) * 0 = +0), as the body requires
-        v[p] = row0 + p < rows ? map8(gv[p], uv[p], kZero4, SwigluH{}) : kZero4;
-        if (STORE_Y && row0 + p < rows)
-            store16(h + (row0 + p) * f + col0, v[p]);
-    }
+        for (int p = 0; p < 8; ++p) {
+            // rows past the end hold zeros (silu(0) * 0 = +0), as the body requires
+            v[p] = row0 + p < rows ? map8(gv[p], uv[p], kZero4, fn) : kZero4;
+            if (STORE_Y && row0 + p < rows)
+                store16(h + (row0 + p) * f + col0, v[p]);
+        }
+    };
+    if (wave_has_deep_gate(gv))
+        produce(SwigluH<true>{});
+    else
+        produce(SwigluH<false>{});
     if constexpr (ROW || COL)
         quant_block_body<ROW, COL, false, false>(v, rows, f, ld_t, b.rb, b.cb, q, s, qt, st, lds);
 }
@@ -219,16 +265,22 @@ __global__ __launch_bounds__(256) void swiglu_bwd_quant_kernel(
             gv[p] = r < rows ? load16(gu + r * 2 * f + col0) : kZero4;
             uv[p] = r < rows ? load16(gu + r * 2 * f + f + col0) : kZero4;
         }
+        auto produce = [&](auto fg, auto fu) __attribute__((always_inline)) {
 #pragma unroll
-        for (int p = 0; p < 8; ++p) {
-            const bool in = row0 + p < rows;
-            dg[p] = in ? map8(gv[p], uv[p], dv[p], SwigluDGate{}) : kZero4;
-            du[p] = in ? map8(gv[p], uv[p], dv[p], SwigluDUp{}) : kZero4;
-            if (STORE_Y && in) {
-                store16(dgu + (row0 + p) * 2 * f + col0, dg[p]);
-                store16(dgu + (row0 + p) * 2 * f + f + col0, du[p]);
+            for (int p = 0; p < 8; ++p) {
+                const bool in = row0 + p < rows;
+                dg[p] = in ? map8(gv[p], uv[p], dv[p], fg) : kZero4;
+                du[p] = in ? map8(gv[p], uv[p], dv[p], fu) : kZero4;
+                if (STORE_Y && in) {
+                    store16(dgu + (row0 + p) * 2 * f + col0, dg[p]);
+                    store16(dgu + (row0 + p) * 2 * f + f + col0, du[p]);
+                }
             }
-        }
+        };
+        if (wave_has_deep_gate(gv))
+            produce(SwigluDGate<true>{}, SwigluDUp<true>{});
+        else
+            produce(SwigluDGate<false>{}, SwigluDUp<false>{});
     }
     if constexpr (ROW || COL) {
         quant_block_body<ROW, COL, false, false>(dg, rows, 2 * f, ld_t, b.rb, b.cb, q, s, qt, st,
@@ -328,18 +380,30 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_coef_kernel(
     if (r >= rows)
         return;
     float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-    for (int64_t c = 8 * lane; c < cols; c += 512) {
-        const uint4 dv = load16(dy + r * cols + c);
-        const uint4 xv = load16(x + r * cols + c);
-        const uint4 gv = load16(gamma + c);
-        const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w};
-        const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-        const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+    // four 512-column steps per trip, their loads issued together (the sum
+    // still runs over the steps in column order)
+    for (int64_t c0 = 8 * lane; c0 < cols; c0 += 2048) {
+        uint4 dv[4], xv[4], gv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc[2 * i] = __builtin_fmaf(bf16_lo(gw[i]) * bf16_lo(dw[i]), bf16_lo(xw[i]), acc[2 * i]);
-            acc[2 * i + 1] =
-                __builtin_fmaf(bf16_hi(gw[i]) * bf16_hi(dw[i]), bf16_hi(xw[i]), acc[2 * i + 1]);
+        for (int u = 0; u < 4; ++u) {
+            const int64_t c = c0 + 512 * u;
+            const bool in = c < cols;
+            dv[u] = in ? load16(dy + r * cols + c) : kZero4;
+            xv[u] = in ? load16(x + r * cols + c) : kZero4;
+            gv[u] = in ? load16(gamma + c) : kZero4;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t dw[4] = {dv[u].x, dv[u].y, dv[u].z, dv[u].w};
+            const uint32_t xw[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
+            const uint32_t gw[4] = {gv[u].x, gv[u].y, gv[u].z, gv[u].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[2 * i] =
+                    __builtin_fmaf(bf16_lo(gw[i]) * bf16_lo(dw[i]), bf16_lo(xw[i]), acc[2 * i]);
+                acc[2 * i + 1] = __builtin_fmaf(bf16_hi(gw[i]) * bf16_hi(dw[i]), bf16_hi(xw[i]),
+                                                acc[2 * i + 1]);
+            }
         }
     }
     float sum = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
@@ -419,20 +483,32 @@ __global__ __launch_bounds__(256) void residual_rstd_kernel(const uint16_t* __re
     if (r >= rows)
         return;
     float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-    for (int64_t c = 8 * lane; c < cols; c += 512) {
-        const uint4 av = load16(a + r * cols + c);
-        const uint4 bv = load16(bb + r * cols + c);
-        const uint32_t aw[4] = {av.x, av.y, av.z, av.w};
-        const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
-        uint32_t o[4];
+    // four 512-column steps per trip, loads issued together (the sum runs
+    // over the steps in column order, as in rmsnorm_rstd_kernel)
+    for (int64_t c0 = 8 * lane; c0 < cols; c0 += 2048) {
+        uint4 av[4], bv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            o[i] = pack_bf16(bf16_lo(aw[i]) + bf16_lo(bw[i]), bf16_hi(aw[i]) + bf16_hi(bw[i]));
-            const float lo = bf16_lo(o[i]), hi = bf16_hi(o[i]);
-            acc[2 * i] = __builtin_fmaf(lo, lo, acc[2 * i]);
-            acc[2 * i + 1] = __builtin_fmaf(hi, hi, acc[2 * i + 1]);
+        for (int u = 0; u < 4; ++u) {
+            const int64_t c = c0 + 512 * u;
+            av[u] = c < cols ? load16(a + r * cols + c) : kZero4;
+            bv[u] = c < cols ? load16(bb + r * cols + c) : kZero4;
         }
-        store16(h + r * cols + c, make_uint4(o[0], o[1], o[2], o[3]));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t c = c0 + 512 * u;
+            const uint32_t aw[4] = {av[u].x, av[u].y, av[u].z, av[u].w};
+            const uint32_t bw[4] = {bv[u].x, bv[u].y, bv[u].z, bv[u].w};
+            uint32_t o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                o[i] = pack_bf16(bf16_lo(aw[i]) + bf16_lo(bw[i]), bf16_hi(aw[i]) + bf16_hi(bw[i]));
+                const float lo = bf16_lo(o[i]), hi = bf16_hi(o[i]);
+                acc[2 * i] = __builtin_fmaf(lo, lo, acc[2 * i]);
+                acc[2 * i + 1] = __builtin_fmaf(hi, hi, acc[2 * i + 1]);
+            }
+            if (c < cols)
+                store16(h + r * cols + c, make_uint4(o[0], o[1], o[2], o[3]));
+        }
     }
     float sum = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
 #pragma unroll
@@ -555,11 +631,13 @@ hipError_t launch_residual_rstd(const void* a, const void* b, int64_t rows, int6
                          cols, eps, static_cast<uint16_t*>(h), rstd);
 }
 
-hipError_t launch_probe_sigmoid(uint32_t first, int64_t n, float* out, hipStream_t stream)
+hipError_t launch_probe_sigmoid(uint32_t first, int64_t n, int form, float* out,
+                                hipStream_t stream)
 {
     const int64_t blocks = (n + 255) / 256;
     const unsigned grid = (unsigned)(blocks < 65536 ? blocks : 65536);
-    return launch_kernel(probe_sigmoid_kernel, dim3(grid), dim3(256), stream, first, n, out);
+    return launch_kernel(probe_sigmoid_kernel, dim3(grid), dim3(256), stream, first, n, form,
+                         out);
 }
 
 #undef PURO_DISPATCH_OUTPUTS

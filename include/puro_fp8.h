@@ -242,14 +242,19 @@ puro_status_t puro_fp8_probe_encode(uint32_t first_bits, int64_t n, uint8_t* out
 
 /*
  * Diagnostic: the FP32 sigmoid 1 / (1 + e^-g) that the SwiGLU producers
- * evaluate (puro_fp8_swiglu_quant, puro_fp8_swiglu_bwd_quant; below g = -64
- * they keep it scaled by 2^64, and the probe returns it scaled back), applied to the
+ * evaluate (puro_fp8_swiglu_quant, puro_fp8_swiglu_bwd_quant), applied to the
  * binary32 values whose bit patterns are first_bits, first_bits + 1, ...,
- * first_bits + n - 1 (wrapping modulo 2^32).  out: f32 [n] device buffer,
- * 4-byte aligned.  Lets a test hold the device evaluation to its error bound
- * over whole ranges of inputs.  Requires n >= 0.
+ * first_bits + n - 1 (wrapping modulo 2^32).  The producers use one of two
+ * forms per wave of 64 lanes: the plain form when every gate of the wave is
+ * >= -64, else the deep form (scaled by 2^64 below -64, so results heading
+ * for the subnormal range are not flushed; the probe returns it scaled
+ * back).  form 0: chosen per wave of 64 consecutive inputs as the producers
+ * do; 1: the plain form; 2: the deep form (PURO_ERR_BAD_ENUM otherwise).
+ * out: f32 [n] device buffer, 4-byte aligned.  Lets a test hold each form to
+ * its error bound over whole ranges of inputs.  Requires n >= 0.
  */
-puro_status_t puro_fp8_probe_sigmoid(uint32_t first_bits, int64_t n, float* out, void* stream);
+puro_status_t puro_fp8_probe_sigmoid(uint32_t first_bits, int64_t n, int form, float* out,
+                                     void* stream);
 
 /*
  * Diagnostic: one matrix-core instruction on raw per-lane operand bytes, so

@@ -154,10 +154,12 @@ def test_probe_validation(lib):
     assert lib.puro_fp8_probe_encode(0, -1, P16, None) == SHAPE
     assert lib.puro_fp8_probe_encode(0, 10, None, None) == NULLP
     assert lib.puro_fp8_probe_encode(0, 0, None, None) == OK
-    assert lib.puro_fp8_probe_sigmoid(0, -1, P16, None) == SHAPE
-    assert lib.puro_fp8_probe_sigmoid(0, 10, None, None) == NULLP
-    assert lib.puro_fp8_probe_sigmoid(0, 10, P16 + 2, None) == ALIGN
-    assert lib.puro_fp8_probe_sigmoid(0, 0, None, None) == OK
+    assert lib.puro_fp8_probe_sigmoid(0, -1, 0, P16, None) == SHAPE
+    assert lib.puro_fp8_probe_sigmoid(0, 10, 0, None, None) == NULLP
+    assert lib.puro_fp8_probe_sigmoid(0, 10, 1, P16 + 2, None) == ALIGN
+    assert lib.puro_fp8_probe_sigmoid(0, 10, 3, P16, None) == ENUM
+    assert lib.puro_fp8_probe_sigmoid(0, 10, -1, P16, None) == ENUM
+    assert lib.puro_fp8_probe_sigmoid(0, 0, 2, None, None) == OK
     assert lib.puro_fp8_probe_mfma(6, P16, P16, 0, 0, P16, None) == ENUM
     assert lib.puro_fp8_probe_mfma(-1, P16, P16, 0, 0, P16, None) == ENUM
     assert lib.puro_fp8_probe_mfma(0, None, P16, 0, 0, P16, None) == NULLP

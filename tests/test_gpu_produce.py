@@ -231,29 +231,36 @@ def test_rmsnorm_block_stack_sampled(pf):
     _assert_ok(pc.check_outputs(h, y, lo, hi, sel.numel()), "rmsnorm block_stack")
 
 
-def test_probe_sigmoid_within_its_bound(pf):
+@pytest.mark.parametrize("form", [0, 1, 2])
+def test_probe_sigmoid_within_its_bound(pf, form):
     """The FP32 sigmoid the SwiGLU producers evaluate, through
     puro_fp8_probe_sigmoid, against 1 / (1 + e^-g) in double precision on
-    3 x 64 runs of 2^18 consecutive FP32 inputs (50 M values) spread over
-    [0, 104] in both signs and packed into [-104, -80]: relative error at
-    most 5 * 2^-24 (the budget the producers' tolerance assumes) wherever the
-    result is normal, and below that (g < -87.3, a subnormal result) within
-    5 * 2^-24 of it plus half the subnormal spacing 2^-149, never flushed to
-    zero while the exact value is at least 2^-149."""
+    64 runs of 2^18 consecutive FP32 inputs per range (16.8 M values each):
+    [0, 104], [-64, 0] (both forms), and, for the deep form and the per-wave
+    choice, [-104, 0] and [-104, -80].  Relative error at most 5 * 2^-24 (the
+    budget the producers' tolerance assumes) wherever the result is normal;
+    below that (g < -87.3, a subnormal result) within 5 * 2^-24 of it plus
+    half the subnormal spacing 2^-149, and never flushed to zero while the
+    exact value is at least 2^-149.  form 0 chooses per wave as the
+    producers do, 1 is the plain form (used only when every gate of a wave
+    is >= -64), 2 the deep form."""
     import struct
     bits = lambda v: struct.unpack("<I", struct.pack("<f", v))[0]
     run = 1 << 18
     buf = torch.empty(run, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
+    ranges = [(0, 0.0, 104.0), (0x80000000, 0.0, 64.0)]
+    if form != 1:
+        ranges += [(0x80000000, 0.0, 104.0), (0x80000000, 80.0, 104.0)]
     worst = 0.0
     worst_sub = 0.0
     n_sub = 0
-    for sign, lo, hi in ((0, 0.0, 104.0), (0x80000000, 0.0, 104.0), (0x80000000, 80.0, 104.0)):
-        say("probe_sigmoid", "-" if sign else "+", lo, hi, "64 runs of", run)
+    for sign, lo, hi in ranges:
+        say("probe_sigmoid form", form, "-" if sign else "+", lo, hi, "64 runs of", run)
         b0, b1 = bits(lo), bits(hi)
         for k in range(64):
             first = (b0 + (k * (b1 - b0 - run)) // 63) | sign
-            assert pf.puro_fp8_probe_sigmoid(first, run, buf.data_ptr(), stream) == 0
+            assert pf.puro_fp8_probe_sigmoid(first, run, form, buf.data_ptr(), stream) == 0
             got = host(buf).astype(np.float64)
             g = np.arange(first, first + run, dtype=np.uint64).astype(np.uint32).view(np.float32)
             ref = 1.0 / (1.0 + np.exp(-g.astype(np.float64)))
@@ -270,7 +277,8 @@ def test_probe_sigmoid_within_its_bound(pf):
     say(f"   max relative error {worst / 2.0 ** -24:.3f} x 2^-24; {n_sub} subnormal results, "
         f"worst excess {worst_sub / 2.0 ** -149:.3f} x 2^-149")
     assert worst <= 5 * 2.0 ** -24
-    assert n_sub > 0 and worst_sub <= 2.0 ** -150
+    assert worst_sub <= 2.0 ** -150
+    assert (n_sub > 0) == (form != 1)
 
 
 # ---- RMSNorm backward plus the skip path; residual add with rstd -----------------
