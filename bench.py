@@ -888,6 +888,31 @@ def _oracle_slice(specs, host_tensors, tokens):
     return flops, time.perf_counter() - t0
 
 
+def _oracle_quantizers(specs, host_tensors, tokens=None):
+    """The oracle's quantizers over the full tensors of every layer (or their
+    first `tokens` rows), with the tilings the layer's GEMMs read: (algorithmic
+    bytes, seconds)."""
+    import oracle
+    import synth
+    byts = 0.0
+    t0 = time.perf_counter()
+    for spec, t in zip(specs, host_tensors):
+        tk = spec.tokens if tokens is None else min(tokens, spec.tokens)
+        for name, row, col in (("x", spec.fwd, spec.wgrad), ("dy", spec.dgrad, spec.wgrad)):
+            if not (row or col):
+                continue
+            b = synth.bits(t[name][:tk])
+            if row:
+                oracle.quant_rowwise(b)
+            if col:
+                oracle.quant_colwise(b)
+            byts += act_bytes(b.shape[0], b.shape[1], row, col)
+        if spec.fwd or spec.dgrad:
+            oracle.quant_weight(synth.bits(t["w"]), transpose=spec.dgrad)
+            byts += weight_bytes(spec.d_out, spec.d_in, 2 if spec.dgrad else 1)
+    return byts, time.perf_counter() - t0
+
+
 def cpu_baseline(specs, host_tensors, tokens, single_tokens=256):
     """The oracle on bounded slices of the same workload: the first `tokens`
     tokens of every layer on all the host cores this process may use (every
@@ -901,19 +926,26 @@ def cpu_baseline(specs, host_tensors, tokens, single_tokens=256):
     oracle.set_threads(threads)
     flops, dt = _oracle_slice(specs, host_tensors, tokens)
     used = oracle.get_threads()
+    qb, qt = _oracle_quantizers(specs, host_tensors)
+    quant = {"value": qb / qt / 1e9, "unit": "GB/s", "threads": used, "seconds": round(qt, 2),
+             "sample": f"the full tensors: {qb / 1e9:.2f} GB of algorithmic quantizer bytes "
+                       f"(bf16 in, codes and scales out)"}
     single = None
     if single_tokens > 0:
         oracle.set_threads(1)
         f1, d1 = _oracle_slice(specs, host_tensors, single_tokens)
+        q1b, q1t = _oracle_quantizers(specs, host_tensors, single_tokens)
         single = {"value": f1 / d1 / 1e12, "unit": "TFLOP/s", "threads": 1,
                   "seconds": round(d1, 2),
-                  "sample": f"first {single_tokens} tokens of each layer ({f1 / 1e9:.1f} GFLOP)"}
+                  "sample": f"first {single_tokens} tokens of each layer ({f1 / 1e9:.1f} GFLOP)",
+                  "quantizers_gbps": round(q1b / q1t / 1e9, 3)}
         oracle.set_threads(used)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": used,
             "kind": "oracle", "seconds": round(dt, 2),
             "host_cpu_count": host_cores, "cpu_model": _cpu_model(),
             "threads_from": "OMP_NUM_THREADS" if env else "os.cpu_count()",
             "single_thread": single,
+            "quantizers": quant,
             "sample": (f"first {tokens} tokens of each of the {len(specs)} linear layers: "
                        f"quantize the operands each GEMM reads (1x128, 128x1, 128x128) and run "
                        f"the layer's {'/'.join(_kinds(specs))} GEMMs on that slice "

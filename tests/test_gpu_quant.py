@@ -253,3 +253,30 @@ def test_quant_weight_grouped_mixed_copies(pf):
         ref = pf.quant_weight(w, transpose=True)
         for k in o:
             assert torch.equal(o[k], ref[k]), k
+
+
+def test_quant_weight_grouped_sixteen_weights(pf):
+    """The largest group (16 descriptors, ragged sizes, each combination of
+    code copies): every weight equal to its own launch, so the block search
+    over the prefix sums finds every weight's blocks."""
+    rng = np.random.default_rng(16)
+    shapes = [(128 * int(rng.integers(1, 7)), 128 * int(rng.integers(1, 7))) for _ in range(16)]
+    ws = [dev(synth.normal(sh, 0.02, i, f"grouped16/{i}").to(torch.bfloat16))
+          for i, sh in enumerate(shapes)]
+    P = lambda t: None if t is None else t.data_ptr()
+    outs = []
+    for i, (n, k) in enumerate(shapes):
+        o = {"s": torch.empty((n // 128, k // 128), dtype=torch.float32, device="cuda")}
+        if i % 3 != 1:
+            o["q"] = torch.empty((n, k), dtype=torch.uint8, device="cuda")
+        if i % 3 != 0:
+            o["qt"] = torch.empty((k, n), dtype=torch.uint8, device="cuda")
+        outs.append(o)
+    descs = (pf.WeightDesc * 16)(*[pf.WeightDesc(P(w), n, k, P(o.get("q")), P(o.get("qt")), P(o["s"]))
+                                   for w, (n, k), o in zip(ws, shapes, outs)])
+    say("quant_weight_grouped 16 weights", shapes)
+    assert pf.puro_fp8_quant_weight_grouped(descs, 16, torch.cuda.current_stream().cuda_stream) == 0
+    for w, o in zip(ws, outs):
+        ref = pf.quant_weight(w, transpose=True)
+        for key in o:
+            assert torch.equal(o[key], ref[key]), key
