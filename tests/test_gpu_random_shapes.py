@@ -3,7 +3,8 @@ and scales bit-exact against the oracle, GEMM outputs within the gates of
 tests/parity.py, in every mode -- including shapes that take the split-K path
 (K >= 2048 with fewer than 256 output tiles) and the persistent multi-unit
 walk (more than 256 tiles) -- and the quantize-on-produce kernels (SwiGLU
-forward and backward, RMSNorm) against the oracle's band.  Complements the
+forward and backward, RMSNorm forward and backward, the residual add) against
+the oracle's band.  Complements the
 hand-picked shapes of the other GPU tests with shapes nobody chose."""
 from __future__ import annotations
 
@@ -148,6 +149,55 @@ PRODUCE_CASES = [("swiglu_bwd" if i % 2 else "swiglu", int(_RNG.integers(1, 2500
                   128 * int(_RNG.integers(1, 13)), i % 4 < 2) for i in range(6)]
 RMSNORM_CASES = [(int(_RNG.integers(1, 2500)), 128 * int(_RNG.integers(1, 65)),
                   (0.0, 1e-6, 1e-5)[int(_RNG.integers(0, 3))]) for _ in range(3)]
+
+
+NORM_BWD_CASES = [(int(_RNG.integers(1, 2500)), 128 * int(_RNG.integers(1, 33)),
+                   bool(_RNG.integers(0, 2))) for _ in range(4)] + [(1, 128, True)]
+RESIDUAL_CASES = [(int(_RNG.integers(1, 2500)), 128 * int(_RNG.integers(1, 33))) for _ in range(3)] + [(1, 256)]
+
+
+@pytest.mark.parametrize("rows,cols,skip", NORM_BWD_CASES)
+def test_rmsnorm_bwd_random(pf, rows, cols, skip):
+    """Random ragged RMSNorm-backward shapes (with and without the skip-path
+    gradient) against the oracle's band."""
+    import oracle
+    import produce_check as pc
+    import synth
+    from parity import dev
+    from test_gpu_produce import _assert_ok, _host_outputs, _tol_bwd
+    say("rmsnorm_bwd random", rows, cols, skip)
+    d = synth.rmsnorm_bwd_inputs(rows, cols, seed=rows + cols)
+    rstd = torch.from_numpy(oracle.rmsnorm_fwd(synth.bits(d["x"]), synth.bits(d["gamma"]), 1e-6,
+                                               2.0 ** -18)[3].astype(np.float32))
+    gin = d["gin"] if skip else None
+    out = pf.rmsnorm_bwd_quant(dev(d["dy"]), dev(d["x"]), dev(d["gamma"]), dev(rstd),
+                               None if gin is None else dev(gin), row=True, col=True,
+                               bf16_out=True)
+    y, lo, hi = oracle.rmsnorm_bwd(synth.bits(d["dy"]), synth.bits(d["x"]), synth.bits(d["gamma"]),
+                                   rstd.numpy(), None if gin is None else synth.bits(gin),
+                                   _tol_bwd(cols))
+    _assert_ok(pc.check_outputs(_host_outputs(out), y, lo, hi, rows), f"rmsnorm_bwd {rows}x{cols}")
+
+
+@pytest.mark.parametrize("rows,cols", RESIDUAL_CASES)
+def test_residual_add_then_norm_random(pf, rows, cols):
+    """Random ragged residual add + one-pass norm: h bit-exact, rstd within
+    TOL, the norm's outputs within the oracle's band."""
+    import oracle
+    import produce_check as pc
+    import synth
+    from parity import bf16_host_bits, dev, host
+    from test_gpu_produce import TOL, _assert_ok, _host_outputs
+    say("residual + norm random", rows, cols)
+    d = synth.residual_inputs(rows, cols, seed=rows + cols)
+    r = pf.residual_add_rstd(dev(d["a"]), dev(d["b"]), eps=1e-6)
+    h = oracle.residual_add(synth.bits(d["a"]), synth.bits(d["b"]))
+    assert np.array_equal(bf16_host_bits(r["h"]), h)
+    y, lo, hi, rstd = oracle.rmsnorm_fwd(h, synth.bits(d["gamma"]), float(np.float32(1e-6)), TOL)
+    assert np.max(np.abs(host(r["rstd"]).astype(np.float64) - rstd) / rstd) <= TOL
+    out = pf.rmsnorm_quant_rstd(r["h"], dev(d["gamma"]), r["rstd"], row=True, col=True,
+                                bf16_out=True)
+    _assert_ok(pc.check_outputs(_host_outputs(out), y, lo, hi, rows), f"residual {rows}x{cols}")
 
 
 @pytest.mark.parametrize("op,rows,f,wide", PRODUCE_CASES)
