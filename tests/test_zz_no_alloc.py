@@ -12,7 +12,9 @@ import torch
 from parity import say
 
 pytestmark = pytest.mark.gpu
-FWD, DGRAD, WGRAD = 0, 1, 2
+FWD, DGRAD, WGRAD, DGRAD_W, FWD_T = 0, 1, 2, 3, 4
+B_KN = (DGRAD_W, FWD_T)          # b stored [K][N]
+NAMES = ["fwd", "dgrad", "wgrad", "dgrad_w", "fwd_t"]
 WORKSPACE = 5
 
 
@@ -30,15 +32,16 @@ def _operands(mode, M, N, K, seed):
         q = torch.randint(0, 0xFF, (r, c), dtype=torch.uint8, device="cuda:0", generator=g)
         return torch.where((q & 0x7F) == 0x7F, q - 1, q)          # no NaN codes
 
-    sb_shape = {FWD: (N // 128, K // 128), DGRAD: (K // 128, N // 128), WGRAD: (K // 128, N)}[mode]
+    sb_shape = {FWD: (N // 128, K // 128), DGRAD: (K // 128, N // 128), WGRAD: (K // 128, N),
+                DGRAD_W: (K // 128, N // 128), FWD_T: (N // 128, K // 128)}[mode]
     sa = torch.rand((K // 128, M), device="cuda:0", generator=g) + 0.25
     sb = torch.rand(sb_shape, device="cuda:0", generator=g) + 0.25
-    return codes(M, K), sa, codes(N, K), sb
+    return codes(M, K), sa, (codes(K, N) if mode in B_KN else codes(N, K)), sb
 
 
 def _noalloc(pf, mode, a, sa, b, sb, out, accumulate):
     M, K = a.shape
-    N = b.shape[0]
+    N = b.shape[1] if mode in B_KN else b.shape[0]
     c_dtype = pf.OUT_FP32 if out.dtype == torch.float32 else pf.OUT_BF16
     return pf.puro_fp8_gemm_blockscaled_noalloc(
         mode, M, N, K, a.data_ptr(), sa.data_ptr(), b.data_ptr(), sb.data_ptr(), out.data_ptr(),
@@ -52,11 +55,13 @@ def _noalloc(pf, mode, a, sa, b, sb, out, accumulate):
     # no split, then a split one with bf16 output, then a smaller split one
     [(FWD, 1000, 768, 512, torch.bfloat16, False), (FWD, 256, 2048, 4096, torch.bfloat16, False),
      (DGRAD, 129, 256, 2048, torch.float32, False)],
+    # the modes that read the weight codes as [K][N]: split-K, then smaller
+    [(DGRAD_W, 300, 512, 4096, torch.bfloat16, False), (FWD_T, 200, 384, 2048, torch.float32, False)],
 ])
 def test_noalloc_matches_workspace_entry_point(pf, cases):
     for i, (mode, M, N, K, dt, acc) in enumerate(cases):
         ws_need = pf.puro_fp8_gemm_workspace_bytes(mode, M, N, K)
-        say("noalloc", ["fwd", "dgrad", "wgrad"][mode], M, N, K, dt, "acc" if acc else "",
+        say("noalloc", NAMES[mode], M, N, K, dt, "acc" if acc else "",
             f"workspace {ws_need} B")
         assert ws_need <= pf.PURO_FP8_NOALLOC_SCRATCH_BYTES
         a, sa, b, sb = _operands(mode, M, N, K, 100 + i)
