@@ -345,7 +345,8 @@ puro_status_t puro_fp8_rmsnorm_quant(const void* x, const void* gamma, int64_t r
  * RMSNorm forward with the row statistic handed over: as
  * puro_fp8_rmsnorm_quant, but rstd f32 [rows] is an INPUT (as
  * puro_bf16_residual_add_rstd writes it for the norm's input), so the call is one
- * pass over x: the normalize-and-quantize kernel alone.
+ * pass over x: the normalize-and-quantize kernel alone.  Arguments, layouts
+ * and errors as for puro_fp8_rmsnorm_quant (no eps: it is in rstd).
  */
 puro_status_t puro_fp8_rmsnorm_quant_rstd(const void* x, const void* gamma, const float* rstd,
                                           int64_t rows, int64_t cols, uint8_t* q, float* s,
@@ -383,7 +384,9 @@ puro_status_t puro_fp8_rmsnorm_bwd_quant(const void* dy, const void* x, const vo
  * values, rounded to nearest even) and rstd f32 [rows] =
  * 1 / sqrt(mean over the row of h^2 + eps), for puro_fp8_rmsnorm_quant_rstd.
  * a, b, h bf16 [rows][cols]; cols a positive multiple of 128; eps finite and
- * >= 0 (PURO_ERR_BAD_VALUE otherwise).
+ * >= 0 (PURO_ERR_BAD_VALUE otherwise).  Every pointer is required
+ * (PURO_ERR_NULL_POINTER) and 16-byte aligned (PURO_ERR_MISALIGNED); rows = 0
+ * enqueues nothing.  The caller owns all buffers; h must not alias a or b.
  */
 puro_status_t puro_bf16_residual_add_rstd(const void* a, const void* b, int64_t rows, int64_t cols,
                                      float eps, void* h, float* rstd, void* stream);
