@@ -124,7 +124,7 @@ LAYOUTS = {
 def parse_args():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="block_stack",
                    help="a workload by name: " + ", ".join(f"{k} ({v})" for k, v in CONFIGS.items()))
