@@ -74,8 +74,18 @@ if ROOT not in sys.path:
 METRIC = "FP8 block-scaled GEMM TFLOP/s (fwd+dgrad+wgrad) and % of MI355X FP8 peak"
 FP8_PEAK_TFLOPS = 5000.0          # MI355X dense FP8 MFMA, published
 HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E, published
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_block_stack.json")
-MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_block_stack.json")
+# counter files, one pair per workload (the dispatch averages they hold are
+# per kernel over that workload's launches)
+def traffic_file(workload="block_stack"):
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+
+
+def mfma_file(workload="block_stack"):
+    return os.path.join(ROOT, "profiles", f"mfma_{workload}.json")
+
+
+TRAFFIC_FILE = traffic_file()
+MFMA_FILE = mfma_file()
 _CSRC = os.path.join(ROOT, "fp8_block_scaled_tile_amd", "csrc")
 # the sources each profiled kernel is compiled from (its file and the headers it includes)
 GEMM_SOURCES = [os.path.join(_CSRC, n) for n in ("gemm.hip", "device_common.hpp")]
@@ -570,7 +580,7 @@ def _read_pmc_csv(path):
     return out
 
 
-def ingest_pmc(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+def ingest_pmc(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, path=None):
     """Write the traffic file: per kernel, FETCH_SIZE and WRITE_SIZE (KiB per
     dispatch) scaled by the factor a plain copy of known size reads on the
     same counters (bytes expected / bytes counted)."""
@@ -601,12 +611,13 @@ def ingest_pmc(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     doc = {"copy_factor_fetch": ff, "copy_factor_write": fw,
            "gemm_source_sha": sha(GEMM_SOURCES), "quant_source_sha": sha(QUANT_SOURCES),
            "kernels": kernels}
-    with open(TRAFFIC_FILE, "w") as f:
+    path = path or TRAFFIC_FILE
+    with open(path, "w") as f:
         json.dump(doc, f, indent=1, sort_keys=True)
-    print(f"wrote {TRAFFIC_FILE}: {len(kernels)} kernels")
+    print(f"wrote {path}: {len(kernels)} kernels")
 
 
-def ingest_mfma(csv_path):
+def ingest_mfma(csv_path, path=None):
     """Write the matrix-core file from one rocprofv3 pass with the derived
     MfmaUtil (busy cycles of the MFMA units over GPU-active cycles x SIMDs)
     and SQ_INSTS_VALU_MFMA_MOPS_F8 (FP8 multiply-add operations / 512): per
@@ -632,9 +643,10 @@ def ingest_mfma(csv_path):
                   "f8_flop_per_dispatch": k["f8_flop"] / k["dispatches"]}
            for name, k in kernels.items()}
     doc = {"gemm_source_sha": sha(GEMM_SOURCES), "quant_source_sha": sha(QUANT_SOURCES), "kernels": out}
-    with open(MFMA_FILE, "w") as f:
+    path = path or MFMA_FILE
+    with open(path, "w") as f:
         json.dump(doc, f, indent=1, sort_keys=True)
-    print(f"wrote {MFMA_FILE}: {len(out)} kernels")
+    print(f"wrote {path}: {len(out)} kernels")
 
 
 def _profile_entry(path, symbol_prefix):
@@ -655,16 +667,18 @@ def _profile_entry(path, symbol_prefix):
     return None
 
 
-def mfma_busy_for(symbol_prefix):
-    """Duration-weighted MfmaUtil (%) of a kernel from the counter file, or None."""
-    v = _profile_entry(MFMA_FILE, symbol_prefix)
+def mfma_busy_for(symbol_prefix, workload="block_stack"):
+    """Duration-weighted MfmaUtil (%) of a kernel from the workload's counter
+    file, or None."""
+    v = _profile_entry(mfma_file(workload), symbol_prefix)
     return round(v["mfma_util_pct"], 2) if v else None
 
 
-def traffic_for(symbol_prefix):
-    """HBM bytes per dispatch for a kernel, or None if the counters are absent
-    or were taken on a different version of the kernel code."""
-    v = _profile_entry(TRAFFIC_FILE, symbol_prefix)
+def traffic_for(symbol_prefix, workload="block_stack"):
+    """HBM bytes per dispatch for a kernel in the workload, or None if the
+    counters are absent or were taken on a different version of the kernel
+    code."""
+    v = _profile_entry(traffic_file(workload), symbol_prefix)
     return v["hbm_bytes_per_dispatch"] if v else None
 
 
@@ -973,11 +987,12 @@ def copy_calibration():
 
 def main():
     args = parse_args()
+    wl_name = CONFIGS[args.config] if args.config else args.workload
     if args.ingest_pmc:
-        ingest_pmc(*args.ingest_pmc)
+        ingest_pmc(*args.ingest_pmc, path=traffic_file(wl_name))
         return 0
     if args.ingest_mfma:
-        ingest_mfma(args.ingest_mfma)
+        ingest_mfma(args.ingest_mfma, path=mfma_file(wl_name))
         return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: the FP8 linear-layer path is measured on a single "
@@ -1082,12 +1097,12 @@ def main():
     timed = {name: describe(name, d) for name, d in per_class(timed_events).items()}
     dom = max(timed, key=lambda k: timed[k]["ms_per_step"])
     dk = timed[dom]
-    # the counter files hold the block_stack workload's per-dispatch figures
-    traffic = traffic_for(dk["symbol"]) if headline else None
+    # each workload's counter files hold its own per-dispatch figures
+    traffic = traffic_for(dk["symbol"], wl.name)
     roofline = {"bound": "mfma", "achieved": dk["tflops"], "peak": FP8_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(dk["tflops"] / FP8_PEAK_TFLOPS, 4),
                 "traffic": traffic,
-                "mfma_busy_pct": mfma_busy_for(dk["symbol"]) if headline else None,
+                "mfma_busy_pct": mfma_busy_for(dk["symbol"], wl.name),
                 "kernel": dk["symbol"], "launch_class": dom,
                 "algorithmic_gflop_per_launch": dk["avg_gflop"], "avg_ms": dk["avg_ms"],
                 "timed_in": "the timed region"}

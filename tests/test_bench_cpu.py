@@ -131,6 +131,12 @@ def test_step_calls_grouped_weights():
     assert [c[1] for c in one][1] == "quant_weight"
 
 
+def test_counter_files_are_per_workload():
+    assert bench.traffic_file() == bench.TRAFFIC_FILE
+    assert bench.traffic_file("qkv_fwd").endswith("profiles/traffic_qkv_fwd.json")
+    assert bench.mfma_file("down_bwd").endswith("profiles/mfma_down_bwd.json")
+
+
 def test_configs_name_the_workloads():
     import synth
     assert bench.CONFIGS["c5"] == "block_stack"
@@ -150,6 +156,7 @@ def test_ingest_mfma_weights_by_duration_and_gates_on_code(tmp_path, monkeypatch
     csv_path = tmp_path / "c.csv"
     csv_path.write_text(head + "".join(f'{d},"{name}",{c},{v},{a},{b}\n' for d, c, v, a, b in rows))
     monkeypatch.setattr(bench, "MFMA_FILE", str(tmp_path / "m.json"))
+    monkeypatch.setattr(bench, "mfma_file", lambda workload="block_stack": str(tmp_path / "m.json"))
     bench.ingest_mfma(str(csv_path))
     assert bench.mfma_busy_for("void puro::gemm_bs_kernel<0, 0>") == 55.0
     entry = bench._profile_entry(bench.MFMA_FILE, "void puro::gemm_bs_kernel<0, 0>")
@@ -181,6 +188,7 @@ def test_ingest_pmc_scales_by_the_copy_calibration(tmp_path, monkeypatch):
     copy_f = csv("cf.csv", [(neg, 524288.0)])          # half of 1 GiB counted -> factor 2
     copy_w = csv("cw.csv", [(neg, 1048576.0)])         # all of it -> factor 1
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "t.json"))
+    monkeypatch.setattr(bench, "traffic_file", lambda workload="block_stack": str(tmp_path / "t.json"))
     bench.ingest_pmc(fetch, write, copy_f, copy_w)
     import json
     doc = json.load(open(bench.TRAFFIC_FILE))
