@@ -623,8 +623,11 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
                         const uint32_t y1 = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(odd ? a1 : b1), 0x401F);
                         const v4u w = odd ? v4u{y0, y1, b0, b1} : v4u{a0, a1, y0, y1};
                         const size_t col = odd ? idx + 16 * tb - 4 : idx + 16 * ta;
-                        __builtin_nontemporal_store(
-                            w, reinterpret_cast<v4u*>(static_cast<uint16_t*>(C) + col));
+                        // Ordinary stores: measured on the MI355X, non-temporal
+                        // ones made this layout's L2 write 1.4x the output's
+                        // bytes back to memory and ran 2-3% slower; these write
+                        // 1.015x.
+                        *reinterpret_cast<v4u*>(static_cast<uint16_t*>(C) + col) = w;
                     }
                 } else {
 #pragma unroll
@@ -652,8 +655,9 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bs_kernel(
                         w[2 * tn + 1] = pack_bf16(acc[sm][tn][2], acc[sm][tn][3]);
                     }
                     // Non-temporal: the output is not read again by this
-                    // kernel, and streaming it keeps the cached A / B panels
-                    // that other work-groups re-read.
+                    // kernel.  Measured on the MI355X against ordinary stores:
+                    // 2% faster on a 16384 x 16384 output, equal on narrower
+                    // ones, at a cost of 7-18% more bytes written back.
                     v4u* dst = reinterpret_cast<v4u*>(static_cast<uint16_t*>(C) + idx);
                     __builtin_nontemporal_store(v4u{w[0], w[1], w[2], w[3]}, dst);
                     __builtin_nontemporal_store(v4u{w[4], w[5], w[6], w[7]}, dst + 4);
