@@ -74,6 +74,7 @@ if ROOT not in sys.path:
 METRIC = "FP8 block-scaled GEMM TFLOP/s (fwd+dgrad+wgrad) and % of MI355X FP8 peak"
 FP8_PEAK_TFLOPS = 5000.0          # MI355X dense FP8 MFMA, published
 HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E, published
+PEAK_SCLK_GHZ = 2.4               # the engine clock the published peaks assume
 # counter files, one pair per workload (the dispatch averages they hold are
 # per kernel over that workload's launches)
 def traffic_file(workload="block_stack"):
@@ -611,7 +612,7 @@ def ingest_pmc(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, path=None):
     doc = {"copy_factor_fetch": ff, "copy_factor_write": fw,
            "gemm_source_sha": sha(GEMM_SOURCES), "quant_source_sha": sha(QUANT_SOURCES),
            "kernels": kernels}
-    path = path or TRAFFIC_FILE
+    path = path or traffic_file()
     with open(path, "w") as f:
         json.dump(doc, f, indent=1, sort_keys=True)
     print(f"wrote {path}: {len(kernels)} kernels")
@@ -629,21 +630,39 @@ def ingest_mfma(csv_path, path=None):
             d = per.setdefault(row["Dispatch_Id"], {"name": row["Kernel_Name"],
                                                     "ns": int(row["End_Timestamp"]) - int(row["Start_Timestamp"])})
             d[row["Counter_Name"]] = float(row["Counter_Value"])
+    # GRBM_GUI_ACTIVE is summed over the XCDs (accelerator complexes): the
+    # profiler's agent table beside the counter file gives their number
+    agent_csv = csv_path.replace("counter_collection", "agent_info")
+    n_xcc = None
+    if agent_csv != csv_path and os.path.exists(agent_csv):
+        with open(agent_csv) as f:
+            for row in csv.DictReader(f):
+                if row.get("Name", "").startswith("gfx") and row.get("Num_Xcc"):
+                    n_xcc = int(row["Num_Xcc"])
     kernels = {}
     for d in per.values():
         if "MfmaUtil" not in d:
             continue
-        k = kernels.setdefault(d["name"], {"dispatches": 0, "ns": 0, "util_ns": 0.0, "f8_flop": 0.0})
+        k = kernels.setdefault(d["name"], {"dispatches": 0, "ns": 0, "util_ns": 0.0, "f8_flop": 0.0,
+                                           "gui": 0.0})
         k["dispatches"] += 1
         k["ns"] += d["ns"]
         k["util_ns"] += d["MfmaUtil"] * d["ns"]
         k["f8_flop"] += d.get("SQ_INSTS_VALU_MFMA_MOPS_F8", 0.0) * 512.0
+        k["gui"] += d.get("GRBM_GUI_ACTIVE", 0.0)
     out = {name: {"dispatches": k["dispatches"],
                   "mfma_util_pct": k["util_ns"] / k["ns"] if k["ns"] else 0.0,
-                  "f8_flop_per_dispatch": k["f8_flop"] / k["dispatches"]}
+                  "f8_flop_per_dispatch": k["f8_flop"] / k["dispatches"],
+                  # GPU-active cycles per XCD over the dispatches' wall time.
+                  # The counter window is a little wider than the dispatch's
+                  # timestamps (short memory-bound kernels read well above
+                  # 2.4 GHz), so only dispatches of 100 us or more on average
+                  # carry a clock.
+                  "sclk_ghz": (k["gui"] / n_xcc / k["ns"])
+                  if (n_xcc and k["gui"] and k["ns"] >= 100e3 * k["dispatches"]) else None}
            for name, k in kernels.items()}
     doc = {"gemm_source_sha": sha(GEMM_SOURCES), "quant_source_sha": sha(QUANT_SOURCES), "kernels": out}
-    path = path or MFMA_FILE
+    path = path or mfma_file()
     with open(path, "w") as f:
         json.dump(doc, f, indent=1, sort_keys=True)
     print(f"wrote {path}: {len(out)} kernels")
@@ -672,6 +691,13 @@ def mfma_busy_for(symbol_prefix, workload="block_stack"):
     file, or None."""
     v = _profile_entry(mfma_file(workload), symbol_prefix)
     return round(v["mfma_util_pct"], 2) if v else None
+
+
+def sclk_for(symbol_prefix, workload="block_stack"):
+    """The clock (GHz) a kernel ran at in the workload's matrix-core pass, or
+    None."""
+    v = _profile_entry(mfma_file(workload), symbol_prefix)
+    return round(v["sclk_ghz"], 3) if v and v.get("sclk_ghz") else None
 
 
 def traffic_for(symbol_prefix, workload="block_stack"):
@@ -1099,10 +1125,16 @@ def main():
     dk = timed[dom]
     # each workload's counter files hold its own per-dispatch figures
     traffic = traffic_for(dk["symbol"], wl.name)
+    # the published peak assumes 2.4 GHz; the matrix-core pass measures the
+    # clock the kernel actually ran at
+    sclk = sclk_for(dk["symbol"], wl.name)
+    peak_sclk = round(FP8_PEAK_TFLOPS * sclk / PEAK_SCLK_GHZ, 1) if sclk else None
     roofline = {"bound": "mfma", "achieved": dk["tflops"], "peak": FP8_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(dk["tflops"] / FP8_PEAK_TFLOPS, 4),
                 "traffic": traffic,
                 "mfma_busy_pct": mfma_busy_for(dk["symbol"], wl.name),
+                "sclk_ghz": sclk, "peak_at_sclk": peak_sclk,
+                "frac_at_sclk": round(dk["tflops"] / peak_sclk, 4) if peak_sclk else None,
                 "kernel": dk["symbol"], "launch_class": dom,
                 "algorithmic_gflop_per_launch": dk["avg_gflop"], "avg_ms": dk["avg_ms"],
                 "timed_in": "the timed region"}

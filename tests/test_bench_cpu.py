@@ -5,7 +5,19 @@ from __future__ import annotations
 import sys
 import types
 
+import pytest
+
 import bench
+
+
+@pytest.fixture(autouse=True)
+def _counter_files_in_tmp(tmp_path, monkeypatch):
+    """Every test here reads and writes counter files under its own temporary
+    directory, never the committed ones."""
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", bench.traffic_file())
+    monkeypatch.setattr(bench, "MFMA_FILE", bench.mfma_file())
 
 
 class _Buf:
@@ -168,6 +180,27 @@ def test_ingest_mfma_weights_by_duration_and_gates_on_code(tmp_path, monkeypatch
     assert bench.mfma_busy_for("void puro::gemm_bs_kernel<0, 0>") == 55.0
     src.write_text(open(str(src)).read() + "int changed_code;\n")
     assert bench.mfma_busy_for("void puro::gemm_bs_kernel<0, 0>") is None
+
+
+def test_ingest_mfma_clock_from_gpu_active_cycles(tmp_path, monkeypatch):
+    """The clock of a kernel: GRBM_GUI_ACTIVE (summed over the XCDs the agent
+    table names) per XCD over the dispatches' duration; none for kernels of
+    under 100 us on average, or without the agent table."""
+    head = "Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value,Start_Timestamp,End_Timestamp\n"
+    long_k = "void puro::gemm_bs_kernel<0, 0>(int)"
+    short_k = "void puro::quant_block_kernel<true, true, false, false>(int)"
+    rows = []
+    for d, (name, ns) in enumerate([(long_k, 200_000), (long_k, 400_000), (short_k, 20_000)], 1):
+        rows += [(d, name, "MfmaUtil", 10.0, ns), (d, name, "GRBM_GUI_ACTIVE", 8 * 2.0 * ns, ns)]
+    pc = tmp_path / "bench_counter_collection.csv"
+    pc.write_text(head + "".join(f'{d},"{n}",{c},{v},0,{ns}\n' for d, n, c, v, ns in rows))
+    monkeypatch.setattr(bench, "mfma_file", lambda workload="block_stack": str(tmp_path / "m.json"))
+    bench.ingest_mfma(str(pc))
+    assert bench.sclk_for(long_k.split("(")[0]) is None          # no agent table: no XCD count
+    (tmp_path / "bench_agent_info.csv").write_text("Name,Num_Xcc\ngfx950,8\n")
+    bench.ingest_mfma(str(pc))
+    assert bench.sclk_for(long_k.split("(")[0]) == 2.0
+    assert bench.sclk_for(short_k.split("(")[0]) is None
 
 
 def test_ingest_pmc_scales_by_the_copy_calibration(tmp_path, monkeypatch):
