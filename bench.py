@@ -90,7 +90,8 @@ MFMA_FILE = mfma_file()
 _CSRC = os.path.join(ROOT, "fp8_block_scaled_tile_amd", "csrc")
 # the sources each profiled kernel is compiled from (its file and the headers it includes)
 GEMM_SOURCES = [os.path.join(_CSRC, n) for n in ("gemm.hip", "device_common.hpp")]
-QUANT_SOURCES = [os.path.join(_CSRC, n) for n in ("quant.hip", "quant_block.hpp", "device_common.hpp")]
+QUANT_SOURCES = [os.path.join(_CSRC, n) for n in ("quant.hip", "quant_block.hpp", "block_walk.hpp",
+                                                 "device_common.hpp")]
 
 # the workloads by number: the tiny forward, QKV forward, up+gate forward,
 # down-projection backward, and the linear stack of one block (the headline)

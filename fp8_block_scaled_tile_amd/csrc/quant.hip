@@ -11,11 +11,11 @@ template <bool ROW, bool COL, bool WEIGHT, bool WT>
 __global__ __launch_bounds__(256) void quant_block_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_t,
     uint8_t* __restrict__ q, float* __restrict__ s, uint8_t* __restrict__ qt,
-    float* __restrict__ st, int group_rows)
+    float* __restrict__ st, BlockWalk walk)
 {
     __shared__ QuantLds<ROW, COL, WEIGHT, WT> lds;
     const int t = threadIdx.x;
-    const BlockRC b = block_of(blockIdx.x, (WEIGHT ? rows : ld_t) / 128, cols / 128, group_rows);
+    const BlockRC b = block_of(blockIdx.x, (WEIGHT ? rows : ld_t) / 128, cols / 128, walk);
     const int64_t row0 = b.rb * 128 + 8 * (t >> 4);
     const int64_t col0 = b.cb * 128 + 8 * (t & 15);
 
@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void quant_weight_grouped_kernel(const WeightJ
     while (i + 1 < jobs.count && bid >= jobs.first[i + 1])
         ++i;
     const WeightJob J = jobs.j[i];
-    const BlockRC b = block_of(bid - jobs.first[i], J.n / 128, J.k / 128, jobs.group_rows);
+    const BlockRC b = block_of(bid - jobs.first[i], J.n / 128, J.k / 128, grouped_walk(jobs.group_rows));
     const int64_t row0 = b.rb * 128 + 8 * (t >> 4);
     const int64_t col0 = b.cb * 128 + 8 * (t & 15);
     uint4 v[8];
@@ -94,7 +94,7 @@ hipError_t launch_quant_act(const void* x, int64_t rows, int64_t cols, uint8_t* 
     const dim3 grid((unsigned)((rows_pad / 128) * (cols / 128)));
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     const bool row = q != nullptr, col = qt != nullptr;
-    const int gr = quant_group_rows(false, cols);
+    const BlockWalk gr = act_walk(quant_group_rows(false, cols), rows_pad / 128, cols / 128);
     if (row && col)
         return launch_kernel(quant_block_kernel<true, true, false, false>, grid, dim3(256), stream,
                              xb, rows, cols, rows_pad, q, s, qt, st, gr);
@@ -110,7 +110,7 @@ hipError_t launch_quant_weight(const void* w, int64_t n, int64_t k, uint8_t* q, 
 {
     const dim3 grid((unsigned)((n / 128) * (k / 128)));
     const uint16_t* wb = static_cast<const uint16_t*>(w);
-    const int gr = quant_group_rows(true, k);
+    const BlockWalk gr = grouped_walk(quant_group_rows(true, k));
     if (qt)
         return launch_kernel(quant_block_kernel<false, false, true, true>, grid, dim3(256), stream,
                              wb, n, k, n, q, s, qt, nullptr, gr);

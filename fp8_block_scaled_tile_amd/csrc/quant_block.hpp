@@ -20,38 +20,10 @@
 // stores.
 #pragma once
 
+#include "block_walk.hpp"
 #include "device_common.hpp"
 
 namespace puro {
-
-// Block order: the grid is 1-D and walks the 128x128 blocks in groups of
-// `group_rows` block rows, column block by column block inside a group, so
-// the work-groups in flight at any moment read a few contiguous row bands
-// and write contiguous runs of the transposed copy (a plain row-major or
-// column-major walk concentrates the reads or the transposed writes on a
-// few HBM channels when rows are 8 KB or more apart).  The group height is
-// chosen per shape by the launch code (measured on MI355X).
-inline int quant_group_rows(bool weight, int64_t cols)
-{
-    if (weight)
-        return 4;
-    return cols <= 2048 ? 16 : 8;
-}
-
-// Block (rb, cb) taken by work-group `bid` in the grouped walk above.
-struct BlockRC {
-    int64_t rb, cb;
-};
-
-__device__ __forceinline__ BlockRC block_of(int64_t bid, int64_t nrb, int64_t ncb, int group_rows)
-{
-    const int64_t per_group = (int64_t)group_rows * ncb;
-    const int64_t group = bid / per_group;
-    const int64_t j = bid - group * per_group;
-    const int64_t gr = min((int64_t)group_rows, nrb - group * group_rows);
-    const int64_t cb = j / gr;
-    return BlockRC{group * group_rows + (j - cb * gr), cb};
-}
 
 template <bool ROW, bool COL, bool WEIGHT, bool WT>
 struct QuantLds {
