@@ -129,7 +129,8 @@ def test_swiglu_bwd_wide_gate(pf):
 
 # ---- SwiGLU backward -----------------------------------------------------------
 
-@pytest.mark.parametrize("rows,f", [(130, 128), (256, 256), (700, 384)])
+# (1000, 4096): the XCD-tiled block walk (32 block columns, 8 block rows)
+@pytest.mark.parametrize("rows,f", [(130, 128), (256, 256), (700, 384), (1000, 4096)])
 def test_swiglu_bwd_parity(pf, rows, f):
     say("swiglu_bwd_quant", rows, f)
     d = synth.swiglu_inputs(rows, f, seed=3 * rows + f)
@@ -150,8 +151,10 @@ def test_swiglu_bwd_single_orientation(pf, row, col):
 
 # ---- RMSNorm forward -------------------------------------------------------------
 
+# (1000, 4096) and (500, 8192) take the XCD-tiled block walk
 @pytest.mark.parametrize("rows,cols,eps", [(77, 128, 1e-6), (256, 2048, 1e-5),
-                                           (130, 8192, 0.0), (1000, 384, 1e-6)])
+                                           (130, 8192, 0.0), (1000, 384, 1e-6),
+                                           (1000, 4096, 1e-6), (500, 8192, 1e-5)])
 def test_rmsnorm_parity(pf, rows, cols, eps):
     say("rmsnorm_quant", rows, cols, eps)
     d = synth.rmsnorm_inputs(rows, cols, seed=rows + cols)
@@ -290,7 +293,8 @@ def _tol_bwd(cols):
 
 
 @pytest.mark.parametrize("rows,cols,skip", [(77, 128, True), (256, 2048, True),
-                                            (130, 8192, False), (1000, 384, True)])
+                                            (130, 8192, False), (1000, 384, True),
+                                            (1000, 4096, True)])
 def test_rmsnorm_bwd_parity(pf, rows, cols, skip):
     say("rmsnorm_bwd_quant", rows, cols, skip)
     d = synth.rmsnorm_bwd_inputs(rows, cols, seed=rows + cols)
@@ -343,7 +347,7 @@ def test_rmsnorm_bwd_block_stack_sampled(pf):
     _assert_ok(pc.check_outputs(h, y, lo, hi, sel.numel()), "rmsnorm_bwd block_stack")
 
 
-@pytest.mark.parametrize("rows,cols", [(77, 128), (1000, 2048), (130, 8192)])
+@pytest.mark.parametrize("rows,cols", [(77, 128), (1000, 2048), (130, 8192), (500, 8192)])
 def test_residual_add_rstd_then_one_pass_norm(pf, rows, cols):
     """h = a + b bit for bit against the oracle, rstd within TOL of the
     oracle's statistic of h, and the one-pass norm from that rstd equals the

@@ -62,7 +62,13 @@ def test_probe_encode_exhaustive_below_464(pf):
 @pytest.mark.parametrize("rows,cols", [(1, 128), (37, 256), (128, 128), (129, 384),
                                        (300, 512), (1000, 1024), (4096, 2048),
                                        # block rows in groups of 8: 8 + 3, and 8 + 8 + 1
-                                       (1300, 640), (2100, 1152)])
+                                       (1300, 640), (2100, 1152),
+                                       # the XCD-tiled walk: 4x4 tiles stacked 2 high
+                                       # (32-63 block columns) and 1 high (64+), ragged
+                                       # last block row; 1100 x 6144 falls back to the
+                                       # grouped walk (9 block rows)
+                                       (1000, 4096), (1024, 6144), (1000, 8192),
+                                       (3000, 12288), (1100, 6144)])
 @pytest.mark.parametrize("mode", ["row", "col", "dual"])
 def test_quant_act_small(pf, rows, cols, mode):
     x = random_bf16((rows, cols), seed=rows * 7 + cols, stream=f"act/{rows}x{cols}")
