@@ -81,6 +81,25 @@ def test_quant_act_random(pf, rows, cols, mode):
     _check_act(pf, x, row=mode in ("row", "dual"), col=mode in ("col", "dual"), tag="random")
 
 
+# shapes the launcher sends down the XCD-tiled block walk: 4x4-block tiles per
+# XCD, stacked 2 high (32-63 block columns, a multiple of 16) or 1 high (64+,
+# a multiple of 32), with a whole number of super tiles of block rows and a
+# ragged last block row
+_XRNG = np.random.default_rng(4096)
+XCD_ACT_CASES = []
+for _ in range(8):
+    ncb = int(_XRNG.choice([32, 48, 64, 96, 128, 160]))
+    nrb = (4 if ncb >= 64 else 8) * int(_XRNG.integers(1, 4))
+    XCD_ACT_CASES.append((128 * nrb - int(_XRNG.integers(0, 128)), 128 * ncb,
+                          ("row", "col", "dual")[int(_XRNG.integers(0, 3))]))
+
+
+@pytest.mark.parametrize("rows,cols,mode", XCD_ACT_CASES)
+def test_quant_act_random_xcd_walk(pf, rows, cols, mode):
+    x = random_bf16((rows, cols), seed=rows * 37 + cols, stream=f"rand-xcd/{rows}x{cols}")
+    _check_act(pf, x, row=mode in ("row", "dual"), col=mode in ("col", "dual"), tag="random xcd walk")
+
+
 @pytest.mark.parametrize("n,k", WEIGHT_CASES)
 def test_quant_weight_random(pf, n, k):
     import oracle
