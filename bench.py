@@ -126,10 +126,17 @@ KERNEL_SYMBOLS = {
 # read the weight's own codes, so the weight quantizer writes no transposed
 # copy; "nk": FWD + DGRAD on the transposed copy.  Measured in this step on
 # the MI355X (30 steps, one box): w 7.61 ms, nk 7.65 ms; FWD_T on every
-# layer 7.67 ms, DGRAD_W on QKV and up/gate only 7.62 ms.
+# layer 7.67 ms, DGRAD_W on QKV and up/gate only 7.62 ms.  With ordinary stores
+# in the [K][N] layouts, FWD_T for the down projection alone (4.5% faster
+# than FWD on its own at K = 8192, 32768 x 2048) against w: 7.670 against
+# 7.678 ms (three interleaved runs each on one box), within noise once its
+# weight's transposed copy is paid for.
 LAYOUTS = {
     "w": {n: ("fwd", "dgrad_w") for n in ("qkv", "out_proj", "up_gate", "down")},
     "nk": {},
+    # as "w", but the down projection's FWD (K = 8192) on the transposed copy
+    "w_down_t": {**{n: ("fwd", "dgrad_w") for n in ("qkv", "out_proj", "up_gate")},
+                 "down": ("fwd_t", "dgrad_w")},
 }
 
 
