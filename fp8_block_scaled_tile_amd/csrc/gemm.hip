@@ -32,9 +32,11 @@
 //    finished unit's epilogue runs under the next block's MFMAs.  Unit ids
 //    are remapped so the 32 tiles that run together on one XCD form a
 //    compact 4(M) x 8(N) group sharing that XCD's L2.
-//  * bf16 output leaves as non-temporal stores of 64 contiguous bytes per
-//    row and instruction, so the streamed output does not evict the A / B
-//    panels that the other workgroups re-read.
+//  * bf16 output leaves as stores of 64 contiguous bytes per row and
+//    instruction: non-temporal in the row layouts, so the streamed output
+//    does not evict the A / B panels that the other workgroups re-read;
+//    ordinary in the [K][N] layouts, where non-temporal ones cost time and
+//    extra write-back (measured).
 //  * Small-output problems split K across workgroups; the FP32 partials go
 //    to the caller's workspace and a second kernel sums them in a fixed
 //    order (deterministic).
