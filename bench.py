@@ -15,9 +15,10 @@ tokens, inputs already resident in HBM:
 The metric is the GEMM work of the step (2*M*N*K summed over the 12 GEMMs,
 13.19 TFLOP) divided by the whole step's time (quantizers included), in
 TFLOP/s.  Inside the timed region HIP events bracket the launches of the
-FWD and DGRAD GEMMs (on the stream the kernels run on): the dominant
-kernel's achieved rate, reported against the MI355X dense FP8 MFMA peak
-(5.0 PFLOP/s), comes from them.  The per-kernel table ("kernels", the
+dominant GEMM class only (the one with the most time per step in the
+warm-up, where every GEMM launch is bracketed; events on the stream the
+kernels run on): its achieved rate, reported against the MI355X dense FP8
+MFMA peak (5.0 PFLOP/s), comes from them.  The per-kernel table ("kernels", the
 quantizers' rates against HBM at 8 TB/s) comes from the same K steps run
 again with events around every launch.
 
@@ -97,11 +98,6 @@ QUANT_SOURCES = [os.path.join(_CSRC, n) for n in ("quant.hip", "quant_block.hpp"
 # down-projection backward, and the linear stack of one block (the headline)
 CONFIGS = {"c1": "tiny_fwd", "c2": "qkv_fwd", "c3": "upgate_fwd", "c4": "down_bwd",
            "c5": "block_stack"}
-
-# the GEMM classes whose launches carry events inside the timed region: the
-# dominant kernel is the one of these with the most time per step (the
-# WGRAD classes run fewer FLOP per step)
-ROOFLINE_CLASSES = ("gemm_fwd_bf16", "gemm_fwd_t_bf16", "gemm_dgrad_bf16", "gemm_dgrad_w_bf16")
 
 # kernel symbol of each launch class (for matching rocprofv3 summaries)
 KERNEL_SYMBOLS = {
@@ -358,6 +354,15 @@ def step_calls(pf, layers, stream, grouped_weights=False):
 
     return head + [(L.spec.name, name, work, fn) for L in layers
                    for name, work, fn in layer_calls(L)]
+
+
+def dominant_class(timings):
+    """The launch class with the most total time in [(class, ms), ...], or
+    None for no timings (ties go to the class seen first)."""
+    total = {}
+    for name, ms in timings:
+        total[name] = total.get(name, 0.0) + ms
+    return max(total, key=total.get) if total else None
 
 
 def run_step(pf, layers, stream, rec=None, grouped_weights=False):
@@ -1062,14 +1067,6 @@ def main():
     while time.perf_counter() - t_spin < args.spin_up_s:
         run_step(pf, layers, stream, grouped_weights=gw)
         torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        run_step(pf, layers, stream, grouped_weights=gw)
-    torch.cuda.synchronize()
-
-    # timed region: K steps.  Only the launches of the two largest GEMM
-    # classes (FWD and DGRAD, bf16 out) are bracketed by events on their
-    # stream, for the roofline of the dominant kernel; events around all 26
-    # launches would cost the step 1-1.5%.
     def recorder(events, classes=None):
         def rec(name, work):
             if classes is not None and name not in classes:
@@ -1079,10 +1076,22 @@ def main():
             return ev
         return rec
 
+    # warm-up (untimed), every GEMM launch bracketed: the GEMM class with the
+    # most time per step is the dominant kernel of the roofline
+    gemm_classes = {g[1] for L in layers for g in L.gemms}
+    warm_events = []
+    for _ in range(args.warmup):
+        run_step(pf, layers, stream, recorder(warm_events, gemm_classes), grouped_weights=gw)
+    torch.cuda.synchronize()
+    dom_class = dominant_class([(name, e0.elapsed_time(e1)) for name, _, (e0, e1) in warm_events])
+
+    # timed region: K steps.  Only the dominant class's launches are
+    # bracketed by events (on the stream the kernels run on), for its live
+    # per-launch duration; events around all 26 launches would cost the step
+    # 1-1.5%, and each event pair about 6 us of idle GPU time.  Without
+    # warm-up steps every GEMM launch is bracketed.
     timed_events = []
-    # the headline step brackets FWD and DGRAD only; a single-layer workload
-    # (one to three GEMM launches per step) brackets every GEMM launch
-    classes = ROOFLINE_CLASSES if headline else {g[1] for L in layers for g in L.gemms}
+    classes = {dom_class} if dom_class else gemm_classes
     rec = recorder(timed_events, classes)
     torch.cuda.synchronize()
     t0 = time.perf_counter()

@@ -241,11 +241,17 @@ def test_more_than_one_gpu_is_refused(capsys, monkeypatch):
     assert "one GPU" in err or "single" in err
 
 
-def test_roofline_classes_are_gemm_classes():
-    """The classes timed inside the timed region are GEMM launch classes with
-    kernel symbols, so the roofline always names a GEMM kernel."""
-    for c in bench.ROOFLINE_CLASSES:
-        assert c.startswith("gemm") and c in bench.KERNEL_SYMBOLS
+def test_dominant_class_is_the_one_with_most_time():
+    """The roofline's kernel: the class with the most total time over the
+    warm-up's bracketed launches (several launches of one class add up)."""
+    t = [("gemm_fwd_bf16", 0.5), ("gemm_dgrad_w_bf16", 0.9), ("gemm_fwd_bf16", 0.5),
+         ("gemm_wgrad_fp32", 0.95)]
+    assert bench.dominant_class(t) == "gemm_fwd_bf16"
+    assert bench.dominant_class(t[1:2] + t[3:]) == "gemm_wgrad_fp32"
+    assert bench.dominant_class([]) is None
+    for c in ("gemm_fwd_bf16", "gemm_fwd_t_bf16", "gemm_dgrad_w_bf16", "gemm_wgrad_fp32",
+              "gemm_wgrad_splitk"):
+        assert c in bench.KERNEL_SYMBOLS
 
 
 def test_vendor_fp8_leg_is_omitted_without_fp8_support():
