@@ -553,9 +553,9 @@ hipError_t launch_swiglu_quant(const void* gu, int64_t rows, int64_t f, uint8_t*
     // The grouped walk: measured on MI355X at 32768 x 8192, the XCD-tiled
     // walk of the plain quantizer makes this kernel 3-6% slower (its reads
     // are two blocks of the 16384-column input per work-group).
-    const BlockWalk gr = grouped_walk(quant_group_rows(false, f));
+    const BlockWalk walk = grouped_walk(quant_group_rows(false, f));
     return PURO_DISPATCH_OUTPUTS(swiglu_quant_kernel, grid,
-                                 (g, rows, f, rows_pad, q, s, qt, st, h, gr));
+                                 (g, rows, f, rows_pad, q, s, qt, st, h, walk));
 }
 
 hipError_t launch_swiglu_bwd_quant(const void* dh, const void* gu, int64_t rows, int64_t f,
@@ -567,9 +567,9 @@ hipError_t launch_swiglu_bwd_quant(const void* dh, const void* gu, int64_t rows,
     const uint16_t* d = static_cast<const uint16_t*>(dh);
     const uint16_t* g = static_cast<const uint16_t*>(gu);
     uint16_t* dgu = static_cast<uint16_t*>(yout);
-    const BlockWalk gr = act_walk(quant_group_rows(false, 2 * f), rows_pad / 128, f / 128);
+    const BlockWalk walk = act_walk(quant_group_rows(false, 2 * f), rows_pad / 128, f / 128);
     return PURO_DISPATCH_OUTPUTS(swiglu_bwd_quant_kernel, grid,
-                                 (d, g, rows, f, rows_pad, q, s, qt, st, dgu, gr));
+                                 (d, g, rows, f, rows_pad, q, s, qt, st, dgu, walk));
 }
 
 hipError_t launch_rmsnorm_quant(const void* x, const void* gamma, int64_t rows, int64_t cols,
@@ -585,9 +585,9 @@ hipError_t launch_rmsnorm_quant(const void* x, const void* gamma, int64_t rows, 
         return e;
     const int64_t rows_pad = (rows + 127) / 128 * 128;
     const dim3 grid((unsigned)((rows_pad / 128) * (cols / 128)));
-    const BlockWalk gr = act_walk(quant_group_rows(false, cols), rows_pad / 128, cols / 128);
+    const BlockWalk walk = act_walk(quant_group_rows(false, cols), rows_pad / 128, cols / 128);
     return PURO_DISPATCH_OUTPUTS(rmsnorm_quant_kernel, grid,
-                                 (xb, gb, rstd, rows, cols, rows_pad, q, s, qt, st, y, gr));
+                                 (xb, gb, rstd, rows, cols, rows_pad, q, s, qt, st, y, walk));
 }
 
 hipError_t launch_rmsnorm_quant_rstd(const void* x, const void* gamma, const float* rstd,
@@ -599,9 +599,9 @@ hipError_t launch_rmsnorm_quant_rstd(const void* x, const void* gamma, const flo
     uint16_t* y = static_cast<uint16_t*>(yout);
     const int64_t rows_pad = (rows + 127) / 128 * 128;
     const dim3 grid((unsigned)((rows_pad / 128) * (cols / 128)));
-    const BlockWalk gr = act_walk(quant_group_rows(false, cols), rows_pad / 128, cols / 128);
+    const BlockWalk walk = act_walk(quant_group_rows(false, cols), rows_pad / 128, cols / 128);
     return PURO_DISPATCH_OUTPUTS(rmsnorm_quant_kernel, grid,
-                                 (xb, gb, rstd, rows, cols, rows_pad, q, s, qt, st, y, gr));
+                                 (xb, gb, rstd, rows, cols, rows_pad, q, s, qt, st, y, walk));
 }
 
 hipError_t launch_rmsnorm_bwd_quant(const void* dy, const void* x, const void* gamma,
@@ -620,10 +620,10 @@ hipError_t launch_rmsnorm_bwd_quant(const void* dy, const void* x, const void* g
         return e;
     const int64_t rows_pad = (rows + 127) / 128 * 128;
     const dim3 grid((unsigned)((rows_pad / 128) * (cols / 128)));
-    const BlockWalk gr = act_walk(quant_group_rows(false, cols), rows_pad / 128, cols / 128);
+    const BlockWalk walk = act_walk(quant_group_rows(false, cols), rows_pad / 128, cols / 128);
     return PURO_DISPATCH_OUTPUTS(rmsnorm_bwd_quant_kernel, grid,
                                  (db, xb, gb, rstd, coef, ib, rows, cols, rows_pad, q, s, qt, st,
-                                  y, gr));
+                                  y, walk));
 }
 
 hipError_t launch_residual_rstd(const void* a, const void* b, int64_t rows, int64_t cols, float eps,

@@ -94,15 +94,15 @@ hipError_t launch_quant_act(const void* x, int64_t rows, int64_t cols, uint8_t* 
     const dim3 grid((unsigned)((rows_pad / 128) * (cols / 128)));
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     const bool row = q != nullptr, col = qt != nullptr;
-    const BlockWalk gr = act_walk(quant_group_rows(false, cols), rows_pad / 128, cols / 128);
+    const BlockWalk walk = act_walk(quant_group_rows(false, cols), rows_pad / 128, cols / 128);
     if (row && col)
         return launch_kernel(quant_block_kernel<true, true, false, false>, grid, dim3(256), stream,
-                             xb, rows, cols, rows_pad, q, s, qt, st, gr);
+                             xb, rows, cols, rows_pad, q, s, qt, st, walk);
     if (row)
         return launch_kernel(quant_block_kernel<true, false, false, false>, grid, dim3(256), stream,
-                             xb, rows, cols, rows_pad, q, s, qt, st, gr);
+                             xb, rows, cols, rows_pad, q, s, qt, st, walk);
     return launch_kernel(quant_block_kernel<false, true, false, false>, grid, dim3(256), stream,
-                         xb, rows, cols, rows_pad, q, s, qt, st, gr);
+                         xb, rows, cols, rows_pad, q, s, qt, st, walk);
 }
 
 hipError_t launch_quant_weight(const void* w, int64_t n, int64_t k, uint8_t* q, uint8_t* qt,
@@ -110,12 +110,12 @@ hipError_t launch_quant_weight(const void* w, int64_t n, int64_t k, uint8_t* q, 
 {
     const dim3 grid((unsigned)((n / 128) * (k / 128)));
     const uint16_t* wb = static_cast<const uint16_t*>(w);
-    const BlockWalk gr = grouped_walk(quant_group_rows(true, k));
+    const BlockWalk walk = grouped_walk(quant_group_rows(true, k));
     if (qt)
         return launch_kernel(quant_block_kernel<false, false, true, true>, grid, dim3(256), stream,
-                             wb, n, k, n, q, s, qt, nullptr, gr);
+                             wb, n, k, n, q, s, qt, nullptr, walk);
     return launch_kernel(quant_block_kernel<false, false, true, false>, grid, dim3(256), stream,
-                         wb, n, k, n, q, s, nullptr, nullptr, gr);
+                         wb, n, k, n, q, s, nullptr, nullptr, walk);
 }
 
 hipError_t launch_quant_weight_grouped(const WeightJob* jobs, int count, hipStream_t stream)
