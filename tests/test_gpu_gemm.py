@@ -364,6 +364,16 @@ def test_block_stack_wgrad_split_sampled(pf):
     (2, DGRAD, torch.bfloat16),     # up/gate dgrad, dX [32768 x 2048], K = 16384
     (2, DGRAD_W, torch.bfloat16),   # the same from the weight's own codes
     (2, WGRAD, torch.float32),      # up/gate wgrad, dW [16384 x 2048], K = 32768 tokens
+    # the step's other launches: with the two above and the split out-proj
+    # wgrad, every GEMM the benchmark step runs is checked at its own shape
+    (0, DGRAD_W, torch.bfloat16),   # QKV dgrad, K = 6144
+    (0, WGRAD, torch.float32),      # QKV wgrad, dW [6144 x 2048]: split-K
+    (1, FWD, torch.bfloat16),       # out-proj forward, 2048 -> 2048
+    (1, DGRAD_W, torch.bfloat16),
+    (2, FWD, torch.bfloat16),       # up/gate forward, Y [32768 x 16384]
+    (3, FWD, torch.bfloat16),       # down forward, K = 8192
+    (3, DGRAD_W, torch.bfloat16),   # down dgrad, dX [32768 x 8192]
+    (3, WGRAD, torch.float32),      # down wgrad, dW [2048 x 8192]
 ])
 def test_block_stack_headline_sampled(pf, linear, mode, out_dtype):
     """The transformer-block workload's own shapes (32768 tokens), quantized
