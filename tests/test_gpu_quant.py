@@ -97,6 +97,31 @@ def test_quant_act_largest_block_stack_gradient(pf):
     _check_act(pf, t, row=True, col=True, tag="block_stack/up_gate/dy")
 
 
+@pytest.mark.parametrize("linear,which", [(0, "x"), (0, "dy"), (1, "x"), (1, "dy"), (2, "x"),
+                                          (3, "x"), (3, "dy")])
+def test_quant_act_block_stack_launches(pf, linear, which):
+    """With the up/gate dY above, every dual quantizer launch of the benchmark
+    step at its own shape (32768 tokens; the 2048-, 6144- and 8192-column
+    operands), all codes and scales against the oracle."""
+    spec = synth.workload("block_stack").linears[linear]
+    t = synth.linear_inputs(spec, need=(which,))[which]
+    _check_act(pf, t, row=True, col=True, tag=f"block_stack/{spec.name}/{which}")
+
+
+def test_quant_weight_grouped_block_stack(pf):
+    """The benchmark step's grouped weight launch: the block's four weights
+    (QKV 6144 x 2048, out-proj 2048 x 2048, up/gate 16384 x 2048, down
+    2048 x 8192) in one launch, codes only, against the oracle."""
+    ws = [synth.linear_inputs(spec, need=("w",))["w"] for spec in synth.workload("block_stack").linears]
+    say("quant_weight_grouped block_stack", [tuple(w.shape) for w in ws])
+    got = pf.quant_weight_grouped([dev(w) for w in ws], transpose=False, codes=True)
+    for w, g in zip(ws, got):
+        q, _, s = oracle.quant_weight(synth.bits(w), transpose=False)
+        assert np.array_equal(host(g["q"]), q)
+        assert np.array_equal(host(g["s"]).view(np.uint32), s.view(np.uint32))
+        assert "qt" not in g
+
+
 def test_quant_act_special_tiles(pf):
     """Zero tiles, negative zeros, bf16 subnormal amax (the 2^64 rescale),
     huge values, exact power-of-two amax, one outlier per tile."""
