@@ -28,18 +28,24 @@ elements the stated max-element gate is attainable by the hardware at all.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 import oracle
 
-_DEC = None
+_DEC32 = None
 
 
-def _dec():
-    global _DEC
-    if _DEC is None:
-        _DEC = oracle.e4m3_decode_table()
-    return _DEC
+def _dec32():
+    """E4M3 decode table in float32: every E4M3 value, and every product of
+    two of them (|p| from 2^-18 to 448^2 < 2^18, at most 8 significant bits),
+    is exact in float32."""
+    global _DEC32
+    if _DEC32 is None:
+        _DEC32 = oracle.e4m3_decode_table().astype(np.float32)
+    return _DEC32
 
 
 def element_bound(mode: int, a: np.ndarray, sa: np.ndarray, b: np.ndarray, sb: np.ndarray,
@@ -59,23 +65,25 @@ def bounds(mode: int, a, sa, b, sb, ii, jj, ref, chunk: int = 1024):
 
 
 def _bounds(mode, a, sa, b, sb, ii, jj, ref, chunk):
-    dec = _dec()
+    dec = _dec32()
     K = a.shape[1]
     KB = K // 128
     out = np.empty(len(ii), np.float64)
     stat = np.empty(len(ii), np.float64)
-    for s0 in range(0, len(ii), chunk):
+
+    def one_chunk(s0):
         i = np.asarray(ii[s0:s0 + chunk])
         j = np.asarray(jj[s0:s0 + chunk])
-        p = dec[a[i]] * dec[b[j]]                          # [S, K] exact products
+        p = np.abs(dec[a[i]] * dec[b[j]])                  # [S, K] exact |products|
         S = p.shape[0]
-        g = np.abs(p).reshape(S, K // 8, 8)
-        gmax = g.max(axis=2)
-        with np.errstate(divide="ignore"):
-            e = np.floor(np.log2(np.where(gmax > 0, gmax, 1.0)))
-        quantum = np.where(gmax > 0, np.exp2(e - 13.0), 0.0)        # [S, K/8]
+        gmax = p.reshape(S, K // 8, 8).max(axis=2)
+        # gmax = f * 2^e with f in [0.5, 1): the group's largest product has
+        # exponent E_g = e - 1, and the truncation quantum is 2^(E_g - 13)
+        e = np.frexp(gmax)[1]
+        quantum = np.where(gmax > 0, np.ldexp(1.0, e - 14), 0.0)   # [S, K/8], float64
         blk_trunc = 8.0 * quantum.reshape(S, KB, 16).sum(axis=2)   # [S, KB]
-        blk_abs = np.abs(p).reshape(S, KB, 128).sum(axis=2)
+        # exact in float64 in any order: multiples of 2^-18 below 2^25
+        blk_abs = p.reshape(S, KB, 128).sum(axis=2, dtype=np.float64)
         sA = sa[:, i].T.astype(np.float64)                          # [S, KB]
         if mode == 0:
             sB = sb[j // 128, :].astype(np.float64)
@@ -89,4 +97,15 @@ def _bounds(mode, a, sa, b, sb, ii, jj, ref, chunk):
         out[s0:s0 + chunk] = (sc * blk_trunc).sum(axis=1) + rounding
         var = (sc ** 2 * (8.0 / 3.0) * (quantum ** 2).reshape(S, KB, 16).sum(axis=2)).sum(axis=1)
         stat[s0:s0 + chunk] = 8.0 * np.sqrt(var) + rounding
+
+    # chunks are independent (each writes its own slice); numpy releases the
+    # GIL inside these loops, so threads share the work
+    starts = range(0, len(ii), chunk)
+    workers = min(16, os.cpu_count() or 1, max(1, len(starts)))
+    if workers > 1:
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(one_chunk, starts))
+    else:
+        for s0 in starts:
+            one_chunk(s0)
     return out, stat
